@@ -1,0 +1,144 @@
+/*
+ * mx.h -- C ABI of libmx: MX FP4 block quantization and the FP4-weight matmul on AMD
+ * MI355X (gfx950).
+ *
+ * Method (pages cited by key):
+ *  [MXS]  hotelren.com/news/2192771, the article opening with "量化技术演进与微缩量化原理"
+ *         (microscaling: FP4 elements sharing one FP8 block scale).
+ *  [FP4L] gtnt.cn/news/16247, "为什么我们需要4-bit浮点量化" (4-bit float quantization).
+ *
+ *  Quantize ([MXS] section 3.1 item 2, quantize_block; item 3, two-level scaling): for every
+ *  block of `block` consecutive elements along a row, a = max |x|; the block scale s is the
+ *  value of the scale format nearest to a / (6 g) (ties to the even code; E8M0 ties to the
+ *  larger power of two; out-of-range values saturate); every element becomes the E2M1 code
+ *  nearest to |x| / (s g), clipped at 6 ([FP4L] section 2.1, round(clip(.))), ties to the
+ *  even code, with the sign bit of x; a zero scale codes the whole block as zero.
+ *  Dequantize ([MXS] sections 1 and 3.1 item 3): x^ = e(code) * s * g.
+ *  Matmul ([FP4L] section 3.1, dequantize then matmul): Y = X . dequant(Wq)^T.
+ *
+ * Formats
+ *  E2M1 element code (4 bits): [sign][exp 2][man 1], bias 1, values
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6} and their negatives; no Inf/NaN.
+ *  MX_SCALE_E4M3:  OCP E4M3FN byte (bias 7, subnormals, 0x7F NaN, max 448); a block scale
+ *                  of 0 (byte 0x00) flushes the block.
+ *  MX_SCALE_UE5M3: unsigned 5-bit exponent (bias 15, subnormals), 3-bit mantissa,
+ *                  0xFF NaN, max 114688.
+ *  MX_SCALE_E8M0:  2^(byte - 127), bytes 0..254; never zero.
+ *  tensor_scale g: fp32, finite, normal, > 0 (1.0 = single-level scaling).
+ *
+ * Layout MX_LAYOUT_ROWMAJOR (the only layout defined):
+ *  codes : rows x (k/2) bytes, row-major, no padding; byte j of row r holds element 2j in
+ *          its low nibble and element 2j+1 in its high nibble ([FP4L] section 4.3: two FP4
+ *          values per byte).
+ *  scales: rows x (k/block) bytes, row-major, no padding; byte b of row r is the scale of
+ *          elements [b*block, (b+1)*block) of row r.
+ *  Dense tensors (x, y) are row-major with a leading dimension (row stride) in ELEMENTS.
+ *
+ * Conventions common to every entry point
+ *  - Every pointer is a DEVICE pointer owned by the caller.  The library never allocates,
+ *    frees, or synchronizes; it keeps no global mutable state and is thread-safe.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *    Outputs are valid once the stream has reached the call.
+ *  - Arguments are validated on the host before anything is launched.  On an error status
+ *    nothing has been written.  No exception crosses this boundary and nothing is printed.
+ *  - Pointers to non-empty tensors must be 16-byte aligned (MX_ERR_ALIGNMENT otherwise).
+ *  - A call on an empty tensor (rows, k, m or n equal to 0) returns MX_OK and launches
+ *    nothing; its pointers may then be NULL.  Exception: mx_gemm with k == 0 and m, n > 0
+ *    writes Y = 0 (an empty sum).
+ *  - Inputs must be finite; the result for non-finite inputs is unspecified.
+ *  - MX_ERR_HIP is returned when a launch fails (hipGetLastError after the launch).
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = -1, /* null pointer, negative size, k % block, bad enum, bad g, ... */
+    MX_ERR_UNSUPPORTED = -2, /* a valid combination this library does not implement        */
+    MX_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned                           */
+    MX_ERR_HIP = -4          /* the HIP runtime reported an error at launch                */
+} mx_status;
+
+typedef enum { MX_SCALE_E4M3 = 0, MX_SCALE_UE5M3 = 1, MX_SCALE_E8M0 = 2 } mx_scale_fmt;
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
+typedef enum { MX_LAYOUT_ROWMAJOR = 0 } mx_layout;
+typedef enum { MX_A16 = 0, MX_A4 = 1 } mx_act_mode;
+
+/*
+ * mx_quantize -- MX block quantization of a rows x k tensor.
+ *  x          : input, rows x k, element type x_type (MX_F32 or MX_BF16), row stride ld_x >= k.
+ *  block      : block size along k, one of 4, 8, 16, 32, 64, 128, 256; k % block == 0.
+ *  fmt        : block-scale format.
+ *  tensor_scale: per-tensor fp32 scale g ([MXS] section 3.1 item 3; 1.0 for none).
+ *  codes      : output, rows x k/2 bytes (layout above).
+ *  scales     : output, rows x k/block bytes.
+ * Errors: MX_ERR_INVALID_ARG for a null pointer, rows/k/ld_x negative or ld_x < k, k odd,
+ * a block size outside the list, k % block != 0, an unknown fmt/x_type/layout, or g not a
+ * finite normal positive number; MX_ERR_ALIGNMENT for a misaligned pointer.
+ * Codes and scale bytes are bit-exact with the definition above.
+ */
+mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
+                      int block, mx_scale_fmt fmt, float tensor_scale, mx_layout layout,
+                      uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * mx_dequantize -- y = e(code) * s * g for a rows x k quantized tensor.
+ *  codes, scales, rows, k, block, fmt, tensor_scale, layout: as written by mx_quantize.
+ *  y          : output, rows x k, element type y_type, row stride ld_y >= k.
+ * Output value: one fp32 rounding (nearest even) of the exact product e*s*g; for MX_BF16
+ * output, the nearest-even bf16 of that fp32 value.  With g = 1 both are exact unless the
+ * product overflows (then +-Inf).  Errors as for mx_quantize.
+ */
+mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                        int block, mx_scale_fmt fmt, float tensor_scale, mx_layout layout,
+                        void* y, mx_dtype y_type, int64_t ld_y, void* stream);
+
+/*
+ * mx_gemm_workspace_size -- bytes of device workspace mx_gemm needs for this shape and mode
+ * (0 when none).  MX_A4 needs room for the quantized activations:
+ * m*k/2 code bytes + m*k/32 scale bytes, each rounded up to 256 bytes.
+ * Returns 0 for arguments mx_gemm would reject.
+ */
+size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode);
+
+/*
+ * mx_gemm -- Y = X . dequant(Wq)^T with fp32 accumulation.
+ *  x          : activations, bf16, m x k, row stride ld_x >= k.
+ *  w_codes    : weight codes, n x k/2 bytes; w_scales: n x k/block bytes (mx_quantize
+ *               output for an n x k weight).
+ *  block, fmt, tensor_scale, layout: those of the weight.
+ *  mode       : MX_A16 -- X is used as given (bf16 x dequantized weight);
+ *               MX_A4  -- X is first MX-quantized along k with block 32, E8M0 scales and
+ *               g = 1 (bit-identical to mx_quantize with those arguments) into `workspace`,
+ *               and the product runs on the block-scaled FP4 matrix cores.  Requires
+ *               fmt == MX_SCALE_E8M0 and block == 32 (MX_ERR_UNSUPPORTED otherwise).
+ *  y          : output, m x n, element type y_type, row stride ld_y >= n.
+ *  workspace  : device buffer of at least mx_gemm_workspace_size(...) bytes (may be NULL
+ *               when that is 0); owned by the caller, contents on return unspecified.
+ * The weight's per-tensor scale is applied to the fp32 accumulator.  Accuracy: for each
+ * output, |Y - Y_exact| <= 2e-5 * sum_k |Xhat_k * What_k| before the output rounding
+ * (bf16 output adds at most half a bf16 ulp).
+ * Errors: as for mx_quantize, plus MX_ERR_INVALID_ARG when ld_y < n or the workspace is
+ * smaller than required, and MX_ERR_UNSUPPORTED as above.
+ */
+mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
+                  const uint8_t* w_codes, const uint8_t* w_scales, int block, mx_scale_fmt fmt,
+                  float tensor_scale, mx_layout layout, mx_act_mode mode, void* y,
+                  mx_dtype y_type, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mx_status_string(mx_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX_H */

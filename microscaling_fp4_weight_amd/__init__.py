@@ -1,0 +1,152 @@
+"""MX FP4 block quantization and FP4-weight GEMV/GEMM on AMD MI355X (gfx950).
+
+A thin ctypes binding over libmx.so, whose C ABI is declared in include/mx.h.  Every
+function here only marshals torch tensors (device memory) and the current HIP stream into
+that ABI: all arithmetic runs in the library's HIP kernels.  There is no CPU fallback;
+importing this package without a built libmx.so raises.
+
+    import microscaling_fp4_weight_amd as mx
+    codes, scales = mx.mx_quantize(w, block=32, fmt="e8m0")          # w: (n, k) bf16 / f32 on GPU
+    w_hat = mx.mx_dequantize(codes, scales, k, 32, "e8m0", out_dtype=torch.bfloat16)
+    y = mx.mx_gemm(x, codes, scales, block=32, fmt="e8m0", mode="a4")  # y = x . dequant(w)^T
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
+           "mx_status_string", "MXError", "lib", "FMT", "MODE", "DTYPE", "STATUS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmx.so")
+
+FMT = {"e4m3": 0, "ue5m3": 1, "e8m0": 2}
+DTYPE = {"f32": 0, "bf16": 1}
+MODE = {"a16": 0, "a4": 1}
+LAYOUT = {"rowmajor": 0}
+STATUS = {0: "MX_OK", -1: "MX_ERR_INVALID_ARG", -2: "MX_ERR_UNSUPPORTED", -3: "MX_ERR_ALIGNMENT",
+          -4: "MX_ERR_HIP"}
+
+_lib = None
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({mx_status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmx.so with argument types set (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m microscaling_fp4_weight_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, i64, f32, vp, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    L.mx_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, i32, vp, vp, vp]
+    L.mx_quantize.restype = i32
+    L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, i32, f32, i32, vp, i32, i64, vp]
+    L.mx_dequantize.restype = i32
+    L.mx_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    L.mx_gemm_workspace_size.restype = sz
+    L.mx_gemm.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp,
+                          sz, vp]
+    L.mx_gemm.restype = i32
+    L.mx_status_string.argtypes = [i32]
+    L.mx_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def mx_status_string(status: int) -> str:
+    return lib().mx_status_string(status).decode()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MXError(status, where)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return DTYPE["bf16"]
+    if dt == torch.float32:
+        return DTYPE["f32"]
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _rows_ld(t: torch.Tensor, name: str):
+    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D tensor with unit stride along its last dimension")
+    return t.size(0), t.size(1), t.stride(0) if t.size(0) > 1 else t.size(1)
+
+
+def mx_quantize(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0,
+                layout: str = "rowmajor", codes: torch.Tensor | None = None,
+                scales: torch.Tensor | None = None, stream=None):
+    """MX-quantize a 2-D bf16/fp32 GPU tensor (rows x k) along k.
+    Returns (codes uint8 rows x k/2, scales uint8 rows x k/block)."""
+    rows, k, ld = _rows_ld(x, "x")
+    if codes is None:
+        codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // max(block, 1)), dtype=torch.uint8, device=x.device)
+    st = lib().mx_quantize(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt],
+                           tensor_scale, LAYOUT[layout], _ptr(codes), _ptr(scales), _stream(stream))
+    _check(st, "mx_quantize")
+    return codes, scales
+
+
+def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, k: int, block: int, fmt: str,
+                  tensor_scale: float = 1.0, out_dtype: torch.dtype = torch.bfloat16,
+                  layout: str = "rowmajor", y: torch.Tensor | None = None, stream=None):
+    """y = e(code) * s * g as a rows x k tensor of out_dtype (bf16 or fp32)."""
+    rows = codes.size(0)
+    if y is None:
+        y = torch.empty((rows, k), dtype=out_dtype, device=codes.device)
+    _, _, ld = _rows_ld(y, "y")
+    st = lib().mx_dequantize(_ptr(codes), _ptr(scales), rows, k, block, FMT[fmt], tensor_scale,
+                             LAYOUT[layout], _ptr(y), _dtype_code(y.dtype), ld, _stream(stream))
+    _check(st, "mx_dequantize")
+    return y
+
+
+def mx_gemm_workspace_size(m: int, n: int, k: int, block: int, mode: str) -> int:
+    return int(lib().mx_gemm_workspace_size(m, n, k, block, MODE[mode]))
+
+
+def mx_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, block: int, fmt: str,
+            tensor_scale: float = 1.0, mode: str = "a16", out_dtype: torch.dtype = torch.bfloat16,
+            layout: str = "rowmajor", y: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None, stream=None):
+    """Y = X . dequant(Wq)^T.  x: m x k bf16; w_codes: n x k/2; w_scales: n x k/block."""
+    m, k, ldx = _rows_ld(x, "x")
+    n = w_codes.size(0)
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _, _, ldy = _rows_ld(y, "y")
+    need = mx_gemm_workspace_size(m, n, k, block, mode)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().mx_gemm(_ptr(x), m, n, k, ldx, _ptr(w_codes), _ptr(w_scales), block, FMT[fmt],
+                       tensor_scale, LAYOUT[layout], MODE[mode], _ptr(y), _dtype_code(y.dtype), ldy,
+                       _ptr(workspace), wbytes, _stream(stream))
+    _check(st, "mx_gemm")
+    return y

@@ -1,0 +1,186 @@
+// mx_api.cpp -- the C ABI of libmx (declared in include/mx.h): argument validation,
+// dispatch to the gfx950 kernels, and error mapping.  Host code only; no allocation, no
+// synchronization, no global mutable state.
+#include "mx.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "mx_internal.h"
+
+namespace {
+
+bool valid_block(int b)
+{
+    return b == 4 || b == 8 || b == 16 || b == 32 || b == 64 || b == 128 || b == 256;
+}
+
+bool valid_g(float g) { return std::isfinite(g) && std::isnormal(g) && g > 0.0f; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+constexpr size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Common checks of a quantized tensor description.
+mx_status check_quantized(int64_t rows, int64_t k, int block, mx_scale_fmt fmt, float g,
+                          mx_layout layout)
+{
+    if (rows < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0)
+        return MX_ERR_INVALID_ARG;
+    if (fmt != MX_SCALE_E4M3 && fmt != MX_SCALE_UE5M3 && fmt != MX_SCALE_E8M0)
+        return MX_ERR_INVALID_ARG;
+    if (layout != MX_LAYOUT_ROWMAJOR) return MX_ERR_INVALID_ARG;
+    if (!valid_g(g)) return MX_ERR_INVALID_ARG;
+    return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(mx_status s)
+{
+    switch (s) {
+        case MX_OK: return "success";
+        case MX_ERR_INVALID_ARG: return "invalid argument";
+        case MX_ERR_UNSUPPORTED: return "unsupported combination";
+        case MX_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case MX_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
+                      int block, mx_scale_fmt fmt, float tensor_scale, mx_layout layout,
+                      uint8_t* codes, uint8_t* scales, void* stream)
+{
+    mx_status st = check_quantized(rows, k, block, fmt, tensor_scale, layout);
+    if (st != MX_OK) return st;
+    if (x_type != MX_F32 && x_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_x < k) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return MX_OK;
+    if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
+    const int esize = x_type == MX_BF16 ? 2 : 4;
+    if (rows * (k / 32) > INT32_MAX - 1024) return MX_ERR_UNSUPPORTED;
+    mxk::QuantArgs a;
+    a.x = x;
+    a.bf16 = x_type == MX_BF16;
+    a.rows = rows;
+    a.k = k;
+    a.ldx = ld_x;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = (double)tensor_scale;
+    a.codes = codes;
+    a.scales = scales;
+    a.fast = (k % 32 == 0) && ((ld_x * esize) % 16 == 0);
+    return from_hip(mxk::launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                        int block, mx_scale_fmt fmt, float tensor_scale, mx_layout layout,
+                        void* y, mx_dtype y_type, int64_t ld_y, void* stream)
+{
+    mx_status st = check_quantized(rows, k, block, fmt, tensor_scale, layout);
+    if (st != MX_OK) return st;
+    if (y_type != MX_F32 && y_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_y < k) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return MX_OK;
+    if (!y || !codes || !scales) return MX_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
+    const int esize = y_type == MX_BF16 ? 2 : 4;
+    if (rows * (k / 32) > INT32_MAX - 1024) return MX_ERR_UNSUPPORTED;
+    mxk::DequantArgs a;
+    a.codes = codes;
+    a.scales = scales;
+    a.rows = rows;
+    a.k = k;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = (double)tensor_scale;
+    a.y = y;
+    a.bf16 = y_type == MX_BF16;
+    a.ldy = ld_y;
+    a.fast = (k % 32 == 0) && ((ld_y * esize) % 16 == 0);
+    return from_hip(mxk::launch_dequantize(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode)
+{
+    if (m < 0 || n < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;
+    if (mode != MX_A4) return 0;
+    if (block != 32) return 0;
+    return round256((size_t)m * (size_t)(k / 2)) + round256((size_t)m * (size_t)(k / 32));
+}
+
+mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
+                  const uint8_t* w_codes, const uint8_t* w_scales, int block, mx_scale_fmt fmt,
+                  float tensor_scale, mx_layout layout, mx_act_mode mode, void* y,
+                  mx_dtype y_type, int64_t ld_y, void* workspace, size_t workspace_bytes,
+                  void* stream)
+{
+    if (m < 0 || n < 0) return MX_ERR_INVALID_ARG;
+    mx_status st = check_quantized(n, k, block, fmt, tensor_scale, layout);
+    if (st != MX_OK) return st;
+    if (mode != MX_A16 && mode != MX_A4) return MX_ERR_INVALID_ARG;
+    if (y_type != MX_F32 && y_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_x < k || ld_y < n) return MX_ERR_INVALID_ARG;
+    if (mode == MX_A4 && (fmt != MX_SCALE_E8M0 || block != 32)) return MX_ERR_UNSUPPORTED;
+    if (m == 0 || n == 0) return MX_OK;
+    if (!y) return MX_ERR_INVALID_ARG;
+    if (!aligned16(y)) return MX_ERR_ALIGNMENT;
+    if (k == 0)  // an empty sum: Y = 0
+        return from_hip(mxk::launch_fill_zero(y, m, n, ld_y, y_type == MX_BF16, static_cast<hipStream_t>(stream)));
+    if (!x || !w_codes || !w_scales) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y))
+        return MX_ERR_ALIGNMENT;
+    const size_t need = mx_gemm_workspace_size(m, n, k, block, mode);
+    if (workspace_bytes < need || (need && !workspace)) return MX_ERR_INVALID_ARG;
+    if (need && !aligned16(workspace)) return MX_ERR_ALIGNMENT;
+    if (m * (k / 32) > INT32_MAX - 1024) return MX_ERR_UNSUPPORTED;
+
+    mxk::GemmArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    a.ldx = ld_x;
+    a.wc = w_codes;
+    a.ws = w_scales;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = tensor_scale;
+    a.y = y;
+    a.y_bf16 = y_type == MX_BF16;
+    a.ldy = ld_y;
+    a.xq_codes = nullptr;
+    a.xq_scales = nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mode == MX_A16) return from_hip(mxk::launch_gemm_a16(a, s));
+
+    // W4A4: MX-quantize the activations (block 32, E8M0, g = 1) into the workspace with the
+    // quantize kernel itself, then run the FP4 matrix-core product.
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.xq_codes = ws;
+    a.xq_scales = ws + round256((size_t)m * (size_t)(k / 2));
+    mxk::QuantArgs q;
+    q.x = x;
+    q.bf16 = true;
+    q.rows = m;
+    q.k = k;
+    q.ldx = ld_x;
+    q.block = 32;
+    q.fmt = mxk::FMT_E8M0;
+    q.g = 1.0;
+    q.codes = a.xq_codes;
+    q.scales = a.xq_scales;
+    q.fast = (ld_x * 2) % 16 == 0;  // k % 32 == 0 holds (block 32)
+    hipError_t e = mxk::launch_quantize(q, s);
+    if (e != hipSuccess) return MX_ERR_HIP;
+    return from_hip(mxk::launch_gemm_a4(a, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,327 @@
+// mx_device.h -- gfx950 device helpers for MX FP4 block quantization (scale encoding,
+// element encoding, dequantization).  Private to libmx.
+//
+// Method: hotelren.com/news/2192771, article "量化技术演进与微缩量化原理", section 3.1
+// item 2 (block scale = FP8(absmax / 6); element = FP4(x / scale)) and item 3 (per-tensor
+// scale g multiplies the block scale); gtnt.cn/news/16247 "为什么我们需要4-bit浮点量化",
+// section 2.1 (clip, then round).  Rounding is to nearest, ties to the even code (E8M0:
+// ties to the larger power of two); scales saturate.
+//
+// Hardware facts used here (gfx950, checked on the device against an exact CPU reference):
+//  * v_cvt_scalef32_pk_fp4_{f32,bf16}(x, scale) returns the E2M1 code nearest to
+//    x / 2^floor(log2 scale) (only the scale's exponent is used; denormal scales work),
+//    ties to even, saturating at +-6, keeping the sign of zero;
+//  * v_cvt_scalef32_pk_{f32,bf16}_fp4(code, scale) returns e(code) * 2^floor(log2 scale)
+//    with IEEE overflow to Inf;
+//  * fp32 division is correctly rounded and fp32 denormals are kept (kernel float mode 3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx_internal.h"
+
+namespace mxk {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+template <int FMT>
+struct ScaleFmt;
+template <>
+struct ScaleFmt<FMT_E4M3> {
+    static constexpr int bias = 7;
+    static constexpr uint32_t maxcode = 0x7E;  // 448; 0x7F is NaN
+};
+template <>
+struct ScaleFmt<FMT_UE5M3> {
+    static constexpr int bias = 15;
+    static constexpr uint32_t maxcode = 0xFE;  // 114688; 0xFF is NaN
+};
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// x >> s rounded to nearest, ties to even (1 <= s <= 31, x < 2^31).
+__device__ __forceinline__ uint32_t rne_shr32(uint32_t x, uint32_t s)
+{
+    return (x + ((1u << (s - 1)) - 1u) + ((x >> s) & 1u)) >> s;
+}
+__device__ __forceinline__ uint64_t rne_shr64(uint64_t x, uint32_t s)
+{
+    return (x + ((1ull << (s - 1)) - 1ull) + ((x >> s) & 1ull)) >> s;
+}
+
+// ---------------------------------------------------------------------------------------
+// Block scale encoding.
+// ---------------------------------------------------------------------------------------
+
+// E4M3 / UE5M3 code nearest to v >= 0 given in fp32 (3 mantissa bits, subnormals,
+// saturation at the largest finite code).
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_code_f32(float v)
+{
+    constexpr int bias = ScaleFmt<FMT>::bias;
+    const uint32_t b = f2u(v);
+    const int e = (int)(b >> 23);
+    if (e == 0) return 0;  // zero or fp32-subnormal: below half the smallest scale
+    const uint32_t sig = (b & 0x7FFFFFu) | 0x800000u;  // value = sig * 2^(e - 150)
+    const int et = e - 127 + bias;                     // target exponent field if normal
+    uint32_t code;
+    if (et >= 1) {
+        code = ((uint32_t)(et - 1) << 3) + rne_shr32(sig, 20);  // a carry moves to et + 1
+    } else {
+        const int sh = 148 - bias - e;  // subnormal step 2^(-2-bias)
+        code = sh > 31 ? 0u : rne_shr32(sig, (uint32_t)sh);
+    }
+    return code < ScaleFmt<FMT>::maxcode ? code : ScaleFmt<FMT>::maxcode;
+}
+
+// Same from an fp64 value (used with a per-tensor scale, where v = a / (6 g) is formed in
+// fp64 by a correctly rounded division, which decides every midpoint exactly).
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_code_f64(double v)
+{
+    constexpr int bias = ScaleFmt<FMT>::bias;
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int e = (int)((b >> 52) & 0x7FF);
+    if (e == 0) return 0;
+    const uint64_t sig = (b & 0xFFFFFFFFFFFFFull) | (1ull << 52);  // value = sig * 2^(e-1075)
+    const int et = e - 1023 + bias;
+    uint64_t code;
+    if (et >= 1) {
+        if (et > 40) return ScaleFmt<FMT>::maxcode;
+        code = ((uint64_t)(et - 1) << 3) + rne_shr64(sig, 49);
+    } else {
+        const int sh = 1073 - bias - e;
+        code = sh > 63 ? 0ull : rne_shr64(sig, (uint32_t)sh);
+    }
+    return code < ScaleFmt<FMT>::maxcode ? (uint32_t)code : ScaleFmt<FMT>::maxcode;
+}
+
+// E4M3 / UE5M3 byte -> fp32 value (exact).  E4M3 bytes 0x80..0xFE are negative values;
+// the quantizer never writes them, but dequantization honours them.
+template <int FMT>
+__device__ __forceinline__ float fp8_value(uint32_t code)
+{
+    constexpr int bias = ScaleFmt<FMT>::bias;
+    const uint32_t sign = FMT == FMT_E4M3 ? (code & 0x80u) << 24 : 0u;
+    const uint32_t E = FMT == FMT_E4M3 ? (code >> 3) & 15u : code >> 3, M = code & 7u;
+    if (E) return u2f(sign | ((E - bias + 127) << 23) | (M << 20));
+    return u2f(sign | f2u((float)M * u2f((uint32_t)(127 - 2 - bias) << 23)));  // M * 2^(-2-bias)
+}
+
+// E8M0 byte of the power of two nearest to a / 6 (ties up), from the fp32 bits of
+// a = |absmax|: with a = f * 2^ea, f in [1, 2), the midpoint 1.5 * 2^k of a/6 is a = 9 * 2^k,
+// so k = ea - 3 + [f >= 1.125] and byte = k + 127, clamped to [0, 254].
+__device__ __forceinline__ uint32_t e8m0_code_absmax(uint32_t abits)
+{
+    const int e = (int)(abits >> 23);
+    const int byte = e - 3 + ((abits & 0x7FFFFFu) >= 0x100000u ? 1 : 0);
+    return byte < 0 ? 0u : (byte > 254 ? 254u : (uint32_t)byte);
+}
+
+// E8M0 byte nearest to v >= 0 given in fp64 (ties up).
+__device__ __forceinline__ uint32_t e8m0_code_f64(double v)
+{
+    if (v == 0.0) return 0;
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int k = (int)((b >> 52) & 0x7FF) - 1023 + ((b & 0xFFFFFFFFFFFFFull) >= (1ull << 51) ? 1 : 0);
+    const int byte = k + 127;
+    return byte < 0 ? 0u : (byte > 254 ? 254u : (uint32_t)byte);
+}
+
+// 2^(byte - 127) as fp32 (byte 0 is the fp32 denormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t byte)
+{
+    return byte ? u2f(byte << 23) : u2f(0x00400000u);
+}
+__device__ __forceinline__ double e8m0_value_f64(uint32_t byte)
+{
+    return __builtin_bit_cast(double, (uint64_t)(byte + 1023 - 127) << 52);
+}
+
+// Scale byte of a block from its absmax bits (fp32 bits of a >= 0), for g == 1.
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_code_g1(uint32_t abits)
+{
+    if constexpr (FMT == FMT_E8M0) {
+        return e8m0_code_absmax(abits);
+    } else {
+        // fl32(a / 6) decides every FP8 midpoint exactly (a correctly rounded quotient of an
+        // fp32 value by 6 never lands on, or crosses, a value with 5 significant bits).
+        return fp8_code_f32<FMT>(u2f(abits) / 6.0f);
+    }
+}
+
+// Scale byte for a per-tensor scale g (six_g = 6 * g, exact in fp64).
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_code_g(uint32_t abits, double six_g)
+{
+    const double v = (double)u2f(abits) / six_g;
+    if constexpr (FMT == FMT_E8M0) return e8m0_code_f64(v);
+    else return fp8_code_f64<FMT>(v);
+}
+
+// Decoded scale as fp64 (exact).
+template <int FMT>
+__device__ __forceinline__ double scale_value_f64(uint32_t byte)
+{
+    if constexpr (FMT == FMT_E8M0) return e8m0_value_f64(byte);
+    else return (double)fp8_value<FMT>(byte);
+}
+
+// ---------------------------------------------------------------------------------------
+// Element encoding with g == 1.
+//
+// s = m * 2^E with m in {1, 1.125, ..., 1.875}.  The hardware converter divides by 2^E
+// exactly, so the element path feeds it x' = x / m, formed as fma(x, chi, x * clo) where
+// chi + clo approximates 1/m to ~2^-48: every tie x = t * s lands exactly on t * 2^E and
+// every other input stays on its side of the decision points (checked exhaustively over
+// all bf16 inputs for all eight m).  E8M0 has m = 1 and feeds x directly.
+// ---------------------------------------------------------------------------------------
+
+struct EncG1 {
+    float pow2;  // 2^E for the converter
+    float chi;   // 1/m, high part (0 when the block scale is 0)
+    float clo;   // 1/m, low part
+};
+
+__device__ __forceinline__ void recip_parts(uint32_t mi, float& chi, float& clo)
+{
+    // chi = 1/m rounded down to fp32, clo = fl32(1/m - chi) >= 0 for m = 1 + mi/8.  Both
+    // parts are non-negative so that x' keeps the sign of x, also for x = -0.
+    switch (mi) {
+        case 0: chi = u2f(0x3f800000u); clo = 0.0f; break;
+        case 1: chi = u2f(0x3f638e38u); clo = u2f(0x33638e39u); break;
+        case 2: chi = u2f(0x3f4cccccu); clo = u2f(0x334ccccdu); break;
+        case 3: chi = u2f(0x3f3a2e8bu); clo = u2f(0x3322e8bau); break;
+        case 4: chi = u2f(0x3f2aaaaau); clo = u2f(0x332aaaabu); break;
+        case 5: chi = u2f(0x3f1d89d8u); clo = u2f(0x331d89d9u); break;
+        case 6: chi = u2f(0x3f124924u); clo = u2f(0x33124925u); break;
+        default: chi = u2f(0x3f088888u); clo = u2f(0x33088889u); break;
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ EncG1 enc_params_g1(uint32_t byte)
+{
+    EncG1 p;
+    if constexpr (FMT == FMT_E8M0) {
+        p.pow2 = e8m0_value(byte);
+        p.chi = 1.0f;
+        p.clo = 0.0f;
+    } else {
+        const float s = fp8_value<FMT>(byte);
+        const uint32_t sb = f2u(s);
+        if (sb == 0) {  // flushed block: x' = +-0 -> codes 0 / 8
+            p.pow2 = 1.0f;
+            p.chi = 0.0f;
+            p.clo = 0.0f;
+        } else {
+            p.pow2 = u2f(sb & 0x7F800000u);
+            recip_parts((sb >> 20) & 7u, p.chi, p.clo);
+        }
+    }
+    return p;
+}
+
+// Two fp32 elements -> one code byte (lo element in the low nibble), g == 1.
+template <int FMT>
+__device__ __forceinline__ uint32_t enc_pair_g1(float lo, float hi, const EncG1& p, uint32_t old,
+                                                int sel_dummy = 0)
+{
+    (void)sel_dummy;
+    if constexpr (FMT != FMT_E8M0) {
+        lo = __builtin_fmaf(lo, p.chi, lo * p.clo);
+        hi = __builtin_fmaf(hi, p.chi, hi * p.clo);
+    }
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, lo, hi, p.pow2, 0) & 0xFFu;
+}
+
+// ---------------------------------------------------------------------------------------
+// Element encoding with a per-tensor scale g != 1: compare |x| with the exact decision
+// points t * s * g (t = 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; formed exactly in fp64).
+// Each becomes an fp32 threshold u with  [|x| passes t*s*g]  <=>  [|x| > u]:
+//   strict ">" points (ties go down): u = largest fp32 <= t*s*g;
+//   ">=" points (ties go up):         u = that value, minus one ulp if it equals t*s*g.
+// The code magnitude is the number of thresholds |x| exceeds.
+// ---------------------------------------------------------------------------------------
+
+struct EncG {
+    uint32_t u[7];  // fp32 bit patterns, compared as unsigned integers with |x|'s bits
+};
+
+__device__ __forceinline__ uint32_t rd32_bits(double t)  // t > 0
+{
+    float f = (float)t;
+    uint32_t b = f2u(f);
+    if ((double)f > t) b -= 1u;  // also maps +Inf (t beyond FLT_MAX) to FLT_MAX
+    return b;
+}
+
+template <int FMT>
+__device__ __forceinline__ EncG enc_params_g(uint32_t byte, double g)
+{
+    EncG p;
+    const double s = scale_value_f64<FMT>(byte);
+    if (s == 0.0) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) p.u[i] = 0x7F800000u;  // nothing exceeds +Inf
+        return p;
+    }
+    const double sg = s * g;
+    const double t[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+        const double tt = t[i] * sg;
+        uint32_t b = rd32_bits(tt);
+        if ((i & 1) && (double)u2f(b) == tt) b -= 1u;  // ">=" points: 0.75, 1.75, 3.5
+        p.u[i] = b;
+    }
+    return p;
+}
+
+__device__ __forceinline__ uint32_t enc_elem_g(uint32_t xbits32, const EncG& p)
+{
+    const uint32_t a = xbits32 & 0x7FFFFFFFu;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) c += (a > p.u[i]) ? 1u : 0u;
+    return c | ((xbits32 >> 28) & 8u);
+}
+
+// ---------------------------------------------------------------------------------------
+// Dequantization helpers.
+// ---------------------------------------------------------------------------------------
+
+// For g == 1: e * s = (e * 2^E) * m, both steps exact (m = 0 for a flushed block).
+struct DecG1 {
+    float pow2;
+    float mant;
+};
+
+template <int FMT>
+__device__ __forceinline__ DecG1 dec_params_g1(uint32_t byte)
+{
+    DecG1 p;
+    if constexpr (FMT == FMT_E8M0) {
+        p.pow2 = e8m0_value(byte);
+        p.mant = 1.0f;
+    } else {
+        // s = mant * pow2 with mant = +-(1 + M/8) carrying the sign of s, or mant = +-0
+        const uint32_t sb = f2u(fp8_value<FMT>(byte));
+        const bool zero = (sb & 0x7FFFFFFFu) == 0;
+        p.pow2 = zero ? 1.0f : u2f(sb & 0x7F800000u);
+        p.mant = zero ? u2f(sb) : u2f((sb & 0x807FFFFFu) | 0x3F800000u);
+    }
+    return p;
+}
+
+}  // namespace mxk

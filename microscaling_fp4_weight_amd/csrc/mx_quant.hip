@@ -1,0 +1,440 @@
+// mx_quant.hip -- MX FP4 block quantization and dequantization kernels for gfx950.
+//
+// Method: hotelren.com/news/2192771, article "量化技术演进与微缩量化原理", section 3.1
+// (quantize_block: absmax -> FP8 scale of absmax/6 -> FP4 of x/scale; two-level scaling);
+// gtnt.cn/news/16247 "为什么我们需要4-bit浮点量化", sections 2.1 (clip then round) and 4.3
+// (two FP4 codes per byte).
+//
+// Fast path: one lane owns 32 consecutive elements of a row (64 B of bf16 / 128 B of fp32,
+// loaded with 128-bit loads) and writes their 16 code bytes with one 128-bit store.  Blocks
+// of up to 32 elements are lane-local; larger blocks (64..256) span 2..8 neighbouring lanes
+// and reduce their absmax with cross-lane shuffles.  Requires k % 32 == 0 and 16-byte
+// aligned rows.  The generic path (one thread per block, scalar accesses) covers every
+// other valid shape with the same arithmetic.
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mxk {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------------------
+// quantize, fast path
+// ---------------------------------------------------------------------------------------
+template <int BLOCK, int FMT, bool BF16, bool G1>
+__global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t groups_per_row,
+    uint32_t total_groups, double g, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, int64_t k)
+{
+    constexpr int NW = BF16 ? 16 : 32;                    // 32-bit words holding 32 elements
+    constexpr int NB = BLOCK <= 32 ? 32 / BLOCK : 1;      // blocks (or block parts) per lane
+    constexpr int WPB = NW / NB;                          // words per lane-local block part
+    constexpr int LANES = BLOCK > 32 ? BLOCK / 32 : 1;    // lanes sharing one block
+
+    const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+    const bool active = gid < total_groups;
+    const uint32_t row = active ? gid / groups_per_row : 0u;
+    const uint32_t gc = active ? gid - row * groups_per_row : 0u;
+
+    uint32_t w[NW];
+    if (active) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(x + (int64_t)row * ldx_bytes +
+                                                        (int64_t)gc * (BF16 ? 64 : 128));
+#pragma unroll
+        for (int j = 0; j < NW / 4; ++j) {
+            const u32x4 v = __builtin_nontemporal_load(p + j);
+            w[4 * j + 0] = v.x;
+            w[4 * j + 1] = v.y;
+            w[4 * j + 2] = v.z;
+            w[4 * j + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) w[j] = 0u;
+    }
+
+    // absmax bits (fp32 pattern of |x|) per lane-local block part
+    uint32_t amax[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        if constexpr (BF16) {
+            u16x2 m = __builtin_bit_cast(u16x2, w[b * WPB] & 0x7FFF7FFFu);
+#pragma unroll
+            for (int j = 1; j < WPB; ++j)
+                m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[b * WPB + j] & 0x7FFF7FFFu));
+            const uint32_t mm = m.x > m.y ? m.x : m.y;
+            amax[b] = mm << 16;
+        } else {
+            uint32_t m = w[b * WPB] & 0x7FFFFFFFu;
+#pragma unroll
+            for (int j = 1; j < WPB; ++j) {
+                const uint32_t a = w[b * WPB + j] & 0x7FFFFFFFu;
+                m = a > m ? a : m;
+            }
+            amax[b] = m;
+        }
+    }
+    if constexpr (LANES > 1) {
+#pragma unroll
+        for (int off = 1; off < LANES; off <<= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)amax[0], off);
+            amax[0] = o > amax[0] ? o : amax[0];
+        }
+    }
+
+    // scale bytes
+    uint32_t sbyte[NB];
+    const double six_g = 6.0 * g;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) sbyte[b] = G1 ? scale_code_g1<FMT>(amax[b]) : scale_code_g<FMT>(amax[b], six_g);
+
+    if (active) {
+        uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
+        if constexpr (NB == 1) {
+            if (LANES == 1 || (gc % LANES) == 0) sp[gc / LANES] = (uint8_t)sbyte[0];
+        } else if constexpr (NB == 2) {
+            *reinterpret_cast<uint16_t*>(sp + gc * 2) = (uint16_t)(sbyte[0] | (sbyte[1] << 8));
+        } else if constexpr (NB == 4) {
+            *reinterpret_cast<uint32_t*>(sp + gc * 4) =
+                sbyte[0] | (sbyte[1] << 8) | (sbyte[2] << 16) | (sbyte[3] << 24);
+        } else {
+            const uint32_t lo = sbyte[0] | (sbyte[1] << 8) | (sbyte[2] << 16) | (sbyte[3] << 24);
+            const uint32_t hi = sbyte[4] | (sbyte[5] << 8) | (sbyte[6] << 16) | (sbyte[7] << 24);
+            const u32x2 sv = {lo, hi};
+            *reinterpret_cast<u32x2*>(sp + gc * 8) = sv;
+        }
+    }
+
+    // element codes: 4 output words of 8 codes each
+    uint32_t out[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = 0u;
+
+    if constexpr (G1) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const EncG1 p = enc_params_g1<FMT>(sbyte[b]);
+            if constexpr (BF16) {
+                // pair j = elements (2j, 2j+1) = word j
+#pragma unroll
+                for (int jj = 0; jj < WPB; ++jj) {
+                    const int j = b * WPB + jj;
+                    uint32_t r;
+                    if constexpr (FMT == FMT_E8M0) {
+                        const bf16x2 v = __builtin_bit_cast(bf16x2, w[j]);
+                        switch (j & 3) {
+                            case 0: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j >> 2], v, p.pow2, 0); break;
+                            case 1: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j >> 2], v, p.pow2, 1); break;
+                            case 2: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j >> 2], v, p.pow2, 2); break;
+                            default: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out[j >> 2], v, p.pow2, 3); break;
+                        }
+                    } else {
+                        float lo = u2f(w[j] << 16), hi = u2f(w[j] & 0xFFFF0000u);
+                        lo = __builtin_fmaf(lo, p.chi, lo * p.clo);
+                        hi = __builtin_fmaf(hi, p.chi, hi * p.clo);
+                        switch (j & 3) {
+                            case 0: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 0); break;
+                            case 1: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 1); break;
+                            case 2: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 2); break;
+                            default: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 3); break;
+                        }
+                    }
+                    out[j >> 2] = r;
+                }
+            } else {
+                // fp32: pair j = words (2j, 2j+1)
+#pragma unroll
+                for (int jj = 0; jj < WPB / 2; ++jj) {
+                    const int j = b * (WPB / 2) + jj;
+                    float lo = u2f(w[2 * j]), hi = u2f(w[2 * j + 1]);
+                    if constexpr (FMT != FMT_E8M0) {
+                        lo = __builtin_fmaf(lo, p.chi, lo * p.clo);
+                        hi = __builtin_fmaf(hi, p.chi, hi * p.clo);
+                    }
+                    uint32_t r;
+                    switch (j & 3) {
+                        case 0: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 0); break;
+                        case 1: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 1); break;
+                        case 2: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 2); break;
+                        default: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out[j >> 2], lo, hi, p.pow2, 3); break;
+                    }
+                    out[j >> 2] = r;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const EncG p = enc_params_g<FMT>(sbyte[b], g);
+            constexpr int EPB = 32 / NB;  // elements per lane-local block part
+#pragma unroll
+            for (int ee = 0; ee < EPB; ++ee) {
+                const int e = b * EPB + ee;
+                const uint32_t xb = BF16 ? ((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16)) : w[e];
+                out[e >> 3] |= enc_elem_g(xb, p) << (4 * (e & 7));
+            }
+        }
+    }
+
+    if (active) {
+        u32x4* cp = reinterpret_cast<u32x4*>(codes + (int64_t)row * (k / 2) + (int64_t)gc * 16);
+        const u32x4 ov = {out[0], out[1], out[2], out[3]};
+        __builtin_nontemporal_store(ov, cp);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// quantize, generic path: one thread per block
+// ---------------------------------------------------------------------------------------
+template <int FMT, bool BF16, bool G1>
+__global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
+    const uint8_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t k, int block, double g,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    const int64_t nb = k / block;
+    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (id >= rows * nb) return;
+    const int64_t r = id / nb, b = id - r * nb;
+    const int64_t base = r * ldx + b * block;
+    auto bits = [&](int64_t i) -> uint32_t {
+        if constexpr (BF16) return (uint32_t)reinterpret_cast<const uint16_t*>(x)[base + i] << 16;
+        else return reinterpret_cast<const uint32_t*>(x)[base + i];
+    };
+    uint32_t amax = 0;
+    for (int i = 0; i < block; ++i) {
+        const uint32_t a = bits(i) & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+    }
+    const uint32_t sb = G1 ? scale_code_g1<FMT>(amax) : scale_code_g<FMT>(amax, 6.0 * g);
+    scales[r * nb + b] = (uint8_t)sb;
+    uint8_t* cp = codes + r * (k / 2) + b * (block / 2);
+    if constexpr (G1) {
+        const EncG1 p = enc_params_g1<FMT>(sb);
+        for (int i = 0; i < block; i += 2) cp[i / 2] = (uint8_t)enc_pair_g1<FMT>(u2f(bits(i)), u2f(bits(i + 1)), p, 0u);
+    } else {
+        const EncG p = enc_params_g<FMT>(sb, g);
+        for (int i = 0; i < block; i += 2)
+            cp[i / 2] = (uint8_t)(enc_elem_g(bits(i), p) | (enc_elem_g(bits(i + 1), p) << 4));
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dequantize, fast path: one lane per 32 consecutive elements
+// ---------------------------------------------------------------------------------------
+template <int FMT, bool G1, bool OUT_BF16>
+__device__ __forceinline__ void dec_byte_pair(uint32_t cw, int sel, float pow2, float mant,
+                                             double sg, float& lo, float& hi)
+{
+    f32x2 f;
+    const float sc = G1 ? pow2 : 1.0f;
+    switch (sel) {
+        case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 0); break;
+        case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 1); break;
+        case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 2); break;
+        default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, sc, 3); break;
+    }
+    if constexpr (G1) {
+        lo = (FMT == FMT_E8M0) ? f.x : f.x * mant;
+        hi = (FMT == FMT_E8M0) ? f.y : f.y * mant;
+    } else {  // one rounding of the exact e * s * g
+        lo = (float)((double)f.x * sg);
+        hi = (float)((double)f.y * sg);
+    }
+}
+
+template <int BLOCK, int FMT, bool G1, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    uint32_t groups_per_row, uint32_t total_groups, int64_t k, double g,
+    uint8_t* __restrict__ y, int64_t ldy_bytes)
+{
+    constexpr int NB = BLOCK <= 32 ? 32 / BLOCK : 1;
+    constexpr int LANES = BLOCK > 32 ? BLOCK / 32 : 1;
+    const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
+    if (gid >= total_groups) return;
+    const uint32_t row = gid / groups_per_row;
+    const uint32_t gc = gid - row * groups_per_row;
+
+    const u32x4 cv = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(codes + (int64_t)row * (k / 2) + (int64_t)gc * 16));
+    const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+    const uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
+    uint32_t sbyte[NB];
+    if constexpr (NB == 1) {
+        sbyte[0] = sp[gc / LANES];
+    } else if constexpr (NB == 2) {
+        const uint32_t v = *reinterpret_cast<const uint16_t*>(sp + gc * 2);
+        sbyte[0] = v & 0xFF; sbyte[1] = v >> 8;
+    } else if constexpr (NB == 4) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(sp + gc * 4);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sbyte[b] = (v >> (8 * b)) & 0xFF;
+    } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(sp + gc * 8);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) { sbyte[b] = (v.x >> (8 * b)) & 0xFF; sbyte[4 + b] = (v.y >> (8 * b)) & 0xFF; }
+    }
+
+    uint32_t o[OUT_BF16 ? 16 : 32];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float pow2 = 1.0f, mant = 1.0f;
+        double sg = 0.0;
+        if constexpr (G1) {
+            const DecG1 p = dec_params_g1<FMT>(sbyte[b]);
+            pow2 = p.pow2;
+            mant = p.mant;
+        } else {
+            sg = scale_value_f64<FMT>(sbyte[b]) * g;
+        }
+        constexpr int PPB = 16 / NB;  // code bytes (element pairs) per block part
+#pragma unroll
+        for (int jj = 0; jj < PPB; ++jj) {
+            const int j = b * PPB + jj;  // pair index 0..15
+            if constexpr (OUT_BF16 && G1 && FMT == FMT_E8M0) {
+                bf16x2 h;
+                switch (j & 3) {
+                    case 0: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 0); break;
+                    case 1: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 1); break;
+                    case 2: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 2); break;
+                    default: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 3); break;
+                }
+                o[j] = __builtin_bit_cast(uint32_t, h);
+            } else {
+                float lo, hi;
+                dec_byte_pair<FMT, G1, OUT_BF16>(cw[j >> 2], j & 3, pow2, mant, sg, lo, hi);
+                if constexpr (OUT_BF16) {
+                    bf16x2 h;
+                    h.x = (__bf16)lo;
+                    h.y = (__bf16)hi;
+                    o[j] = __builtin_bit_cast(uint32_t, h);
+                } else {
+                    o[2 * j] = f2u(lo);
+                    o[2 * j + 1] = f2u(hi);
+                }
+            }
+        }
+    }
+    u32x4* yp = reinterpret_cast<u32x4*>(y + (int64_t)row * ldy_bytes + (int64_t)gc * (OUT_BF16 ? 64 : 128));
+#pragma unroll
+    for (int q = 0; q < (OUT_BF16 ? 4 : 8); ++q) {
+        const u32x4 ov = {o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        __builtin_nontemporal_store(ov, yp + q);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// dequantize, generic path: one thread per element pair
+// ---------------------------------------------------------------------------------------
+template <int FMT, bool G1, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void dequantize_generic_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
+    int64_t k, int block, double g, uint8_t* __restrict__ y, int64_t ldy)
+{
+    const int64_t pairs = k / 2;
+    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (id >= rows * pairs) return;
+    const int64_t r = id / pairs, j = id - r * pairs;
+    const uint32_t cb = codes[r * pairs + j];
+    const uint32_t sb = scales[r * (k / block) + (2 * j) / block];
+    float pow2 = 1.0f, mant = 1.0f;
+    double sg = 0.0;
+    if constexpr (G1) {
+        const DecG1 p = dec_params_g1<FMT>(sb);
+        pow2 = p.pow2;
+        mant = p.mant;
+    } else {
+        sg = scale_value_f64<FMT>(sb) * g;
+    }
+    float lo, hi;
+    dec_byte_pair<FMT, G1, OUT_BF16>(cb, 0, pow2, mant, sg, lo, hi);
+    if constexpr (OUT_BF16) {
+        uint16_t* yp = reinterpret_cast<uint16_t*>(y) + r * ldy + 2 * j;
+        yp[0] = __builtin_bit_cast(uint16_t, (__bf16)lo);
+        yp[1] = __builtin_bit_cast(uint16_t, (__bf16)hi);
+    } else {
+        float* yp = reinterpret_cast<float*>(y) + r * ldy + 2 * j;
+        yp[0] = lo;
+        yp[1] = hi;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+template <int FMT, bool BF16, bool G1>
+static hipError_t launch_quantize_fmt(const QuantArgs& a, hipStream_t st)
+{
+    if (a.fast) {
+        const uint32_t gpr = (uint32_t)(a.k / 32);
+        const uint32_t total = (uint32_t)(a.rows * gpr);
+        const dim3 grid((total + kThreads - 1) / kThreads);
+        const int64_t ldb = a.ldx * (BF16 ? 2 : 4);
+        switch (a.block) {
+#define MXQ(B) case B: hipLaunchKernelGGL((quantize_fast_kernel<B, FMT, BF16, G1>), grid, dim3(kThreads), 0, st, \
+                   (const uint8_t*)a.x, ldb, gpr, total, a.g, a.codes, a.scales, a.k); break;
+            MXQ(4) MXQ(8) MXQ(16) MXQ(32) MXQ(64) MXQ(128) MXQ(256)
+#undef MXQ
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        const int64_t n = a.rows * (a.k / a.block);
+        const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+        hipLaunchKernelGGL((quantize_generic_kernel<FMT, BF16, G1>), grid, dim3(kThreads), 0, st,
+                           (const uint8_t*)a.x, a.ldx, a.rows, a.k, a.block, a.g, a.codes, a.scales);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t st)
+{
+    const bool g1 = a.g == 1.0;
+#define MXF(F) \
+    if (a.fmt == F) { \
+        if (a.bf16) return g1 ? launch_quantize_fmt<F, true, true>(a, st) : launch_quantize_fmt<F, true, false>(a, st); \
+        return g1 ? launch_quantize_fmt<F, false, true>(a, st) : launch_quantize_fmt<F, false, false>(a, st); \
+    }
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, bool G1, bool OUT_BF16>
+static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
+{
+    if (a.fast) {
+        const uint32_t gpr = (uint32_t)(a.k / 32);
+        const uint32_t total = (uint32_t)(a.rows * gpr);
+        const dim3 grid((total + kThreads - 1) / kThreads);
+        const int64_t ldb = a.ldy * (OUT_BF16 ? 2 : 4);
+        switch (a.block) {
+#define MXD(B) case B: hipLaunchKernelGGL((dequantize_fast_kernel<B, FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st, \
+                   a.codes, a.scales, gpr, total, a.k, a.g, (uint8_t*)a.y, ldb); break;
+            MXD(4) MXD(8) MXD(16) MXD(32) MXD(64) MXD(128) MXD(256)
+#undef MXD
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        const int64_t n = a.rows * (a.k / 2);
+        const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
+        hipLaunchKernelGGL((dequantize_generic_kernel<FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st,
+                           a.codes, a.scales, a.rows, a.k, a.block, a.g, (uint8_t*)a.y, a.ldy);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st)
+{
+    const bool g1 = a.g == 1.0;
+#define MXF(F) \
+    if (a.fmt == F) { \
+        if (a.bf16) return g1 ? launch_dequantize_fmt<F, true, true>(a, st) : launch_dequantize_fmt<F, false, true>(a, st); \
+        return g1 ? launch_dequantize_fmt<F, true, false>(a, st) : launch_dequantize_fmt<F, false, false>(a, st); \
+    }
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mxk

@@ -155,3 +155,15 @@ def c5_weight(row0=0, nrows=None):
     """405B FFN weight 53248 x 16384 bf16: 16 contiguous row bands of 3328 rows; bands with
     index 3 mod 4 at sigma 0.02 (the narrow layers mixed in), the rest at 0.01."""
     return banded_bf16((53248, 16384), "c5.w", 16, 4, 3, 0.01, 0.02, row0=row0, nrows=nrows)
+
+
+def absmax_bf16(a: np.ndarray) -> float:
+    """max |x| of a bf16-bits array (the largest magnitude bit pattern)."""
+    m = np.uint16(np.max(a & np.uint16(0x7FFF)))
+    return float(bf16_to_f32(np.array([m], dtype=np.uint16))[0])
+
+
+def c5_tensor_scale(w: np.ndarray) -> float:
+    """Per-tensor scale of the 405B FFN weight: g = fl32(max|W| / (6 * 114688)), which puts the
+    largest block's UE5M3 scale at the top of the format's range."""
+    return float(np.float32(absmax_bf16(w) / (6.0 * 114688.0)))

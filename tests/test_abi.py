@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: libmx.so loads, exports exactly what include/mx.h declares,
+and rejects invalid arguments on the host with the documented status (nothing is launched
+on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN = 0, -1, -2, -3
+E4M3, UE5M3, E8M0 = 0, 1, 2
+F32, BF16 = 0, 1
+A16, A4 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def L():
+    import microscaling_fp4_weight_amd as mx
+    return mx.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(mx_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_match_header(L):
+    names = declared_functions()
+    assert names == ["mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_quantize",
+                     "mx_status_string"]
+    for n in names:
+        assert hasattr(L, n)
+    so = os.path.join(ROOT, "microscaling_fp4_weight_amd", "libmx.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", so], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r" T (mx_\w+)$", out, re.M)))
+    assert exported == names
+
+
+def test_status_strings(L):
+    for s in (OK, INVALID, UNSUPPORTED, ALIGN, -4):
+        assert L.mx_status_string(s)
+    assert L.mx_status_string(OK) == b"success"
+
+
+FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize("args,status", [
+    # (x, x_type, rows, k, ld_x, block, fmt, g, layout, codes, scales) -> status
+    ((FAKE, BF16, 4, 33, 33, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # k odd / k % block
+    ((FAKE, BF16, 4, 48, 48, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # k % block
+    ((FAKE, BF16, 4, 64, 64, 12, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # block not listed
+    ((FAKE, BF16, 4, 64, 64, 512, E8M0, 1.0, 0, FAKE, FAKE), INVALID),
+    ((FAKE, BF16, -1, 64, 64, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),    # negative rows
+    ((FAKE, BF16, 4, 64, 32, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # ld < k
+    ((FAKE, 7, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),        # dtype
+    ((FAKE, BF16, 4, 64, 64, 32, 3, 1.0, 0, FAKE, FAKE), INVALID),        # fmt
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 1, FAKE, FAKE), INVALID),     # layout
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 0.0, 0, FAKE, FAKE), INVALID),     # g = 0
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, -1.0, 0, FAKE, FAKE), INVALID),    # g < 0
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, float("inf"), 0, FAKE, FAKE), INVALID),
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, float("nan"), 0, FAKE, FAKE), INVALID),
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1e-40, 0, FAKE, FAKE), INVALID),   # subnormal g
+    ((None, BF16, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # null x
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 0, None, FAKE), INVALID),
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE, None), INVALID),
+    ((FAKE + 8, BF16, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE, FAKE), ALIGN),   # misaligned
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE + 1, FAKE), ALIGN),
+    ((None, BF16, 0, 64, 64, 32, E8M0, 1.0, 0, None, None), OK),          # empty: no launch
+    ((None, BF16, 5, 0, 0, 32, E8M0, 1.0, 0, None, None), OK),
+])
+def test_quantize_validation(L, args, status):
+    assert L.mx_quantize(*args, None) == status
+
+
+def test_dequantize_validation(L):
+    # (codes, scales, rows, k, block, fmt, g, layout, y, y_type, ld_y)
+    assert L.mx_dequantize(FAKE, FAKE, 4, 64, 32, E8M0, 1.0, 0, FAKE, 9, 64, None) == INVALID
+    assert L.mx_dequantize(FAKE, FAKE, 4, 64, 32, E8M0, 1.0, 0, FAKE, F32, 63, None) == INVALID
+    assert L.mx_dequantize(FAKE, FAKE, 4, 60, 8, E8M0, 1.0, 0, FAKE, F32, 64, None) == INVALID
+    assert L.mx_dequantize(FAKE, None, 4, 64, 32, E8M0, 1.0, 0, FAKE, F32, 64, None) == INVALID
+    assert L.mx_dequantize(FAKE, FAKE, 4, 64, 32, E8M0, 1.0, 0, FAKE + 4, F32, 64, None) == ALIGN
+    assert L.mx_dequantize(None, None, 0, 64, 32, E8M0, 1.0, 0, None, F32, 64, None) == OK
+
+
+def test_gemm_validation_and_workspace(L):
+    ws = L.mx_gemm_workspace_size
+    assert ws(2048, 28672, 8192, 32, A16) == 0
+    assert ws(2048, 28672, 8192, 32, A4) == 2048 * 4096 + 2048 * 256
+    assert ws(3, 5, 64, 32, A4) == 256 + 256  # each part rounded up to 256 bytes
+    assert ws(3, 5, 64, 16, A4) == 0          # W4A4 needs block 32
+    assert ws(3, 5, 63, 32, A4) == 0
+
+    def gemm(m=4, n=8, k=64, ldx=64, block=32, fmt=E8M0, g=1.0, mode=A16, yt=F32, ldy=8,
+             work=None, wbytes=0, x=FAKE, wc=FAKE, wsc=FAKE, y=FAKE):
+        return L.mx_gemm(x, m, n, k, ldx, wc, wsc, block, fmt, g, 0, mode, y, yt, ldy, work,
+                         wbytes, None)
+
+    assert gemm(mode=A4, fmt=E4M3) == UNSUPPORTED      # W4A4 is E8M0-only
+    assert gemm(mode=A4, block=64) == UNSUPPORTED      # and block 32 only
+    assert gemm(mode=A4, work=FAKE, wbytes=100) == INVALID   # workspace too small
+    assert gemm(mode=A4, work=None, wbytes=0) == INVALID
+    assert gemm(ldy=7) == INVALID
+    assert gemm(ldx=63) == INVALID
+    assert gemm(k=48) == INVALID                       # k % block
+    assert gemm(mode=2) == INVALID
+    assert gemm(yt=5) == INVALID
+    assert gemm(g=0.0) == INVALID
+    assert gemm(y=None) == INVALID
+    assert gemm(y=FAKE + 2) == ALIGN
+    assert gemm(wsc=FAKE + 8) == ALIGN
+    assert gemm(m=0, x=None, y=None) == OK
+    assert gemm(n=0, wc=None, wsc=None, y=None) == OK
+    assert gemm(k=0, y=FAKE + 2) == ALIGN

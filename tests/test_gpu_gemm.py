@@ -1,0 +1,244 @@
+"""GPU parity: mx_gemm (W4A16 and W4A4) through the C ABI against the fp64 CPU oracle.
+
+Tolerance (fixed by the benchmark spec for the matmul): |Y - Yref| <= 2e-5 * sum_k |x_k w_k|
+on the fp32 output; bf16 output adds half a bf16 ulp of Yref (its own rounding).  Cases:
+decode GEMV M in {1, 4, 16} and prefill GEMM with ragged M/N/K tails for every block size
+and format, the generic path, k = 0, W4A4 (activation pre-pass bit-identical to
+mx_quantize, then block-scaled FP4 MFMA), and the full-size workloads -- tiny round trip,
+decode shapes, 70B-FFN prefill, 405B-FFN with two-level scaling -- on sampled outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_fp4_weight_amd as mx
+import oracle
+import synth
+from gpu_util import DEV, assert_gemm_close, bf16_dev, f32_dev, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["e4m3", "ue5m3", "e8m0"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mx.lib()
+
+
+def quantize_ref(w, block, fmt, g=1.0):
+    """Oracle weight quantization -> host arrays and device copies."""
+    c, s = oracle.quantize(w, block, fmt, g)
+    return c, s, torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV)
+
+
+def check(x, c, s, cd, sd, block, fmt, g, mode, out, rows=None, cols=None, what=""):
+    xd = bf16_dev(x)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = mx.mx_gemm(xd, cd, sd, block, fmt, g, mode, out_dtype=dt)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm(x, c, s, block, fmt, g, mode, mrows=rows, ncols=cols)
+    got = to_host_bits(y.float())
+    if rows is not None:
+        got = got[rows]
+    if cols is not None:
+        got = got[:, cols]
+    assert_gemm_close(got, yref, aref, out == "bf16", what or f"{mode} {fmt} B={block} {out}")
+    return y
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [4, 8, 16, 32, 64, 128, 256])
+def test_gemv_a16(m, fmt, block):
+    n, k = 100, 768  # ragged n; k = 6 k-tiles, split over 4 waves unevenly
+    x = synth.normal((m, k), "bf16", f"gv.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", "gv.w", 0.02, 0.01, 20.0)
+    c, s, cd, sd = quantize_ref(w, block, fmt)
+    for out in ("f32", "bf16"):
+        check(x, c, s, cd, sd, block, fmt, 1.0, "a16", out)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [4, 16, 32, 128])
+def test_gemm_a16_ragged(fmt, block):
+    m, n, k = 200, 300, 640  # 2 x 3 workgroup tiles, all ragged; k-tail of 128
+    x = synth.normal((m, k), "bf16", "gg.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gg.w", 0.02, 0.01, 20.0)
+    c, s, cd, sd = quantize_ref(w, block, fmt)
+    for out in ("f32", "bf16"):
+        check(x, c, s, cd, sd, block, fmt, 1.0, "a16", out)
+
+
+def test_gemm_a16_k_tail_32():
+    m, n, k = 40, 70, 160  # k % 128 == 32
+    x = synth.normal((m, k), "bf16", "gt.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gt.w", 0.02)
+    for m_ in (5, 40):
+        c, s, cd, sd = quantize_ref(w, 32, "e8m0")
+        check(x[:m_], c, s, cd, sd, 32, "e8m0", 1.0, "a16", "f32")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_tensor_scale(fmt):
+    g = float(np.float32(0.0173))
+    m, n, k = 33, 64, 256
+    x = synth.normal((m, k), "bf16", "gs.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gs.w", 0.02, 0.01, 20.0)
+    c, s, cd, sd = quantize_ref(w, 32, fmt, g)
+    check(x, c, s, cd, sd, 32, fmt, g, "a16", "f32")
+    check(x[:3], c, s, cd, sd, 32, fmt, g, "a16", "bf16")
+
+
+def test_gemm_generic_path():
+    # k = 48 is not a multiple of 32: the generic kernel; an odd activation stride too
+    m, n, k = 7, 9, 48
+    x = synth.normal((m, k), "bf16", "gp.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gp.w", 0.02)
+    for fmt in FMTS:
+        c, s, cd, sd = quantize_ref(w, 16, fmt)
+        check(x, c, s, cd, sd, 16, fmt, 1.0, "a16", "f32")
+    big = synth.normal((m, 75), "bf16", "gp.ld", 1.0)
+    xd = bf16_dev(big)[:, :64]
+    w2 = synth.normal((n, 64), "bf16", "gp.w2", 0.02)
+    c, s, cd, sd = quantize_ref(w2, 32, "e8m0")
+    y = mx.mx_gemm(xd, cd, sd, 32, "e8m0", 1.0, "a16", out_dtype=torch.float32)
+    yref, aref = oracle.gemm(np.ascontiguousarray(big[:, :64]), c, s, 32, "e8m0")
+    assert_gemm_close(to_host_bits(y), yref, aref, False, "strided x")
+
+
+def test_gemm_k_zero_writes_zeros():
+    x = torch.empty((3, 0), dtype=torch.bfloat16, device=DEV)
+    cd = torch.empty((5, 0), dtype=torch.uint8, device=DEV)
+    sd = torch.empty((5, 0), dtype=torch.uint8, device=DEV)
+    y = torch.full((3, 5), 7.0, dtype=torch.float32, device=DEV)
+    mx.mx_gemm(x, cd, sd, 32, "e8m0", 1.0, "a16", y=y)
+    assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("mnk", [(1, 64, 128), (16, 96, 256), (200, 300, 640), (129, 257, 160)])
+def test_gemm_a4(mnk):
+    m, n, k = mnk
+    x = synth.normal((m, k), "bf16", f"ga.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", "ga.w", 0.015, 0.001, 20.0)
+    c, s, cd, sd = quantize_ref(w, 32, "e8m0")
+    for out in ("f32", "bf16"):
+        check(x, c, s, cd, sd, 32, "e8m0", 1.0, "a4", out)
+
+
+def test_gemm_a4_prepass_matches_quantize():
+    """The activations quantized inside mx_gemm (workspace) are byte-identical to
+    mx_quantize(X, 32, E8M0) and to the oracle."""
+    m, n, k = 37, 64, 512
+    x = synth.normal((m, k), "bf16", "gw.x", 1.0, 0.01, 20.0)
+    w = synth.normal((n, k), "bf16", "gw.w", 0.02)
+    c, s, cd, sd = quantize_ref(w, 32, "e8m0")
+    xd = bf16_dev(x)
+    need = mx.mx_gemm_workspace_size(m, n, k, 32, "a4")
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    mx.mx_gemm(xd, cd, sd, 32, "e8m0", 1.0, "a4", workspace=ws)
+    torch.cuda.synchronize()
+    wsh = to_host_bits(ws)
+    codes = wsh[: m * k // 2].reshape(m, k // 2)
+    off = (m * k // 2 + 255) // 256 * 256
+    scales = wsh[off: off + m * k // 32].reshape(m, k // 32)
+    rc, rs = oracle.quantize(x, 32, "e8m0")
+    np.testing.assert_array_equal(codes, rc)
+    np.testing.assert_array_equal(scales, rs)
+    qc, qs = mx.mx_quantize(xd, 32, "e8m0")
+    np.testing.assert_array_equal(to_host_bits(qc), codes)
+    np.testing.assert_array_equal(to_host_bits(qs), scales)
+
+
+# ------------------------------------------------------------------------ full-size workloads
+
+def test_c1_tiny_round_trip_and_gemv():
+    """256 x 256 fp32 weight ~ N(0, 0.02^2) with 1% outliers x20, block 32 E4M3, g = 1:
+    quantize -> dequantize bit-exact; y = W^ x within tolerance; error split reported."""
+    w = synth.c1_weight()
+    x = synth.c1_x()
+    c, s = mx.mx_quantize(f32_dev(w), 32, "e4m3")
+    rc, rs = oracle.quantize(w, 32, "e4m3")
+    np.testing.assert_array_equal(to_host_bits(c), rc)
+    np.testing.assert_array_equal(to_host_bits(s), rs)
+    y = mx.mx_dequantize(c, s, 256, 32, "e4m3", out_dtype=torch.float32)
+    np.testing.assert_array_equal(to_host_bits(y).view(np.uint32),
+                                  oracle.dequantize(rc, rs, 256, 32, "e4m3").view(np.uint32))
+    for out in ("f32", "bf16"):
+        check(x, rc, rs, c, s, 32, "e4m3", 1.0, "a16", out, what=f"C1 gemv {out}")
+    split = oracle.mse_split(w, 32, "e4m3")
+    assert split["total"] > 0
+
+
+@pytest.mark.parametrize("n", [4096, 14336])
+def test_c3_decode_gemv(n):
+    """Decode GEMV K=4096, N in {4096, 14336}, M in {1, 4, 16}; block 32 E8M0; bf16 out."""
+    w = synth.c3_weight(n)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize(wd, 32, "e8m0")
+    cols = np.unique(np.concatenate([np.arange(0, n, 97), [n - 1]]))
+    c = to_host_bits(cd[cols])
+    s = to_host_bits(sd[cols])
+    rc, rs = oracle.quantize(w[cols], 32, "e8m0")
+    np.testing.assert_array_equal(c, rc)
+    np.testing.assert_array_equal(s, rs)
+    for m in (1, 4, 16):
+        x = synth.c3_x(m)
+        y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "e8m0", 1.0, "a16", out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        yref, aref = oracle.gemm(x, rc, rs, 32, "e8m0", 1.0, "a16")
+        assert_gemm_close(to_host_bits(y.float())[:, cols], yref, aref, True, f"C3 n={n} m={m}")
+
+
+def _c4_setup():
+    w = synth.c4_weight()
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize(wd, 32, "e8m0")
+    del wd
+    cols = np.array([0, 1, 5000, 14335, 20000, 28671])
+    rows = np.array([0, 1, 700, 1500, 2047])
+    rc, rs = oracle.quantize(w[cols], 32, "e8m0")
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
+    return cd, sd, rc, rs, rows, cols
+
+
+@pytest.mark.parametrize("mode", ["a16", "a4"])
+def test_c4_prefill(mode):
+    """70B FFN prefill M=2048, K=8192, N=28672, block 32 E8M0: W4A16 and W4A4."""
+    cd, sd, rc, rs, rows, cols = _c4_setup()
+    x = synth.c4_x()
+    y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "e8m0", 1.0, mode, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm(x[rows], rc, rs, 32, "e8m0", 1.0, mode)
+    assert_gemm_close(to_host_bits(y[rows][:, cols]), yref, aref, False, f"C4 {mode}")
+
+
+@pytest.fixture(scope="module")
+def c5_weights():
+    w = synth.c5_weight()
+    g = synth.c5_tensor_scale(w)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize(wd, 32, "ue5m3", g)
+    del wd
+    cols = np.array([0, 3328 * 3 + 5, 26000, 53247])
+    rc, rs = oracle.quantize(w[cols], 32, "ue5m3", g)
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    return cd, sd, rc, rs, cols, g
+
+
+@pytest.mark.parametrize("m", [1, 256, 4096])
+def test_c5_two_level(m, c5_weights):
+    """405B FFN K=16384, N=53248, UE5M3 block 32 with per-tensor g; W4A16, fp32 accumulate,
+    bf16 out (fp32 out also checked for M=1)."""
+    cd, sd, rc, rs, cols, g = c5_weights
+    x = synth.c5_x(m)
+    rows = np.unique(np.array([0, m // 2, m - 1]))
+    for out in (("f32", "bf16") if m == 1 else ("bf16",)):
+        dt = torch.float32 if out == "f32" else torch.bfloat16
+        y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "ue5m3", g, "a16", out_dtype=dt)
+        torch.cuda.synchronize()
+        yref, aref = oracle.gemm(x[rows], rc, rs, 32, "ue5m3", g, "a16")
+        assert_gemm_close(to_host_bits(y.float())[rows][:, cols], yref, aref, out == "bf16",
+                          f"C5 m={m} {out}")

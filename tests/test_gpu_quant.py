@@ -1,0 +1,181 @@
+"""GPU parity: mx_quantize / mx_dequantize through the C ABI against the CPU oracle.
+
+Codes and scale bytes must be bit-exact; dequantized values bit-exact.  Cases: every block
+size x scale format x input dtype on small tensors spanning several workgroups with a
+ragged tail; the edge-case tensor (every scale byte, every bf16 magnitude to 6, exact ties,
+zero / flush / saturating / subnormal blocks); shapes that take the generic path (k not a
+multiple of 32, odd row stride); empty tensors; a per-tensor scale; and the full-size
+Llama-7B FFN (4096 x 11008) and 405B FFN (53248 x 16384) weights in the launch
+configuration the benchmark times, on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_fp4_weight_amd as mx
+import oracle
+import synth
+from gpu_util import DEV, bf16_dev, edge_tensor, f32_dev, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["e4m3", "ue5m3", "e8m0"]
+BLOCKS = [4, 8, 16, 32, 64, 128, 256]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mx.lib()
+
+
+def run_quant(x_host: np.ndarray, block: int, fmt: str, g: float = 1.0):
+    xd = bf16_dev(x_host) if x_host.dtype == np.uint16 else f32_dev(x_host)
+    c, s = mx.mx_quantize(xd, block, fmt, g)
+    torch.cuda.synchronize()
+    return to_host_bits(c), to_host_bits(s)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", BLOCKS)
+def test_quantize_small(dtype, fmt, block):
+    # 37 rows x 1280: 1480 lanes of 32 elements -> 6 workgroups, the last one partial
+    x = synth.normal((37, 1280), dtype, f"gq.{dtype}", 0.02, 0.01, 20.0)
+    c, s = run_quant(x, block, fmt)
+    rc, rs = oracle.quantize(x, block, fmt)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", BLOCKS)
+def test_quantize_edge_tensor(fmt, block):
+    x = edge_tensor()
+    c, s = run_quant(x, block, fmt)
+    rc, rs = oracle.quantize(x, block, fmt)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+    # and as fp32 input
+    xf = synth.bf16_to_f32(x)
+    c2, s2 = run_quant(xf, block, fmt)
+    np.testing.assert_array_equal(s2, rs)
+    np.testing.assert_array_equal(c2, rc)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("g", [0.37, 2.0 ** -7, 1234.5])
+def test_quantize_tensor_scale(fmt, g):
+    g = float(np.float32(g))
+    x = synth.normal((19, 1024), "bf16", "gq.g", 0.3, 0.01, 20.0)
+    x = np.concatenate([x, edge_tensor(1024)[:40]])
+    for block in (4, 32, 256):
+        c, s = run_quant(x, block, fmt, g)
+        rc, rs = oracle.quantize(x, block, fmt, g)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(c, rc)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_generic_path(fmt):
+    # k = 48 (not a multiple of 32) and an odd row stride both take the generic kernel
+    x = synth.normal((33, 48), "bf16", "gq.gen", 0.05, 0.01, 20.0)
+    for block in (4, 8, 16):
+        c, s = run_quant(x, block, fmt)
+        rc, rs = oracle.quantize(x, block, fmt)
+        np.testing.assert_array_equal(s, rs)
+        np.testing.assert_array_equal(c, rc)
+    big = synth.normal((9, 263), "bf16", "gq.ld", 0.05, 0.01, 20.0)
+    xd = bf16_dev(big)[:, :256]  # row stride 263 elements
+    c, s = mx.mx_quantize(xd, 32, fmt)
+    rc, rs = oracle.quantize(np.ascontiguousarray(big[:, :256]), 32, fmt)
+    np.testing.assert_array_equal(to_host_bits(s), rs)
+    np.testing.assert_array_equal(to_host_bits(c), rc)
+
+
+def test_quantize_empty():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    c, s = mx.mx_quantize(x, 32, "e8m0")
+    assert c.shape == (0, 32) and s.shape == (0, 2)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [4, 16, 32, 128])
+@pytest.mark.parametrize("g", [1.0, 0.37])
+def test_dequantize(out, fmt, block, g):
+    g = float(np.float32(g))
+    x = np.concatenate([synth.normal((21, 512), "bf16", "gd", 0.02, 0.01, 20.0), edge_tensor(512)[:64]])
+    rc, rs = oracle.quantize(x, block, fmt, g)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = mx.mx_dequantize(torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV), 512, block,
+                         fmt, g, out_dtype=dt)
+    ref = oracle.dequantize(rc, rs, 512, block, fmt, g, out)
+    got = to_host_bits(y)
+    if out == "f32":
+        np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_dequantize_all_scale_bytes():
+    # every code with every scale byte (including those whose products overflow)
+    for fmt in FMTS:
+        codes = np.tile(np.arange(256, dtype=np.uint8), 256).reshape(256, 256)  # 512 elems/row
+        scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 512 // 32, axis=1)
+        ok = np.array([np.isfinite(oracle.scale_value(b, fmt)) for b in range(256)])
+        codes, scales = codes[ok], scales[ok]
+        for out in ("f32", "bf16"):
+            dt = torch.float32 if out == "f32" else torch.bfloat16
+            y = mx.mx_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                                 512, 32, fmt, 1.0, out_dtype=dt)
+            ref = oracle.dequantize(codes, scales, 512, 32, fmt, 1.0, out)
+            got = to_host_bits(y)
+            if out == "f32":
+                np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+            else:
+                np.testing.assert_array_equal(got, ref)
+
+
+def test_quantize_deterministic():
+    x = synth.normal((64, 4096), "bf16", "gq.det", 0.02, 0.01, 20.0)
+    xd = bf16_dev(x)
+    a = [to_host_bits(t) for t in mx.mx_quantize(xd, 16, "ue5m3")]
+    b = [to_host_bits(t) for t in mx.mx_quantize(xd, 16, "ue5m3")]
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
+SAMPLE_ROWS_C2 = [0, 1, 777, 2048, 3001, 4094, 4095]
+
+
+@pytest.mark.parametrize("sigma", synth.C2_SIGMAS)
+def test_c2_full_size_sampled(sigma):
+    """Llama-7B FFN weight 4096 x 11008 bf16, every block size and format, as the benchmark
+    launches it; rows compared with the oracle on a sample."""
+    w = synth.c2_weight(sigma)
+    wd = bf16_dev(w)
+    for fmt in FMTS:
+        for block in BLOCKS:
+            c, s = mx.mx_quantize(wd, block, fmt)
+            rows = SAMPLE_ROWS_C2
+            rc, rs = oracle.quantize(w[rows], block, fmt)
+            np.testing.assert_array_equal(to_host_bits(s[rows]), rs, err_msg=f"{fmt} B={block}")
+            np.testing.assert_array_equal(to_host_bits(c[rows]), rc, err_msg=f"{fmt} B={block}")
+            y = mx.mx_dequantize(c, s, 11008, block, fmt, 1.0, out_dtype=torch.bfloat16)
+            np.testing.assert_array_equal(to_host_bits(y[rows]),
+                                          oracle.dequantize(rc, rs, 11008, block, fmt, 1.0, "bf16"))
+    del wd
+
+
+def test_c5_full_size_two_level_sampled():
+    """405B FFN weight 53248 x 16384 bf16, UE5M3 block 32 times a per-tensor scale
+    g = fl32(max|W| / (6 * 114688)); sampled rows bit-exact, including the narrow bands."""
+    w = synth.c5_weight()
+    g = synth.c5_tensor_scale(w)
+    wd = bf16_dev(w)
+    c, s = mx.mx_quantize(wd, 32, "ue5m3", g)
+    rows = [0, 3327, 3328 * 3, 3328 * 3 + 17, 26000, 3328 * 15, 53247]
+    rc, rs = oracle.quantize(w[rows], 32, "ue5m3", g)
+    np.testing.assert_array_equal(to_host_bits(s[rows]), rs)
+    np.testing.assert_array_equal(to_host_bits(c[rows]), rc)
