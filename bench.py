@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of the MX FP4 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+
+One step = the whole block-size/scale sweep on the Llama-7B FFN-shaped weight
+(4096 x 11008 bf16 ~ N(0, sigma^2), 0.1% entries x20): for every sigma in {0.005, 0.02, 0.1},
+block in {4, 8, 16, 32, 64, 128, 256} and scale format in {E4M3, UE5M3, E8M0}, one MX quantize
+(bf16 -> codes + scales) and one dequantize (codes + scales -> bf16): 126 launches.  Inputs
+and outputs rotate over > 512 MB of distinct buffers so every launch reads HBM, not the
+256 MB Infinity Cache.  `value` is the algorithmic bytes of a step divided by its time.
+
+The remaining rows of the hot path are measured in the same run (`rows`): decode GEMV
+(M in {1,4,16}, K 4096, N in {4096, 14336}, block 32 E8M0, bf16 out, back-to-back over
+distinct weight copies), 70B-FFN prefill GEMM (2048 x 8192 x 28672) in W4A16 and W4A4, and
+the 405B-FFN shapes with two-level UE5M3 scaling (offline weight quantize; GEMV M=1; GEMM
+M=256, 4096).  `roofline` is for the dominant kernel, the B=32 E8M0 quantize; `cpu_baseline`
+times the single-threaded CPU oracle on a bounded sample of the same sweep.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MX quantize GB/s; MXFP4 GEMV/GEMM TFLOP/s (% of HBM / MFMA roofline)"
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # dense bf16 MFMA FLOP/s
+PEAK_FP4 = 10.1e15         # dense fp4 MFMA FLOP/s
+FMTS = ("e4m3", "ue5m3", "e8m0")
+BLOCKS = (4, 8, 16, 32, 64, 128, 256)
+SIGMAS = (0.005, 0.02, 0.1)
+C2_ROWS, C2_K = 4096, 11008
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def quant_bytes(n: int, block: int, in_bytes: int = 2) -> int:
+    """Algorithmic HBM bytes of one quantize (or dequantize to the same dtype) of n elements:
+    read the dense tensor, write n/2 code bytes and n/block scale bytes."""
+    return n * in_bytes + n // 2 + n // block
+
+
+def gemv_bytes(m: int, n: int, k: int, block: int) -> int:
+    return n * k // 2 + n * k // block + 2 * m * k + 2 * m * n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="skip the GEMV/GEMM rows")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
+              "build has no multi-GPU path (see the sharding note in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import microscaling_fp4_weight_amd as mx
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = mx.lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    # ---------------------------------------------------------------- C2 sweep setup
+    t0 = time.time()
+    inputs = []
+    for sigma in SIGMAS:
+        w = synth.c2_weight(sigma)
+        wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)
+        inputs.append(wd)
+        inputs.append(wd.clone())  # two copies per sigma: six 90 MB inputs in rotation
+    n = C2_ROWS * C2_K
+    configs = [(si, b, f) for b in BLOCKS for f in FMTS for si in range(len(SIGMAS))]
+    codes = [torch.empty((C2_ROWS, C2_K // 2), dtype=torch.uint8, device=dev) for _ in configs]
+    scales = [torch.empty((C2_ROWS, C2_K // b), dtype=torch.uint8, device=dev) for (_, b, _) in configs]
+    deq_out = [torch.empty((C2_ROWS, C2_K), dtype=torch.bfloat16, device=dev) for _ in range(6)]
+    log(f"C2 setup {time.time() - t0:.1f}s: {len(configs)} configs")
+
+    qcalls, dcalls = [], []
+    step_bytes = 0
+    for i, (si, b, f) in enumerate(configs):
+        x = inputs[2 * si + (i // len(SIGMAS)) % 2]
+        qcalls.append((x.data_ptr(), 1, C2_ROWS, C2_K, C2_K, b, mx.FMT[f], 1.0, 0,
+                       codes[i].data_ptr(), scales[i].data_ptr(), sp))
+        dcalls.append((codes[i].data_ptr(), scales[i].data_ptr(), C2_ROWS, C2_K, b, mx.FMT[f], 1.0,
+                       0, deq_out[i % 6].data_ptr(), 1, C2_K, sp))
+        step_bytes += 2 * quant_bytes(n, b)
+    dom = next(i for i, c in enumerate(configs) if c[1] == 32 and c[2] == "e8m0")
+    q, dq = L.mx_quantize, L.mx_dequantize
+
+    def step(ev=None):
+        for i, c in enumerate(qcalls):
+            if ev is not None and i == dom:
+                ev[0].record(stream)
+            st = q(*c)
+            if ev is not None and i == dom:
+                ev[1].record(stream)
+            if st:
+                raise mx.MXError(st, "mx_quantize")
+        for c in dcalls:
+            st = dq(*c)
+            if st:
+                raise mx.MXError(st, "mx_dequantize")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    dom_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        step(dom_events[s])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom_ms = sorted(a.elapsed_time(b) for a, b in dom_events)
+    dom_avg_ms = sum(dom_ms) / len(dom_ms)
+    dom_bytes = quant_bytes(n, 32)
+    log(f"C2 sweep: {ms_per_step:.3f} ms/step, {value:.0f} GB/s; dominant kernel avg {dom_avg_ms * 1e3:.2f} us")
+
+    # per-config kernel times (one event pair per launch, outside the timed steps)
+    per_cfg = {}
+    for kind, calls, fn in (("quantize", qcalls, q), ("dequantize", dcalls, dq)):
+        evs = []
+        for rep in range(3):
+            for i, c in enumerate(calls):
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(*c)
+                b_.record(stream)
+                evs.append((i, a, b_))
+        torch.cuda.synchronize()
+        acc = {}
+        for i, a, b_ in evs:
+            acc.setdefault(i, []).append(a.elapsed_time(b_))
+        for i, ts in acc.items():
+            si, b, f = configs[i]
+            key = f"{kind}.B{b}.{f}"
+            per_cfg.setdefault(key, []).append(min(ts))
+    per_config = {}
+    for key, ts in per_cfg.items():
+        b = int(key.split(".")[1][1:])
+        t = sorted(ts)[len(ts) // 2]
+        gbs = quant_bytes(n, b) / (t * 1e-3) / 1e9
+        per_config[key] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
+                           "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3)}
+
+    # traffic counters (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE), taken from the committed
+    # profile when the quantize kernel's source has not changed since it was measured
+    traffic = load_traffic("quantize")
+
+    roofline = {"bound": "hbm", "kernel": "quantize_fast_kernel<32, E8M0, bf16, g=1>",
+                "achieved": round(dom_bytes / (dom_avg_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": round(dom_bytes / (dom_avg_ms * 1e-3) / PEAK_HBM, 4),
+                "traffic": traffic, "bytes_per_launch": dom_bytes,
+                "avg_launch_us": round(dom_avg_ms * 1e3, 3)}
+
+    # free the sweep buffers before the GEMM rows
+    del inputs, codes, scales, deq_out, qcalls, dcalls
+    torch.cuda.empty_cache()
+
+    rows = None if args.no_rows else measure_rows(mx, L, torch, np, synth, dev, stream)
+
+    cpu = None if args.no_cpu else cpu_baseline(np, synth)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b-ffn 4096x11008 bf16 block/scale sweep: 3 sigma x 7 blocks "
+                               "x 3 scale formats, quantize + dequantize (126 launches/step)",
+                   "rows": C2_ROWS, "k": C2_K, "sigmas": list(SIGMAS), "blocks": list(BLOCKS),
+                   "formats": list(FMTS), "bytes_per_step": step_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "per_config": per_config,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def load_traffic(kernel: str):
+    """Counter-derived HBM bytes per launch for `kernel` from profiles/traffic.json, or None
+    if absent or measured on a different source than the current one."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))[kernel]
+    except (KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "microscaling_fp4_weight_amd", "csrc", rec["source"])
+    dev_h = os.path.join(ROOT, "microscaling_fp4_weight_amd", "csrc", "mx_device.h")
+    h = hashlib.sha256(open(src, "rb").read() + open(dev_h, "rb").read()).hexdigest()[:16]
+    if h != rec.get("source_sha"):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def time_launches(torch, stream, launches, reps=1):
+    """Run each launch `reps` times back to back; returns per-launch durations (ms) from HIP
+    events on the launch stream."""
+    evs = []
+    for _ in range(reps):
+        for fn in launches:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def measure_rows(mx, L, torch, np, synth, dev, stream):
+    """The GEMV / GEMM / two-level rows of the hot path, each timed with HIP events."""
+    rows = {}
+    bf = torch.bfloat16
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
+
+    # decode GEMV: distinct weight copies (>= 512 MB) launched back to back
+    for nn, copies in ((4096, 64), (14336, 20)):
+        w = dev_bf16(synth.c3_weight(nn))
+        c0, s0 = mx.mx_quantize(w, 32, "e8m0")
+        del w
+        cs = [(c0.clone(), s0.clone()) for _ in range(copies)]
+        for m in (1, 4, 16):
+            x = dev_bf16(synth.c3_x(m))
+            y = torch.empty((m, nn), dtype=bf, device=dev)
+            launches = [lambda c=c, s=s: mx.mx_gemm(x, c, s, 32, "e8m0", 1.0, "a16", y=y)
+                        for c, s in cs]
+            time_launches(torch, stream, launches)  # warm-up
+            ts = time_launches(torch, stream, launches, reps=3)
+            tot = sum(ts) / 3
+            byt = gemv_bytes(m, nn, 4096, 32)
+            gbs = byt * copies / (tot * 1e-3) / 1e9
+            rows[f"gemv_a16.m{m}.n{nn}.k4096"] = {
+                "GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
+                "median_launch_us": round(sorted(ts)[len(ts) // 2] * 1e3, 2),
+                "TFLOP/s": round(2 * m * nn * 4096 * copies / (tot * 1e-3) / 1e12, 2)}
+        del cs, c0, s0
+        log(f"decode GEMV n={nn} done")
+
+    # 70B-FFN prefill: W4A16 and W4A4
+    w = dev_bf16(synth.c4_weight())
+    c4, s4 = mx.mx_quantize(w, 32, "e8m0")
+    del w
+    x = dev_bf16(synth.c4_x())
+    M, N, K = 2048, 28672, 8192
+    flops = 2 * M * N * K
+    y = torch.empty((M, N), dtype=bf, device=dev)
+    ws = torch.empty(mx.mx_gemm_workspace_size(M, N, K, 32, "a4"), dtype=torch.uint8, device=dev)
+    for mode, peak in (("a16", PEAK_BF16), ("a4", PEAK_FP4)):
+        fn = lambda: mx.mx_gemm(x, c4, s4, 32, "e8m0", 1.0, mode, y=y, workspace=ws)
+        time_launches(torch, stream, [fn], reps=2)
+        ts = time_launches(torch, stream, [fn], reps=5)
+        t = sorted(ts)[len(ts) // 2]
+        tf = flops / (t * 1e-3) / 1e12
+        rows[f"gemm_{mode}.m{M}.n{N}.k{K}"] = {"TFLOP/s": round(tf, 1),
+                                                "frac_peak": round(tf * 1e12 / peak, 4),
+                                                "peak_TFLOP/s": peak / 1e12, "ms": round(t, 3)}
+        log(f"C4 {mode}: {t:.3f} ms, {tf:.0f} TFLOP/s")
+    del c4, s4, x, y, ws
+    torch.cuda.empty_cache()
+
+    # 405B-FFN: offline two-level quantize, GEMV M=1, GEMM M=256 / 4096
+    wh = synth.c5_weight()
+    g = synth.c5_tensor_scale(wh)
+    w = dev_bf16(wh)
+    del wh
+    N, K = 53248, 16384
+    c5 = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    s5 = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    fn = lambda: mx.mx_quantize(w, 32, "ue5m3", g, codes=c5, scales=s5)
+    time_launches(torch, stream, [fn])
+    ts = time_launches(torch, stream, [fn], reps=3)
+    t = sorted(ts)[1]
+    gbs = quant_bytes(N * K, 32) / (t * 1e-3) / 1e9
+    rows["quantize.ue5m3.g.n53248.k16384"] = {"GB/s": round(gbs, 1),
+                                              "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
+                                              "ms": round(t, 3)}
+    del w
+    torch.cuda.empty_cache()
+    for m in (1, 256, 4096):
+        x = dev_bf16(synth.c5_x(m))
+        y = torch.empty((m, N), dtype=bf, device=dev)
+        fn = lambda: mx.mx_gemm(x, c5, s5, 32, "ue5m3", g, "a16", y=y)
+        time_launches(torch, stream, [fn])
+        ts = time_launches(torch, stream, [fn], reps=3)
+        t = sorted(ts)[1]
+        tf = 2 * m * N * K / (t * 1e-3) / 1e12
+        ent = {"TFLOP/s": round(tf, 2), "ms": round(t, 3)}
+        if m == 1:
+            gbs = gemv_bytes(1, N, K, 32) / (t * 1e-3) / 1e9
+            ent.update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3)})
+        else:
+            ent.update({"frac_peak_bf16": round(tf * 1e12 / PEAK_BF16, 4)})
+        rows[f"gemm_a16.ue5m3.g.m{m}.n{N}.k{K}"] = ent
+        log(f"C5 m={m}: {t:.3f} ms")
+        del x, y
+    del c5, s5
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(np, synth):
+    """The CPU oracle as it stands (single-threaded C, fp64) on a bounded sample of the
+    sweep: the first 192 of 4096 rows of each sigma's weight, every block size and format,
+    quantize + dequantize."""
+    import oracle
+    sample_rows = 192
+    t0 = time.perf_counter()
+    byt = 0
+    for sigma in SIGMAS:
+        w = synth.c2_weight(sigma, row0=0, nrows=sample_rows)
+        for b in BLOCKS:
+            for f in FMTS:
+                c, s = oracle.quantize(w, b, f)
+                oracle.dequantize(c, s, C2_K, b, f, 1.0, "bf16")
+                byt += 2 * quant_bytes(sample_rows * C2_K, b)
+    dt = time.perf_counter() - t0
+    log(f"cpu oracle sample: {dt:.1f}s")
+    return {"value": round(byt / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{sample_rows} of {C2_ROWS} rows of each sigma's 4096x11008 weight, all 63 "
+                      "(sigma, block, format) quantize + dequantize, single-threaded C oracle"}
+
+
+if __name__ == "__main__":
+    main()

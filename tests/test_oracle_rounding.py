@@ -180,3 +180,18 @@ def test_scale_of_fl32_quotient_is_exact(ox, fmt):
     exact = ox.scale_bytes(a.astype(np.float64), 1.0, fmt)
     via_q = ox.scale_bytes(6.0 * q.astype(np.float64), 1.0, fmt)
     np.testing.assert_array_equal(exact, via_q)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e8m0"])
+def test_scale_of_f64_reciprocal_product_is_exact(ox, fmt):
+    """Rounding fl32(fl64(a) * fl64(1/6)) onto the scale format also gives the byte of the
+    exact a/6 (the product lands on a midpoint exactly when a/6 does, and otherwise stays far
+    enough from it); the GPU scale path computes the quotient this way."""
+    vals = np.array([ox.scale_value(b, fmt) for b in range(0x7F if fmt == "e4m3" else 0xFF)])
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    mids = mids[(6 * mids < 3e38) & (6 * mids > 1e-37)]
+    a = np.concatenate([around(6.0 * mids, 512), _f32_range(1e-36, 3e38, 104729)]).astype(np.float32)
+    q = (a.astype(np.float64) * (1.0 / 6.0)).astype(np.float32)
+    exact = ox.scale_bytes(a.astype(np.float64), 1.0, fmt)
+    via_q = ox.scale_bytes(6.0 * q.astype(np.float64), 1.0, fmt)
+    np.testing.assert_array_equal(exact, via_q)
