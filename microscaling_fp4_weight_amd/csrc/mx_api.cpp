@@ -23,6 +23,18 @@ mx_status from_hip(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; 
 
 constexpr size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Large tensors are processed in row chunks so that every launch indexes fewer than 2^29
+// work units (the kernels use 32-bit unit indices and grid sizes); k itself is bounded.
+constexpr int64_t kMaxUnitsPerLaunch = int64_t(1) << 29;
+constexpr int64_t kMaxK = int64_t(1) << 25;  // keeps per-workgroup buffer ranges below 2^31 bytes
+
+int64_t chunk_rows(int64_t k)
+{
+    const int64_t per_row = k / 2 > 1 ? k / 2 : 1;  // finest unit of any kernel: an element pair
+    const int64_t r = kMaxUnitsPerLaunch / per_row;
+    return r > 0 ? r : 1;
+}
+
 // Common checks of a quantized tensor description.
 mx_status check_quantized(int64_t rows, int64_t k, int block, mx_scale_fmt fmt, float g,
                           mx_layout layout)
@@ -64,7 +76,7 @@ mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, i
     if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
     const int esize = x_type == MX_BF16 ? 2 : 4;
-    if (rows * (k / 32) > INT32_MAX - 1024) return MX_ERR_UNSUPPORTED;
+    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
     mxk::QuantArgs a;
     a.x = x;
     a.bf16 = x_type == MX_BF16;
@@ -77,7 +89,16 @@ mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, i
     a.codes = codes;
     a.scales = scales;
     a.fast = (k % 32 == 0) && ((ld_x * esize) % 16 == 0);
-    return from_hip(mxk::launch_quantize(a, static_cast<hipStream_t>(stream)));
+    const int64_t step = chunk_rows(k);
+    for (int64_t r0 = 0; r0 < rows; r0 += step) {
+        mxk::QuantArgs c = a;
+        c.x = static_cast<const uint8_t*>(x) + r0 * ld_x * esize;
+        c.codes = codes + r0 * (k / 2);
+        c.scales = scales + r0 * (k / block);
+        c.rows = rows - r0 < step ? rows - r0 : step;
+        if (mxk::launch_quantize(c, static_cast<hipStream_t>(stream)) != hipSuccess) return MX_ERR_HIP;
+    }
+    return MX_OK;
 }
 
 mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
@@ -92,7 +113,7 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
     if (!y || !codes || !scales) return MX_ERR_INVALID_ARG;
     if (!aligned16(y) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
     const int esize = y_type == MX_BF16 ? 2 : 4;
-    if (rows * (k / 32) > INT32_MAX - 1024) return MX_ERR_UNSUPPORTED;
+    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
     mxk::DequantArgs a;
     a.codes = codes;
     a.scales = scales;
@@ -105,7 +126,16 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
     a.bf16 = y_type == MX_BF16;
     a.ldy = ld_y;
     a.fast = (k % 32 == 0) && ((ld_y * esize) % 16 == 0);
-    return from_hip(mxk::launch_dequantize(a, static_cast<hipStream_t>(stream)));
+    const int64_t step = chunk_rows(k);
+    for (int64_t r0 = 0; r0 < rows; r0 += step) {
+        mxk::DequantArgs c = a;
+        c.codes = codes + r0 * (k / 2);
+        c.scales = scales + r0 * (k / block);
+        c.y = static_cast<uint8_t*>(y) + r0 * ld_y * esize;
+        c.rows = rows - r0 < step ? rows - r0 : step;
+        if (mxk::launch_dequantize(c, static_cast<hipStream_t>(stream)) != hipSuccess) return MX_ERR_HIP;
+    }
+    return MX_OK;
 }
 
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode)
@@ -140,7 +170,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     const size_t need = mx_gemm_workspace_size(m, n, k, block, mode);
     if (workspace_bytes < need || (need && !workspace)) return MX_ERR_INVALID_ARG;
     if (need && !aligned16(workspace)) return MX_ERR_ALIGNMENT;
-    if (m * (k / 32) > INT32_MAX - 1024) return MX_ERR_UNSUPPORTED;
+    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
 
     mxk::GemmArgs a;
     a.x = static_cast<const uint16_t*>(x);
@@ -159,28 +189,40 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     a.xq_codes = nullptr;
     a.xq_scales = nullptr;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (mode == MX_A16) return from_hip(mxk::launch_gemm_a16(a, s));
-
-    // W4A4: MX-quantize the activations (block 32, E8M0, g = 1) into the workspace with the
-    // quantize kernel itself, then run the FP4 matrix-core product.
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    a.xq_codes = ws;
-    a.xq_scales = ws + round256((size_t)m * (size_t)(k / 2));
-    mxk::QuantArgs q;
-    q.x = x;
-    q.bf16 = true;
-    q.rows = m;
-    q.k = k;
-    q.ldx = ld_x;
-    q.block = 32;
-    q.fmt = mxk::FMT_E8M0;
-    q.g = 1.0;
-    q.codes = a.xq_codes;
-    q.scales = a.xq_scales;
-    q.fast = (ld_x * 2) % 16 == 0;  // k % 32 == 0 holds (block 32)
-    hipError_t e = mxk::launch_quantize(q, s);
-    if (e != hipSuccess) return MX_ERR_HIP;
-    return from_hip(mxk::launch_gemm_a4(a, s));
+    // rows of Y per launch: keeps per-launch unit counts (outputs, pre-pass pairs) < 2^29
+    const int64_t per_row = n > k / 2 ? n : k / 2;
+    int64_t step = kMaxUnitsPerLaunch / (per_row > 0 ? per_row : 1);
+    step = step < 1 ? 1 : (step > 256 ? step & ~int64_t(255) : step);
+    for (int64_t r0 = 0; r0 < m; r0 += step) {
+        mxk::GemmArgs c = a;
+        c.m = m - r0 < step ? m - r0 : step;
+        c.x = a.x + r0 * ld_x;
+        c.y = static_cast<uint8_t*>(y) + r0 * ld_y * (y_type == MX_BF16 ? 2 : 4);
+        if (mode == MX_A16) {
+            if (mxk::launch_gemm_a16(c, s) != hipSuccess) return MX_ERR_HIP;
+            continue;
+        }
+        // W4A4: MX-quantize the activations (block 32, E8M0, g = 1) into the workspace with
+        // the quantize kernel itself, then run the FP4 matrix-core product.
+        c.xq_codes = ws + r0 * (k / 2);
+        c.xq_scales = ws + round256((size_t)m * (size_t)(k / 2)) + r0 * (k / 32);
+        mxk::QuantArgs q;
+        q.x = c.x;
+        q.bf16 = true;
+        q.rows = c.m;
+        q.k = k;
+        q.ldx = ld_x;
+        q.block = 32;
+        q.fmt = mxk::FMT_E8M0;
+        q.g = 1.0;
+        q.codes = c.xq_codes;
+        q.scales = c.xq_scales;
+        q.fast = (ld_x * 2) % 16 == 0;  // k % 32 == 0 holds (block 32)
+        if (mxk::launch_quantize(q, s) != hipSuccess) return MX_ERR_HIP;
+        if (mxk::launch_gemm_a4(c, s) != hipSuccess) return MX_ERR_HIP;
+    }
+    return MX_OK;
 }
 
 }  // extern "C"

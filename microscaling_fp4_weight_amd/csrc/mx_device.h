@@ -63,23 +63,21 @@ __device__ __forceinline__ uint64_t rne_shr64(uint64_t x, uint32_t s)
 // ---------------------------------------------------------------------------------------
 
 // E4M3 / UE5M3 code nearest to v >= 0 given in fp32 (3 mantissa bits, subnormals,
-// saturation at the largest finite code).
+// saturation at the largest finite code).  Branch-free: the significand is shifted right by
+// 20 (normal target) or more (subnormal target; the shift saturates at 31, which yields 0
+// for any 24-bit significand), rounded to nearest even, and added to the exponent field.
 template <int FMT>
 __device__ __forceinline__ uint32_t fp8_code_f32(float v)
 {
     constexpr int bias = ScaleFmt<FMT>::bias;
     const uint32_t b = f2u(v);
-    const int e = (int)(b >> 23);
-    if (e == 0) return 0;  // zero or fp32-subnormal: below half the smallest scale
+    const int e = (int)(b >> 23);                      // 0 for zero / fp32 subnormal
     const uint32_t sig = (b & 0x7FFFFFu) | 0x800000u;  // value = sig * 2^(e - 150)
     const int et = e - 127 + bias;                     // target exponent field if normal
-    uint32_t code;
-    if (et >= 1) {
-        code = ((uint32_t)(et - 1) << 3) + rne_shr32(sig, 20);  // a carry moves to et + 1
-    } else {
-        const int sh = 148 - bias - e;  // subnormal step 2^(-2-bias)
-        code = sh > 31 ? 0u : rne_shr32(sig, (uint32_t)sh);
-    }
+    int sh = 148 - bias - e;                           // subnormal step is 2^(-2-bias)
+    sh = sh < 20 ? 20 : (sh > 31 ? 31 : sh);
+    const uint32_t base = et > 1 ? (uint32_t)(et - 1) << 3 : 0u;
+    const uint32_t code = base + rne_shr32(sig, (uint32_t)sh);  // a carry moves to et + 1
     return code < ScaleFmt<FMT>::maxcode ? code : ScaleFmt<FMT>::maxcode;
 }
 
@@ -113,8 +111,9 @@ __device__ __forceinline__ float fp8_value(uint32_t code)
     constexpr int bias = ScaleFmt<FMT>::bias;
     const uint32_t sign = FMT == FMT_E4M3 ? (code & 0x80u) << 24 : 0u;
     const uint32_t E = FMT == FMT_E4M3 ? (code >> 3) & 15u : code >> 3, M = code & 7u;
-    if (E) return u2f(sign | ((E - bias + 127) << 23) | (M << 20));
-    return u2f(sign | f2u((float)M * u2f((uint32_t)(127 - 2 - bias) << 23)));  // M * 2^(-2-bias)
+    const uint32_t normal = ((E - bias + 127) << 23) | (M << 20);
+    const uint32_t sub = f2u((float)M * u2f((uint32_t)(127 - 2 - bias) << 23));  // M * 2^(-2-bias)
+    return u2f(sign | (E ? normal : sub));
 }
 
 // E8M0 byte of the power of two nearest to a / 6 (ties up), from the fp32 bits of
@@ -154,9 +153,10 @@ __device__ __forceinline__ uint32_t scale_code_g1(uint32_t abits)
     if constexpr (FMT == FMT_E8M0) {
         return e8m0_code_absmax(abits);
     } else {
-        // fl32(a / 6) decides every FP8 midpoint exactly (a correctly rounded quotient of an
-        // fp32 value by 6 never lands on, or crosses, a value with 5 significant bits).
-        return fp8_code_f32<FMT>(u2f(abits) / 6.0f);
+        // fl32(fl64(a) * fl64(1/6)) decides every FP8 midpoint exactly: it equals a midpoint
+        // m (5 significant bits) only when a = 6 m, and otherwise stays on a's side of it
+        // (|a/6 - m| >= ulp(a)/6 while both roundings move it by less than ulp(a)/8).
+        return fp8_code_f32<FMT>((float)((double)u2f(abits) * (1.0 / 6.0)));
     }
 }
 
@@ -193,20 +193,17 @@ struct EncG1 {
     float clo;   // 1/m, low part
 };
 
+// chi = 1/m rounded down to fp32 and clo = fl32(1/m - chi) >= 0, for m = 1 + mi/8.  Both
+// parts are non-negative so that x' keeps the sign of x, also for x = -0.
+static __constant__ uint32_t kRecipParts[8][2] = {
+    {0x3f800000u, 0x00000000u}, {0x3f638e38u, 0x33638e39u}, {0x3f4cccccu, 0x334ccccdu},
+    {0x3f3a2e8bu, 0x3322e8bau}, {0x3f2aaaaau, 0x332aaaabu}, {0x3f1d89d8u, 0x331d89d9u},
+    {0x3f124924u, 0x33124925u}, {0x3f088888u, 0x33088889u}};
+
 __device__ __forceinline__ void recip_parts(uint32_t mi, float& chi, float& clo)
 {
-    // chi = 1/m rounded down to fp32, clo = fl32(1/m - chi) >= 0 for m = 1 + mi/8.  Both
-    // parts are non-negative so that x' keeps the sign of x, also for x = -0.
-    switch (mi) {
-        case 0: chi = u2f(0x3f800000u); clo = 0.0f; break;
-        case 1: chi = u2f(0x3f638e38u); clo = u2f(0x33638e39u); break;
-        case 2: chi = u2f(0x3f4cccccu); clo = u2f(0x334ccccdu); break;
-        case 3: chi = u2f(0x3f3a2e8bu); clo = u2f(0x3322e8bau); break;
-        case 4: chi = u2f(0x3f2aaaaau); clo = u2f(0x332aaaabu); break;
-        case 5: chi = u2f(0x3f1d89d8u); clo = u2f(0x331d89d9u); break;
-        case 6: chi = u2f(0x3f124924u); clo = u2f(0x33124925u); break;
-        default: chi = u2f(0x3f088888u); clo = u2f(0x33088889u); break;
-    }
+    chi = u2f(kRecipParts[mi][0]);
+    clo = u2f(kRecipParts[mi][1]);
 }
 
 template <int FMT>
@@ -218,16 +215,13 @@ __device__ __forceinline__ EncG1 enc_params_g1(uint32_t byte)
         p.chi = 1.0f;
         p.clo = 0.0f;
     } else {
-        const float s = fp8_value<FMT>(byte);
-        const uint32_t sb = f2u(s);
-        if (sb == 0) {  // flushed block: x' = +-0 -> codes 0 / 8
-            p.pow2 = 1.0f;
-            p.chi = 0.0f;
-            p.clo = 0.0f;
-        } else {
-            p.pow2 = u2f(sb & 0x7F800000u);
-            recip_parts((sb >> 20) & 7u, p.chi, p.clo);
-        }
+        const uint32_t sb = f2u(fp8_value<FMT>(byte));
+        float chi, clo;
+        recip_parts((sb >> 20) & 7u, chi, clo);
+        const bool zero = sb == 0;  // flushed block: x' = +-0 -> codes 0 / 8
+        p.pow2 = zero ? 1.0f : u2f(sb & 0x7F800000u);
+        p.chi = zero ? 0.0f : chi;
+        p.clo = zero ? 0.0f : clo;
     }
     return p;
 }
@@ -295,6 +289,39 @@ __device__ __forceinline__ uint32_t enc_elem_g(uint32_t xbits32, const EncG& p)
 #pragma unroll
     for (int i = 0; i < 7; ++i) c += (a > p.u[i]) ? 1u : 0u;
     return c | ((xbits32 >> 28) & 8u);
+}
+
+// ---------------------------------------------------------------------------------------
+// Buffer loads: a resource descriptor carries a byte range, and lanes whose offset is out of
+// range read zero without a branch (used for masked rows and k-tails).
+// ---------------------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // an offset beyond every range this library builds
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload128(rsrc_t r, uint32_t off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload32(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload16(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint64_t bload64(rsrc_t r, uint32_t off)
+{
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    return (uint64_t)v.x | ((uint64_t)v.y << 32);
 }
 
 // ---------------------------------------------------------------------------------------

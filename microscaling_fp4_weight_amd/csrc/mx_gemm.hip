@@ -186,74 +186,193 @@ __global__ __launch_bounds__(256) void gemm_a16_kernel(const GemmArgs a)
 }
 
 // ---------------------------------------------------------------------------------------
-// W4A16 GEMV (m <= 16): one MFMA row-tile; a workgroup of 4 waves owns 16 * NS columns,
-// the waves take interleaved k-tiles and their partial sums are added through LDS.
+// W4A16 GEMV (m <= 16): one MFMA row-tile.  A workgroup owns 16 output columns; its
+// GEMV_WAVES waves take contiguous k ranges.  Each wave keeps GEMV_DEPTH k-tiles of weight
+// and activation loads in flight (a rolling prefetch: tile t + GEMV_DEPTH is requested as
+// soon as tile t has been consumed); the waves' partial sums are added through LDS.
 // ---------------------------------------------------------------------------------------
-constexpr int GEMV_NS = 2;
+constexpr int GEMV_WAVES = 4;
+constexpr int GEMV_DEPTH = 4;
+
+template <int BLOCK>
+struct GemvTile {
+    u32x4 cw;         // 32 weight codes of row n
+    uint64_t sb;      // their scale byte(s)
+    u32x4 xv[4];      // 32 activations of row lr (zero for rows >= m)
+};
+
+// Scales covering one lane's 32 k through a buffer resource (zero when out of range).
+template <int BLOCK>
+__device__ __forceinline__ uint64_t bload_lane_scales(rsrc_t r, uint32_t off)
+{
+    if constexpr (BLOCK >= 32) return bload8(r, off);
+    else if constexpr (BLOCK == 16) return bload16(r, off);
+    else if constexpr (BLOCK == 8) return bload32(r, off);
+    else return bload64(r, off);
+}
+
+struct GemvRows {
+    rsrc_t w, s, x;          // this workgroup's 16 weight rows, their scales, the activations
+    uint32_t woff, soff, xoff;  // this lane's row offsets (bytes)
+    uint32_t K;
+};
+
+template <int BLOCK>
+__device__ __forceinline__ void gemv_load(GemvTile<BLOCK>& t, int64_t tile, int64_t t1, int kq,
+                                          const GemvRows& r)
+{
+    const uint32_t kk = (uint32_t)tile * TK + 32 * kq;
+    const bool ok = tile < t1 && kk < r.K;
+    t.cw = bload128(r.w, ok ? r.woff + kk / 2 : kOOB);
+    t.sb = bload_lane_scales<BLOCK>(r.s, ok ? r.soff + kk / BLOCK : kOOB);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.xv[j] = bload128(r.x, ok ? r.xoff + (kk + 8 * j) * 2 : kOOB);
+}
 
 template <int BLOCK, int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(256) void gemv_a16_kernel(const GemmArgs a)
+__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_a16_kernel(const GemmArgs a)
 {
-    __shared__ f32x4 red[3][GEMV_NS][64];
+    __shared__ f32x4 red[GEMV_WAVES - 1][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, kq = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * (16 * GEMV_NS);
-    const int64_t K = a.k;
-    const bool mrow = lr < a.m;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n = n0 + lr;
+    const uint32_t K = (uint32_t)a.k;
+    const int64_t KT = (a.k + TK - 1) / TK;
+    const int64_t per = (KT + GEMV_WAVES - 1) / GEMV_WAVES;
+    const int64_t t0 = wave * per;
+    const int64_t t1 = t0 + per < KT ? t0 + per : KT;
+    const uint32_t rows = (uint32_t)(a.n - n0 < 16 ? a.n - n0 : 16);
 
-    f32x4 acc[GEMV_NS];
-#pragma unroll
-    for (int ns = 0; ns < GEMV_NS; ++ns) acc[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+    GemvRows r;
+    r.w = make_rsrc(a.wc + n0 * (a.k / 2), rows * (K / 2));
+    r.s = make_rsrc(a.ws + n0 * (a.k / BLOCK), rows * (K / BLOCK));
+    r.x = make_rsrc(a.x, (uint32_t)(a.m * a.ldx * 2));
+    r.woff = lr * (K / 2);
+    r.soff = lr * (K / BLOCK);
+    r.xoff = (uint32_t)(lr * a.ldx * 2);
+    r.K = K;
 
-    for (int64_t k0 = (int64_t)wave * TK; k0 < K; k0 += 4 * TK) {
-        const int64_t kk = k0 + 32 * kq;
-        const bool kin = kk < K;
-        u32x4 cw[GEMV_NS];
-        uint64_t sb[GEMV_NS];
+    GemvTile<BLOCK> buf[GEMV_DEPTH];
 #pragma unroll
-        for (int ns = 0; ns < GEMV_NS; ++ns) {
-            const int64_t n = n0 + ns * 16 + lr;
-            cw[ns] = u32x4{0u, 0u, 0u, 0u};
-            sb[ns] = 0;
-            if (n < a.n && kin) {
-                cw[ns] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.wc + n * (K / 2) + kk / 2));
-                sb[ns] = load_lane_scales<BLOCK>(a.ws + n * (K / BLOCK) + kk / BLOCK);
-            }
-        }
-        uint32_t xf[16];
-        {
-            const u32x4* xp = reinterpret_cast<const u32x4*>(a.x + (int64_t)lr * a.ldx + kk);
+    for (int p = 0; p < GEMV_DEPTH; ++p) gemv_load<BLOCK>(buf[p], t0 + p, t1, kq, r);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t tb = t0; tb < t1; tb += GEMV_DEPTH) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (mrow && kin) v = xp[j];
-                xf[4 * j] = v.x; xf[4 * j + 1] = v.y; xf[4 * j + 2] = v.z; xf[4 * j + 3] = v.w;
-            }
-        }
-#pragma unroll
-        for (int ns = 0; ns < GEMV_NS; ++ns) {
+        for (int p = 0; p < GEMV_DEPTH; ++p) {
             uint32_t bw[16];
-            dequant32<BLOCK, FMT>(cw[ns], sb[ns], bw);
+            dequant32<BLOCK, FMT>(buf[p].cw, buf[p].sb, bw);
+            const u32x4 x0 = buf[p].xv[0], x1 = buf[p].xv[1], x2 = buf[p].xv[2], x3 = buf[p].xv[3];
+            gemv_load<BLOCK>(buf[p], tb + p + GEMV_DEPTH, t1, kq, r);
+            const uint32_t xf[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                                     x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[ns] = mfma_bf16(&xf[4 * j], &bw[4 * j], acc[ns]);
+            for (int j = 0; j < 4; ++j) acc = mfma_bf16(&xf[4 * j], &bw[4 * j], acc);
         }
     }
-    if (wave > 0) {
-#pragma unroll
-        for (int ns = 0; ns < GEMV_NS; ++ns) red[wave - 1][ns][lane] = acc[ns];
-    }
+    if (wave > 0) red[wave - 1][lane] = acc;
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-        for (int ns = 0; ns < GEMV_NS; ++ns) {
-            f32x4 s = acc[ns] + red[0][ns][lane] + red[1][ns][lane] + red[2][ns][lane];
-            const int64_t n = n0 + ns * 16 + lr;
+        for (int w = 0; w < GEMV_WAVES - 1; ++w) acc += red[w][lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t m = 4 * kq + i;
-                if (m < a.m && n < a.n) store_y<OUT_BF16>(a.y, a.ldy, m, n, s[i] * a.g);
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int64_t m = 4 * kq + i;
+            if (m < a.m && n < a.n) store_y<OUT_BF16>(a.y, a.ldy, m, n, acc[i] * a.g);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// W4A16 GEMV for m <= 4 on the vector ALUs.  A workgroup owns DOT_ROWS weight rows; its 4
+// waves split k into contiguous ranges of 2048-element chunks.  In a chunk, lane l holds the
+// 32 activations k = c*2048 + 32 l .. +31 of every row of X in registers (reused for all
+// DOT_ROWS weight rows) and, per weight row, loads that row's 16 code bytes for the same k
+// -- one load instruction reads 1 KB of contiguous codes.  Products are accumulated with
+// v_dot2_f32_bf16 into per-lane partial sums, which are reduced across the wave and then
+// across the 4 waves at the end.
+// ---------------------------------------------------------------------------------------
+constexpr int DOT_ROWS = 8;
+constexpr int DOT_WAVES = 4;
+constexpr int DOT_CHUNK = 2048;
+
+template <int BLOCK, int FMT, int MM, bool OUT_BF16>
+__global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs a)
+{
+    __shared__ float red[DOT_WAVES][DOT_ROWS * MM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t n0 = (int64_t)blockIdx.x * DOT_ROWS;
+    const uint32_t K = (uint32_t)a.k;
+    const uint32_t nrows = (uint32_t)(a.n - n0 < DOT_ROWS ? a.n - n0 : DOT_ROWS);
+    const int64_t KC = (a.k + DOT_CHUNK - 1) / DOT_CHUNK;
+    const int64_t per = (KC + DOT_WAVES - 1) / DOT_WAVES;
+    const int64_t c0 = wave * per;
+    const int64_t c1 = c0 + per < KC ? c0 + per : KC;
+
+    const rsrc_t wr = make_rsrc(a.wc + n0 * (a.k / 2), nrows * (K / 2));
+    const rsrc_t sr = make_rsrc(a.ws + n0 * (a.k / BLOCK), nrows * (K / BLOCK));
+    const rsrc_t xr = make_rsrc(a.x, (uint32_t)(a.m * a.ldx * 2));
+
+    float acc[DOT_ROWS][MM];
+#pragma unroll
+    for (int r = 0; r < DOT_ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[r][m] = 0.0f;
+
+    for (int64_t c = c0; c < c1; ++c) {
+        const uint32_t kk = (uint32_t)c * DOT_CHUNK + 32 * lane;
+        const bool ok = kk < K;
+        u32x4 cw[DOT_ROWS];
+        uint64_t sb[DOT_ROWS];
+#pragma unroll
+        for (int r = 0; r < DOT_ROWS; ++r) {
+            cw[r] = bload128(wr, ok ? r * (K / 2) + kk / 2 : kOOB);
+            sb[r] = bload_lane_scales<BLOCK>(sr, ok ? r * (K / BLOCK) + kk / BLOCK : kOOB);
+        }
+        uint32_t xf[MM][16];
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 v = bload128(xr, ok && m < a.m ? (uint32_t)(m * a.ldx * 2) + (kk + 8 * j) * 2 : kOOB);
+                xf[m][4 * j] = v.x; xf[m][4 * j + 1] = v.y; xf[m][4 * j + 2] = v.z; xf[m][4 * j + 3] = v.w;
+            }
+#pragma unroll
+        for (int r = 0; r < DOT_ROWS; ++r) {
+            uint32_t bw[16];
+            dequant32<BLOCK, FMT>(cw[r], sb[r], bw);
+#pragma unroll
+            for (int m = 0; m < MM; ++m)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[r][m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xf[m][i]),
+                                                                __builtin_bit_cast(bf16x2, bw[i]),
+                                                                acc[r][m], false);
+        }
+    }
+    // reduce over the 64 lanes, then over the waves
+#pragma unroll
+    for (int r = 0; r < DOT_ROWS; ++r)
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+            float v = acc[r][m];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            acc[r][m] = v;
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < DOT_ROWS; ++r)
+#pragma unroll
+            for (int m = 0; m < MM; ++m) red[wave][r * MM + m] = acc[r][m];
+    }
+    __syncthreads();
+    if (tid < DOT_ROWS * MM) {
+        const int r = tid / MM, m = tid % MM;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < DOT_WAVES; ++w) v += red[w][tid];
+        if (m < a.m && (uint32_t)r < nrows) store_y<OUT_BF16>(a.y, a.ldy, m, n0 + r, v * a.g);
     }
 }
 
@@ -394,10 +513,23 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
                            dim3(256), 0, st, a);
         return hipGetLastError();
     }
-    if (a.m <= 16) {
-        const dim3 grid((unsigned)((a.n + 16 * GEMV_NS - 1) / (16 * GEMV_NS)));
+    if (a.m <= 4) {
+        const dim3 grid((unsigned)((a.n + DOT_ROWS - 1) / DOT_ROWS));
         switch (a.block) {
-#define MXV(B) case B: hipLaunchKernelGGL((gemv_a16_kernel<B, FMT, OUT_BF16>), grid, dim3(256), 0, st, a); break;
+#define MXD1(B) case B: \
+    if (a.m == 1) hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
+    else hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 4, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
+    break;
+            MXD1(4) MXD1(8) MXD1(16) MXD1(32) MXD1(64) MXD1(128) MXD1(256)
+#undef MXD1
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    if (a.m <= 16) {
+        const dim3 grid((unsigned)((a.n + 15) / 16));
+        switch (a.block) {
+#define MXV(B) case B: hipLaunchKernelGGL((gemv_a16_kernel<B, FMT, OUT_BF16>), grid, dim3(64 * GEMV_WAVES), 0, st, a); break;
             MXV(4) MXV(8) MXV(16) MXV(32) MXV(64) MXV(128) MXV(256)
 #undef MXV
             default: return hipErrorInvalidValue;

@@ -11,6 +11,25 @@ namespace mxk {
 
 enum { FMT_E4M3 = 0, FMT_UE5M3 = 1, FMT_E8M0 = 2 };  // same values as mx_scale_fmt
 
+// Unsigned division by a launch-constant d as a multiply and shift (Granlund & Montgomery's
+// round-up method): q = (mulhi(u, mul) + u) >> shift, exact for every u < 2^31.
+struct FastDiv {
+    uint32_t mul, shift;
+    static FastDiv make(uint32_t d)
+    {
+        uint32_t s = 0;
+        while ((uint64_t(1) << s) < d) ++s;
+        FastDiv f;
+        f.mul = (uint32_t)(((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1);
+        f.shift = s;
+        return f;
+    }
+    __host__ __device__ __forceinline__ uint32_t div(uint32_t u) const
+    {
+        return ((uint32_t)(((uint64_t)u * mul) >> 32) + u) >> shift;
+    }
+};
+
 struct QuantArgs {
     const void* x;
     bool bf16;        // input element type

@@ -5,11 +5,15 @@
 // gtnt.cn/news/16247 "为什么我们需要4-bit浮点量化", sections 2.1 (clip then round) and 4.3
 // (two FP4 codes per byte).
 //
-// Fast path: one lane owns 32 consecutive elements of a row (64 B of bf16 / 128 B of fp32,
-// loaded with 128-bit loads) and writes their 16 code bytes with one 128-bit store.  Blocks
-// of up to 32 elements are lane-local; larger blocks (64..256) span 2..8 neighbouring lanes
-// and reduce their absmax with cross-lane shuffles.  Requires k % 32 == 0 and 16-byte
-// aligned rows.  The generic path (one thread per block, scalar accesses) covers every
+// Quantize fast path: one lane owns 32 consecutive elements of a row (64 B of bf16 / 128 B
+// of fp32, loaded with 128-bit loads) and writes their 16 code bytes with one 128-bit
+// non-temporal store.  Blocks of up to 32 elements are lane-local; larger blocks (64..256)
+// span 2..8 neighbouring lanes and reduce their absmax with cross-lane shuffles.
+// Dequantize fast path: a lane converts 8 consecutive elements (one code dword) per step and
+// writes them with one 128-bit (bf16) or two (fp32) non-temporal stores; consecutive lanes
+// cover consecutive memory.  (On MI355X, measured: plain loads beat non-temporal loads for
+// these streams, non-temporal stores beat plain stores.)  Both require k % 32 == 0 and
+// 16-byte aligned rows; the generic path (one thread per block / element pair) covers every
 // other valid shape with the same arithmetic.
 #include "mx_device.h"
 #include "mx_internal.h"
@@ -23,7 +27,7 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------------------
 template <int BLOCK, int FMT, bool BF16, bool G1>
 __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
-    const uint8_t* __restrict__ x, int64_t ldx_bytes, uint32_t groups_per_row,
+    const uint8_t* __restrict__ x, int64_t ldx_bytes, FastDiv groups_per_row, uint32_t gpr,
     uint32_t total_groups, double g, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, int64_t k)
 {
@@ -34,8 +38,8 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
 
     const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
     const bool active = gid < total_groups;
-    const uint32_t row = active ? gid / groups_per_row : 0u;
-    const uint32_t gc = active ? gid - row * groups_per_row : 0u;
+    const uint32_t row = active ? groups_per_row.div(gid) : 0u;
+    const uint32_t gc = active ? gid - row * gpr : 0u;
 
     uint32_t w[NW];
     if (active) {
@@ -43,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
                                                         (int64_t)gc * (BF16 ? 64 : 128));
 #pragma unroll
         for (int j = 0; j < NW / 4; ++j) {
-            const u32x4 v = __builtin_nontemporal_load(p + j);
+            const u32x4 v = p[j];
             w[4 * j + 0] = v.x;
             w[4 * j + 1] = v.y;
             w[4 * j + 2] = v.z;
@@ -112,9 +116,12 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
     for (int q = 0; q < 4; ++q) out[q] = 0u;
 
     if constexpr (G1) {
+        EncG1 par[NB];  // all blocks' parameters first: their table loads issue together
+#pragma unroll
+        for (int b = 0; b < NB; ++b) par[b] = enc_params_g1<FMT>(sbyte[b]);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const EncG1 p = enc_params_g1<FMT>(sbyte[b]);
+            const EncG1& p = par[b];
             if constexpr (BF16) {
                 // pair j = elements (2j, 2j+1) = word j
 #pragma unroll
@@ -243,84 +250,86 @@ __device__ __forceinline__ void dec_byte_pair(uint32_t cw, int sel, float pow2, 
     }
 }
 
+constexpr int kDeqUnits = 2;  // 8-element units per lane
+
 template <int BLOCK, int FMT, bool G1, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    uint32_t groups_per_row, uint32_t total_groups, int64_t k, double g,
+    FastDiv units_per_row, uint32_t upr, uint32_t total_units, int64_t k, double g,
     uint8_t* __restrict__ y, int64_t ldy_bytes)
 {
-    constexpr int NB = BLOCK <= 32 ? 32 / BLOCK : 1;
-    constexpr int LANES = BLOCK > 32 ? BLOCK / 32 : 1;
-    const uint32_t gid = blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= total_groups) return;
-    const uint32_t row = gid / groups_per_row;
-    const uint32_t gc = gid - row * groups_per_row;
-
-    const u32x4 cv = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(codes + (int64_t)row * (k / 2) + (int64_t)gc * 16));
-    const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
-    const uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
-    uint32_t sbyte[NB];
-    if constexpr (NB == 1) {
-        sbyte[0] = sp[gc / LANES];
-    } else if constexpr (NB == 2) {
-        const uint32_t v = *reinterpret_cast<const uint16_t*>(sp + gc * 2);
-        sbyte[0] = v & 0xFF; sbyte[1] = v >> 8;
-    } else if constexpr (NB == 4) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(sp + gc * 4);
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t wbase = (blockIdx.x * kThreads + (threadIdx.x & ~63u)) * kDeqUnits;
+    // issue every unit's loads first, then convert and store
+    uint32_t cw[kDeqUnits], sb[kDeqUnits][2], row[kDeqUnits], c8[kDeqUnits];
+    bool act[kDeqUnits];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) sbyte[b] = (v >> (8 * b)) & 0xFF;
-    } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(sp + gc * 8);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) { sbyte[b] = (v.x >> (8 * b)) & 0xFF; sbyte[4 + b] = (v.y >> (8 * b)) & 0xFF; }
-    }
-
-    uint32_t o[OUT_BF16 ? 16 : 32];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        float pow2 = 1.0f, mant = 1.0f;
-        double sg = 0.0;
-        if constexpr (G1) {
-            const DecG1 p = dec_params_g1<FMT>(sbyte[b]);
-            pow2 = p.pow2;
-            mant = p.mant;
-        } else {
-            sg = scale_value_f64<FMT>(sbyte[b]) * g;
-        }
-        constexpr int PPB = 16 / NB;  // code bytes (element pairs) per block part
-#pragma unroll
-        for (int jj = 0; jj < PPB; ++jj) {
-            const int j = b * PPB + jj;  // pair index 0..15
-            if constexpr (OUT_BF16 && G1 && FMT == FMT_E8M0) {
-                bf16x2 h;
-                switch (j & 3) {
-                    case 0: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 0); break;
-                    case 1: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 1); break;
-                    case 2: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 2); break;
-                    default: h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j >> 2], pow2, 3); break;
-                }
-                o[j] = __builtin_bit_cast(uint32_t, h);
+    for (int h = 0; h < kDeqUnits; ++h) {
+        const uint32_t u = wbase + h * 64 + lane;  // unit of 8 elements
+        act[h] = u < total_units;
+        row[h] = act[h] ? units_per_row.div(u) : 0u;
+        c8[h] = act[h] ? u - row[h] * upr : 0u;  // the unit holds elements 8*c8 .. 8*c8+7
+        cw[h] = 0u;
+        sb[h][0] = sb[h][1] = 0u;
+        if (act[h]) {
+            cw[h] = *reinterpret_cast<const uint32_t*>(codes + (int64_t)row[h] * (k / 2) + (int64_t)c8[h] * 4);
+            const uint8_t* sp = scales + (int64_t)row[h] * (k / BLOCK);
+            if constexpr (BLOCK == 4) {
+                const uint32_t v = *reinterpret_cast<const uint16_t*>(sp + c8[h] * 2);
+                sb[h][0] = v & 0xFF;
+                sb[h][1] = v >> 8;
             } else {
+                sb[h][0] = sb[h][1] = sp[(c8[h] * 8) / BLOCK];
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < kDeqUnits; ++h) {
+        if (!act[h]) continue;
+        uint32_t o[OUT_BF16 ? 4 : 8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // pair j = elements 2j, 2j+1 of the unit
+            const uint32_t byte = sb[h][BLOCK == 4 ? (j >> 1) : 0];
+            if constexpr (OUT_BF16 && G1 && FMT == FMT_E8M0) {
+                const float pow2 = e8m0_value(byte);
+                bf16x2 hv;
+                switch (j) {
+                    case 0: hv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[h], pow2, 0); break;
+                    case 1: hv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[h], pow2, 1); break;
+                    case 2: hv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[h], pow2, 2); break;
+                    default: hv = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[h], pow2, 3); break;
+                }
+                o[j] = __builtin_bit_cast(uint32_t, hv);
+            } else {
+                float pow2 = 1.0f, mant = 1.0f;
+                double sg = 0.0;
+                if constexpr (G1) {
+                    const DecG1 p = dec_params_g1<FMT>(byte);
+                    pow2 = p.pow2;
+                    mant = p.mant;
+                } else {
+                    sg = scale_value_f64<FMT>(byte) * g;
+                }
                 float lo, hi;
-                dec_byte_pair<FMT, G1, OUT_BF16>(cw[j >> 2], j & 3, pow2, mant, sg, lo, hi);
+                dec_byte_pair<FMT, G1, OUT_BF16>(cw[h], j, pow2, mant, sg, lo, hi);
                 if constexpr (OUT_BF16) {
-                    bf16x2 h;
-                    h.x = (__bf16)lo;
-                    h.y = (__bf16)hi;
-                    o[j] = __builtin_bit_cast(uint32_t, h);
+                    bf16x2 hv;
+                    hv.x = (__bf16)lo;
+                    hv.y = (__bf16)hi;
+                    o[j] = __builtin_bit_cast(uint32_t, hv);
                 } else {
                     o[2 * j] = f2u(lo);
                     o[2 * j + 1] = f2u(hi);
                 }
             }
         }
-    }
-    u32x4* yp = reinterpret_cast<u32x4*>(y + (int64_t)row * ldy_bytes + (int64_t)gc * (OUT_BF16 ? 64 : 128));
-#pragma unroll
-    for (int q = 0; q < (OUT_BF16 ? 4 : 8); ++q) {
-        const u32x4 ov = {o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-        __builtin_nontemporal_store(ov, yp + q);
+        u32x4* yp = reinterpret_cast<u32x4*>(y + (int64_t)row[h] * ldy_bytes + (int64_t)c8[h] * (OUT_BF16 ? 16 : 32));
+        const u32x4 v0 = {o[0], o[1], o[2], o[3]};
+        __builtin_nontemporal_store(v0, yp);
+        if constexpr (!OUT_BF16) {
+            const u32x4 v1 = {o[4], o[5], o[6], o[7]};
+            __builtin_nontemporal_store(v1, yp + 1);
+        }
     }
 }
 
@@ -373,7 +382,7 @@ static hipError_t launch_quantize_fmt(const QuantArgs& a, hipStream_t st)
         const int64_t ldb = a.ldx * (BF16 ? 2 : 4);
         switch (a.block) {
 #define MXQ(B) case B: hipLaunchKernelGGL((quantize_fast_kernel<B, FMT, BF16, G1>), grid, dim3(kThreads), 0, st, \
-                   (const uint8_t*)a.x, ldb, gpr, total, a.g, a.codes, a.scales, a.k); break;
+                   (const uint8_t*)a.x, ldb, FastDiv::make(gpr), gpr, total, a.g, a.codes, a.scales, a.k); break;
             MXQ(4) MXQ(8) MXQ(16) MXQ(32) MXQ(64) MXQ(128) MXQ(256)
 #undef MXQ
             default: return hipErrorInvalidValue;
@@ -404,13 +413,14 @@ template <int FMT, bool G1, bool OUT_BF16>
 static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
 {
     if (a.fast) {
-        const uint32_t gpr = (uint32_t)(a.k / 32);
-        const uint32_t total = (uint32_t)(a.rows * gpr);
-        const dim3 grid((total + kThreads - 1) / kThreads);
+        const uint32_t upr = (uint32_t)(a.k / 8);
+        const uint32_t total = (uint32_t)(a.rows * upr);
+        const uint32_t per_wg = kThreads * kDeqUnits;
+        const dim3 grid((total + per_wg - 1) / per_wg);
         const int64_t ldb = a.ldy * (OUT_BF16 ? 2 : 4);
         switch (a.block) {
 #define MXD(B) case B: hipLaunchKernelGGL((dequantize_fast_kernel<B, FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st, \
-                   a.codes, a.scales, gpr, total, a.k, a.g, (uint8_t*)a.y, ldb); break;
+                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb); break;
             MXD(4) MXD(8) MXD(16) MXD(32) MXD(64) MXD(128) MXD(256)
 #undef MXD
             default: return hipErrorInvalidValue;
