@@ -47,7 +47,8 @@
  *    writes Y = 0 (an empty sum).
  *  - Inputs must be finite; the result for non-finite inputs is unspecified.
  *  - MX_ERR_HIP is returned when a launch fails (hipGetLastError after the launch).
- *  - Rows longer than 2^25 elements (k > 33,554,432) return MX_ERR_UNSUPPORTED.
+ *  - Rows longer than 2^25 elements (k > 33,554,432; for mx_gemm k > 4,194,304) return
+ *    MX_ERR_UNSUPPORTED.
  */
 #ifndef MX_H
 #define MX_H

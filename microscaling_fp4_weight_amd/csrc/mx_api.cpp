@@ -26,7 +26,8 @@ constexpr size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 // Large tensors are processed in row chunks so that every launch indexes fewer than 2^29
 // work units (the kernels use 32-bit unit indices and grid sizes); k itself is bounded.
 constexpr int64_t kMaxUnitsPerLaunch = int64_t(1) << 29;
-constexpr int64_t kMaxK = int64_t(1) << 25;  // keeps per-workgroup buffer ranges below 2^31 bytes
+constexpr int64_t kMaxK = int64_t(1) << 25;      // keeps per-workgroup buffer ranges below 2^31 bytes
+constexpr int64_t kMaxGemmK = int64_t(1) << 22;  // 256-row operand tiles of k/2 bytes stay below 2^31
 
 int64_t chunk_rows(int64_t k)
 {
@@ -170,7 +171,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     const size_t need = mx_gemm_workspace_size(m, n, k, block, mode);
     if (workspace_bytes < need || (need && !workspace)) return MX_ERR_INVALID_ARG;
     if (need && !aligned16(workspace)) return MX_ERR_ALIGNMENT;
-    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
+    if (k > kMaxGemmK) return MX_ERR_UNSUPPORTED;
 
     mxk::GemmArgs a;
     a.x = static_cast<const uint16_t*>(x);

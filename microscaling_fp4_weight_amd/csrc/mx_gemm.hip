@@ -557,6 +557,7 @@ hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t st)
 hipError_t launch_gemm_a4(const GemmArgs& a, hipStream_t st)
 {
     // activations were quantized into the workspace (block 32, E8M0) by the caller
+    if (a.k % 128 == 0) return launch_gemm_a4_mfma(a, st);
     const dim3 grid((unsigned)((a.n + TN - 1) / TN), (unsigned)((a.m + TM - 1) / TM));
     if (a.y_bf16) hipLaunchKernelGGL((gemm_a4_kernel<true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((gemm_a4_kernel<false>), grid, dim3(256), 0, st, a);

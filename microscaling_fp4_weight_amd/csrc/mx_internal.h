@@ -75,6 +75,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_a4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_a4_mfma(const GemmArgs& a, hipStream_t st);
 hipError_t launch_fill_zero(void* y, int64_t m, int64_t n, int64_t ldy, bool bf16, hipStream_t st);
 
 }  // namespace mxk
