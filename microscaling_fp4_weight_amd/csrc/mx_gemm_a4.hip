@@ -6,15 +6,16 @@
 //
 // Tiling: a workgroup computes a 256 x 256 output tile with 4 waves (2 x 2), each a 128 x 128
 // sub-tile of 4 x 4 v_mfma_scale_f32_32x32x64_f8f6f4 results (FP4 operands, fp32
-// accumulators in AGPRs).  The k loop advances 128 elements per stage; each stage's operand
-// tiles (256 rows x 64 code bytes for X and for W, plus 4 E8M0 bytes per row) travel
+// accumulators in AGPRs).  The k loop advances 256 elements per stage; each stage's operand
+// tiles (256 rows x 128 code bytes for X and for W, plus 8 E8M0 bytes per row) travel
 // HBM -> LDS with buffer_load ... lds (no register round trip; rows or k beyond the tensor
-// read as zero), through a 3-deep ring of LDS buffers so that two stages are in flight while
-// one is computed.  In LDS, the four 16-byte chunks of each 64-byte row are rotated by
-// (row / 4) % 4 so that the fragment reads (32 rows x 16 bytes per half-wave) hit distinct
-// banks.  In the row-major layout a lane's 16 code bytes (32 consecutive k of one row) and
-// its scale byte are exactly one MFMA operand slice and the scale that goes with it.
-// Workgroups are mapped so that the m-tiles sharing a weight tile run on the same XCD.
+// read as zero), double-buffered.  A stage row is one whole 128-byte cache line, which halves
+// the number of L2 requests against 64-byte row pieces.  In LDS, the eight 16-byte chunks of
+// each row are permuted by XOR with (row / 2) % 8 so that the fragment reads (16 rows x 16
+// bytes per group of lanes) hit distinct banks.  In the row-major layout a lane's 16 code
+// bytes (32 consecutive k of one row) and its scale byte are exactly one MFMA operand slice
+// and the scale that goes with it.  Workgroups are mapped so that the m-tiles sharing a
+// weight tile run on the same XCD.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -22,38 +23,50 @@ namespace mxk {
 
 namespace a4 {
 
-constexpr int BM = 256, BN = 256, BK = 128, STAGES = 3;
-constexpr int ROWB = BK / 2;                       // code bytes per row per stage (64)
-constexpr int CODE_BYTES = BM * ROWB;              // 16 KB per operand per stage
-constexpr int SCALE_BYTES = BM * (BK / 32);        // 1 KB per operand per stage
+constexpr int BM = 256, BN = 256, BK = 256, STAGES = 2;
+constexpr int ROWB = BK / 2;                       // code bytes per row per stage (128)
+constexpr int SROW = BK / 32;                      // scale bytes per row per stage (8)
+constexpr int CODE_BYTES = BM * ROWB;              // 32 KB per operand per stage
+constexpr int SCALE_BYTES = BM * SROW;             // 2 KB per operand per stage
 constexpr int STAGE_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES;
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;    // 104448
-constexpr int LOADS_PER_STAGE = 10;                // per wave: 4 + 4 code loads, 1 + 1 scale loads
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;    // 139264 (of 160 KB)
+constexpr int LOADS_PER_STAGE = 20;                // per wave: 8 + 8 code loads, 2 + 2 scale loads
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) { return chunk ^ ((row >> 2) & 3u); }
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) { return chunk ^ ((row >> 1) & 7u); }
 
-// Issue one stage's loads (this wave's share) into LDS stage buffer `buf`.
-__device__ __forceinline__ void issue_stage(uint8_t* lds, int buf, int wave, int lane, uint32_t k0,
-                                            rsrc_t ac, rsrc_t bc, rsrc_t as, rsrc_t bs,
-                                            uint32_t K)
+// Issue this wave's share of one stage's loads into the LDS stage buffer at `st`.
+// Codes: each load covers 8 rows x 128 bytes (lane: row lane/8, LDS chunk lane%8).
+// Scales: LDS dword p (of 512 per operand) holds dword p%2 (k 128 (p%2) .. +127 of the
+// stage) of row 128 (p / 256) + 32 ((p / 2) % 4) + (p / 8) % 32, so that the eight dwords a
+// lane needs (rows i*32 + r, i = 0..3, of its 128-row half) are 32 contiguous bytes.
+__device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uint32_t k0,
+                                            rsrc_t ac, rsrc_t bc, rsrc_t as, rsrc_t bs, uint32_t K)
 {
-    uint8_t* st = lds + buf * STAGE_BYTES;
     const uint32_t rowb = K / 2, srow = K / 32;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint32_t row = (uint32_t)(wave * 4 + q) * 16 + (lane >> 2);   // 16 rows per load
-        const uint32_t c = swz(row, lane & 3);                              // global chunk
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t grp = (uint32_t)(wave * 8 + q);           // 8-row group, 0..31
+        const uint32_t row = grp * 8 + (lane >> 3);
+        const uint32_t c = swz(row, lane & 7);                   // global chunk for this LDS slot
         const uint32_t kk = k0 + 32 * c;
         const uint32_t off = kk < K ? row * rowb + kk / 2 : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ac, (lds_void*)(st + (wave * 4 + q) * 1024), 16, off, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(bc, (lds_void*)(st + CODE_BYTES + (wave * 4 + q) * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ac, (lds_void*)(st + grp * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bc, (lds_void*)(st + CODE_BYTES + grp * 1024), 16, off, 0, 0, 0);
     }
-    const uint32_t srow_i = (uint32_t)wave * 64 + lane;  // one scale dword (4 bytes = 128 k) per row
-    const uint32_t soff = k0 < K ? srow_i * srow + k0 / 32 : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_void*)(st + 2 * CODE_BYTES + wave * 256), 4, soff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_void*)(st + 2 * CODE_BYTES + SCALE_BYTES + wave * 256), 4, soff, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t p = (uint32_t)(wave * 2 + t) * 64 + lane;
+        const uint32_t row = (p >> 8) * 128 + ((p >> 1) & 3) * 32 + ((p >> 3) & 31);
+        const uint32_t kk = k0 + 128 * (p & 1);
+        // beyond k: set the top bit (out of every range) arithmetically rather than by a
+        // select, which the compiler would otherwise turn into a branch around the load
+        const uint32_t beyond = (uint32_t)((int32_t)(K - 1 - kk) >> 31);
+        const uint32_t soff = (row * srow + kk / 32) | (beyond & kOOB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_void*)(st + 2 * CODE_BYTES + (wave * 2 + t) * 256), 4, soff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_void*)(st + 2 * CODE_BYTES + SCALE_BYTES + (wave * 2 + t) * 256), 4, soff, 0, 0, 0);
+    }
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -68,11 +81,82 @@ __device__ __forceinline__ void wait_vmcnt()
 // stage about to be read; the clobber keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt lgkmcnt(0) with the other counters left alone: this wave's LDS reads are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Scale dwords of one operand for a lane: s[0] = {row i=0 k-dword 0, 1; i=1 dword 0, 1},
+// s[1] = the same for i = 2, 3.
+struct Scales { u32x4 s[2]; };
+
+__device__ __forceinline__ int scale_byte(const Scales& sc, int i, int j, uint32_t h)
+{
+    const u32x4 v = sc.s[i >> 1];
+    const int d = j >> 1;                                    // k-steps 0, 1 -> dword 0; 2, 3 -> 1
+    const uint32_t w = (i & 1) ? (d ? v.w : v.z) : (d ? v.y : v.x);
+    return (int)((w >> (8 * ((2 * j + h) & 3))) & 0xFFu);
+}
+
+// One k-step (64 k) of this wave's 4 x 4 block of 32 x 32 MFMA tiles.
+// The weight fragment is the MFMA's A operand and the activation fragment its B operand, so
+// each tile is computed transposed (rows n, columns m): a lane then holds four consecutive n
+// of one output row per group, which the epilogue writes with one vector store.
+template <int J>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const u32x4 (&fa)[4], const u32x4 (&fb)[4],
+                                          const Scales& sa, const Scales& sb, uint32_t h)
+{
+    int asx[4], bsx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        asx[i] = scale_byte(sa, i, J, h);
+        bsx[i] = scale_byte(sb, i, J, h);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int jn = 0; jn < 4; ++jn) {
+            // FP4 operands occupy the low four registers of the 8-register operand; the upper
+            // four are not read, so they are left undefined rather than zeroed
+            const i32x8 av = __builtin_shufflevector((i32x4)fa[i], (i32x4)fa[i], 0, 1, 2, 3, -1, -1, -1, -1);
+            const i32x8 bv = __builtin_shufflevector((i32x4)fb[jn], (i32x4)fb[jn], 0, 1, 2, 3, -1, -1, -1, -1);
+            acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][jn], 4, 4, 0, bsx[jn], 0, asx[i]);
+        }
+}
+
+// Fragment reads of k-step J from a stage buffer: rows i*32 further are 4096 bytes apart and
+// share the chunk permutation, so one base offset per operand serves all four.
+template <int J>
+__device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t baseA, uint32_t baseB, uint32_t perm,
+                                           u32x4 (&fa)[4], u32x4 (&fb)[4])
+{
+    const uint32_t chunk = 16 * ((2 * J) ^ perm);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        fa[i] = *reinterpret_cast<const u32x4*>(st + baseA + chunk + i * 32 * ROWB);
+        fb[i] = *reinterpret_cast<const u32x4*>(st + CODE_BYTES + baseB + chunk + i * 32 * ROWB);
+    }
+}
+
+__device__ __forceinline__ void read_scales(const uint8_t* st, uint32_t offSA, uint32_t offSB, Scales& sa, Scales& sb)
+{
+    sa.s[0] = *reinterpret_cast<const u32x4*>(st + offSA);
+    sa.s[1] = *reinterpret_cast<const u32x4*>(st + offSA + 16);
+    sb.s[0] = *reinterpret_cast<const u32x4*>(st + offSB);
+    sb.s[1] = *reinterpret_cast<const u32x4*>(st + offSB + 16);
+}
+
+// scheduling: within a k-step, one MFMA, then the fragment reads for the next k-step, then
+// the remaining fifteen MFMAs, so that the reads' latency hides behind matrix work
+#define A4_SCHED_STEP(ID)                                  \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);    \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, ID);    \
+    __builtin_amdgcn_sched_group_barrier(0x008, 15, ID)
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_a4_kernel(const GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform across the wave; saying so keeps LDS-DMA destinations scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const uint32_t K = (uint32_t)a.k;
 
@@ -104,77 +188,144 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // Pipeline: one stage (four k-steps) per iteration; the fragments of a k-step are read
+    // from LDS while the MFMAs of the previous k-step run.  Before the last k-step of a stage,
+    // once this stage's reads have completed and the next stage has landed, one barrier both
+    // publishes the next stage and frees the current buffer, which then receives the stage
+    // after next.  Stages past the end of k load as zeros (their offsets are out of range),
+    // so every iteration has the same shape.
     const int S = (int)((K + BK - 1) / BK);
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-        if (p < S) issue_stage(lds, p, wave, lane, (uint32_t)p * BK, ac, bc, as, bs, K);
+    issue_stage(lds, wave, lane, 0, ac, bc, as, bs, K);
+    issue_stage(lds + STAGE_BYTES, wave, lane, BK, ac, bc, as, bs, K);
 
     const uint32_t r32 = lane & 31, h = lane >> 5;
+    const uint32_t perm = h ^ ((r32 >> 1) & 7u);              // chunk (2j + h) -> slot (2j) ^ perm
+    const uint32_t baseA = (wm * 128 + r32) * ROWB;
+    const uint32_t baseB = (wn * 128 + r32) * ROWB;
+    const uint32_t offSA = 2 * CODE_BYTES + (wm * 256 + r32 * 8) * 4;
+    const uint32_t offSB = 2 * CODE_BYTES + SCALE_BYTES + (wn * 256 + r32 * 8) * 4;
+
+    u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+    Scales sa, sb;
+    wait_vmcnt<LOADS_PER_STAGE>();
+    barrier_only();
+    read_frags<0>(lds, baseA, baseB, perm, f0a, f0b);
+    read_scales(lds, offSA, offSB, sa, sb);
+
+    uint32_t cur = 0;  // byte offset of stage s's buffer
     for (int s = 0; s < S; ++s) {
-        if (s + 1 < S) wait_vmcnt<LOADS_PER_STAGE>();
-        else wait_vmcnt<0>();
+        const uint32_t nxt = cur ^ (uint32_t)STAGE_BYTES;
+        read_frags<1>(lds + cur, baseA, baseB, perm, f1a, f1b);
+        mfma_step<0>(acc, f0a, f0b, sa, sb, h);
+        A4_SCHED_STEP(0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags<2>(lds + cur, baseA, baseB, perm, f0a, f0b);
+        mfma_step<1>(acc, f1a, f1b, sa, sb, h);
+        A4_SCHED_STEP(1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags<3>(lds + cur, baseA, baseB, perm, f1a, f1b);
+        mfma_step<2>(acc, f0a, f0b, sa, sb, h);
+        A4_SCHED_STEP(2);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm0();
+        wait_vmcnt<0>();
         barrier_only();
-        if (s + STAGES - 1 < S)
-            issue_stage(lds, (s + STAGES - 1) % STAGES, wave, lane, (uint32_t)(s + STAGES - 1) * BK, ac, bc, as, bs, K);
-        const uint8_t* st = lds + (s % STAGES) * STAGE_BYTES;
-        const uint32_t* sa = reinterpret_cast<const uint32_t*>(st + 2 * CODE_BYTES);
-        const uint32_t* sbw = reinterpret_cast<const uint32_t*>(st + 2 * CODE_BYTES + SCALE_BYTES);
-        uint32_t ascale[4], bscale[4];
-        u32x4 fa[2][4], fb[2][4];  // fragments of k-step j in set j (both sets in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        issue_stage(lds + cur, wave, lane, (uint32_t)(s + STAGES) * BK, ac, bc, as, bs, K);
+        Scales sa_n, sb_n;
+        read_frags<0>(lds + nxt, baseA, baseB, perm, f0a, f0b);
+        read_scales(lds + nxt, offSA, offSB, sa_n, sb_n);
+        mfma_step<3>(acc, f1a, f1b, sa, sb, h);
+        // next stage's first fragments and scales first, then the twenty stage loads spread
+        // between MFMAs so that the matrix pipe stays busy while they are issued
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 3);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t c = 2 * j + h;  // this lane's 16-byte chunk of the 64-byte row
+        for (int g = 0; g < 5; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+            __builtin_amdgcn_sched_group_barrier(0x020, 4, 3);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 3);
+        // keep the next stage's reads in this iteration (not sunk into the next one)
+        asm volatile("" ::: "memory");
+        sa = sa_n;
+        sb = sb_n;
+        cur = nxt;
+    }
+    wait_vmcnt<0>();
+
+    // Epilogue.  Transposed 32x32 result layout: for tile (i, jn) a lane holds output row
+    // m = i*32 + lane%32 and, for group q = e/4, columns n = jn*32 + 8q + 4*(lane/32) + e%4.
+    // Rows of a wave's 128 x 128 block are staged through LDS (each wave in a region of its
+    // own, rows padded against bank conflicts) and written back as whole 16-byte chunks, 256
+    // or 512 contiguous bytes per output row, so that every store fills whole cache lines.
+    // Stores go through a buffer descriptor; out-of-range chunks get an out-of-range offset
+    // and are dropped.
+    constexpr uint32_t ESZ = OUT_BF16 ? 2 : 4;
+    const rsrc_t yr = make_rsrc(static_cast<uint8_t*>(a.y) + (m0 * a.ldy + n0) * ESZ, 0x7FFFFFFFu);
+    const uint32_t ldy = (uint32_t)a.ldy;
+    const uint32_t mlim = mrows, nlim = nrows;
+    constexpr uint32_t CE = 16 / ESZ;  // elements per 16-byte chunk
+    // chunk stores need 16-byte aligned rows and chunks wholly in or out of range
+    const bool vec = (ldy % CE) == 0 && (nlim % CE) == 0;
+    if (vec) {
+        constexpr int PASSES = OUT_BF16 ? 1 : 2;             // 128 or 64 rows per pass
+        constexpr int IPP = 4 / PASSES;                       // 32-row blocks per pass
+        constexpr uint32_t RB = 128 * ESZ;                    // bytes of a wave row
+        constexpr uint32_t PITCH = RB + (OUT_BF16 ? 8 : 16);
+        constexpr uint32_t CPR = RB / 16;                     // chunks per row (16 or 32)
+        constexpr uint32_t RPI = 64 / CPR;                    // rows per store instruction
+        constexpr uint32_t PASS_ROWS = 128 / PASSES;
+        static_assert(4 * PASS_ROWS * PITCH <= (uint32_t)LDS_BYTES, "epilogue staging exceeds LDS");
+        uint8_t* stg = lds + wave * PASS_ROWS * PITCH;
+        barrier_only();  // every wave is done reading the stage buffers
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t ra = wm * 128 + i * 32 + r32;
-                const uint32_t rb = wn * 128 + i * 32 + r32;
-                fa[j][i] = *reinterpret_cast<const u32x4*>(st + ra * ROWB + 16 * swz(ra, c));
-                fb[j][i] = *reinterpret_cast<const u32x4*>(st + CODE_BYTES + rb * ROWB + 16 * swz(rb, c));
+        for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+            for (int ii = 0; ii < IPP; ++ii)
+#pragma unroll
+                for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x16& c = acc[pass * IPP + ii][jn];
+                        const float v0 = c[4 * q] * a.g, v1 = c[4 * q + 1] * a.g, v2 = c[4 * q + 2] * a.g, v3 = c[4 * q + 3] * a.g;
+                        uint8_t* dst = stg + (ii * 32 + r32) * PITCH + (jn * 32 + 8 * q + 4 * h) * ESZ;
+                        if constexpr (OUT_BF16) {
+                            const u32x2 w = {__builtin_bit_cast(uint32_t, bf16x2{(__bf16)v0, (__bf16)v1}),
+                                             __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v2, (__bf16)v3})};
+                            *reinterpret_cast<u32x2*>(dst) = w;
+                        } else {
+                            *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+                        }
+                    }
+            // read back row-contiguous chunks (LDS accesses of one wave complete in order)
+#pragma unroll
+            for (uint32_t t = 0; t < PASS_ROWS / RPI; ++t) {
+                const uint32_t row = t * RPI + lane / CPR, chunk = lane % CPR;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * PITCH + chunk * 16);
+                const uint32_t mm = wm * 128 + pass * PASS_ROWS + row, nn = wn * 128 + chunk * CE;
+                const uint32_t off = (mm < mlim && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
+                bstore128(yr, off, v);
             }
         }
+    } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ascale[i] = sa[wm * 128 + i * 32 + r32];
-            bscale[i] = sbw[wn * 128 + i * 32 + r32];
-        }
+            const uint32_t mm = wm * 128 + i * 32 + r32;
+            const bool mok = mm < mlim;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {  // two MFMA k-steps of 64
-            const uint32_t c = 2 * j + h;
-            int asx[4], bsx[4];
+            for (int jn = 0; jn < 4; ++jn)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                asx[i] = (int)((ascale[i] >> (8 * c)) & 0xFFu);
-                bsx[i] = (int)((bscale[i] >> (8 * c)) & 0xFFu);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jn = 0; jn < 4; ++jn) {
-                    const i32x8 av = {(int)fa[j][i].x, (int)fa[j][i].y, (int)fa[j][i].z, (int)fa[j][i].w, 0, 0, 0, 0};
-                    const i32x8 bv = {(int)fb[j][jn].x, (int)fb[j][jn].y, (int)fb[j][jn].z, (int)fb[j][jn].w, 0, 0, 0, 0};
-                    acc[i][jn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        av, bv, acc[i][jn], 4, 4, 0, asx[i], 0, bsx[jn]);
+                for (int e = 0; e < 16; ++e) {
+                    const uint32_t nn = wn * 128 + jn * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                    const uint32_t off = (mok && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
+                    const float v = acc[i][jn][e] * a.g;
+                    if constexpr (OUT_BF16) bstore16(yr, off, __builtin_bit_cast(uint16_t, (__bf16)v));
+                    else bstore32(yr, off, __builtin_bit_cast(uint32_t, v));
                 }
         }
     }
-
-    // epilogue: 32x32 result layout -- lane holds rows 8*(e/4) + 4*(lane/32) + e%4, column lane%32
-    const bool full = m0 + BM <= a.m && n0 + BN <= a.n;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-            const int64_t n = n0 + wn * 128 + jn * 32 + r32;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (full || (m < a.m && n < a.n)) {
-                    const float v = acc[i][jn][e] * a.g;
-                    if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(a.y)[m * a.ldy + n] = (__bf16)v;
-                    else reinterpret_cast<float*>(a.y)[m * a.ldy + n] = v;
-                }
-            }
-        }
 }
 
 }  // namespace a4
@@ -188,6 +339,8 @@ hipError_t launch_gemm_a4_mfma(const GemmArgs& a, hipStream_t st)
     static const hipError_t attr_f32 = hipFuncSetAttribute(
         (const void*)a4::gemm_a4_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, a4::LDS_BYTES);
     if (attr_bf16 != hipSuccess || attr_f32 != hipSuccess) return attr_bf16 != hipSuccess ? attr_bf16 : attr_f32;
+    // output offsets within a tile are 32-bit: (BM - 1) * ldy + BN elements must fit
+    if (((int64_t)(a4::BM - 1) * a.ldy + a4::BN) * (a.y_bf16 ? 2 : 4) >= (int64_t)0x7FFFFFFF) return hipErrorInvalidValue;
     const unsigned tiles = (unsigned)(((a.m + a4::BM - 1) / a4::BM) * ((a.n + a4::BN - 1) / a4::BN));
     if (a.y_bf16) hipLaunchKernelGGL(a4::gemm_a4_kernel<true>, dim3(tiles), dim3(256), a4::LDS_BYTES, st, a);
     else hipLaunchKernelGGL(a4::gemm_a4_kernel<false>, dim3(tiles), dim3(256), a4::LDS_BYTES, st, a);
