@@ -26,12 +26,21 @@
  *  MX_SCALE_E8M0:  2^(byte - 127), bytes 0..254; never zero.
  *  tensor_scale g: fp32, finite, normal, > 0 (1.0 = single-level scaling).
  *
- * Layout MX_LAYOUT_ROWMAJOR (the only layout defined):
+ * Layout MX_LAYOUT_ROWMAJOR:
  *  codes : rows x (k/2) bytes, row-major, no padding; byte j of row r holds element 2j in
  *          its low nibble and element 2j+1 in its high nibble ([FP4L] section 4.3: two FP4
  *          values per byte).
  *  scales: rows x (k/block) bytes, row-major, no padding; byte b of row r is the scale of
  *          elements [b*block, (b+1)*block) of row r.
+ * Layout MX_LAYOUT_TILED (block 32 only; k <= 4,194,304): the same codes; the scales are
+ *  stored in the order the W4A4 matrix-core GEMM streams them, so that each of its k steps
+ *  reads one contiguous 2 KB piece instead of 8 bytes from each of 256 rows.  Rows are
+ *  grouped in tiles of 256 (T = r / 256, t = r % 256) and blocks in stages of 8 (256
+ *  elements; S = b / 8, u = b % 8); with KS = ceil(k / 256) stages, the scale of (r, b) is
+ *  byte  2048 (T KS + S) + 1024 (t / 128) + 32 (t % 32) + 8 ((t / 32) % 4) + u.
+ *  The buffer holds ceil(rows / 256) KS 2048 bytes (mx_scale_bytes).  Bytes of blocks
+ *  past the end of k in a row's last stage are written as 0 by mx_quantize; bytes of rows
+ *  past the end are never written nor used.
  *  Dense tensors (x, y) are row-major with a leading dimension (row stride) in ELEMENTS.
  *
  * Conventions common to every entry point
@@ -70,7 +79,7 @@ typedef enum {
 
 typedef enum { MX_SCALE_E4M3 = 0, MX_SCALE_UE5M3 = 1, MX_SCALE_E8M0 = 2 } mx_scale_fmt;
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
-typedef enum { MX_LAYOUT_ROWMAJOR = 0 } mx_layout;
+typedef enum { MX_LAYOUT_ROWMAJOR = 0, MX_LAYOUT_TILED = 1 } mx_layout;
 typedef enum { MX_A16 = 0, MX_A4 = 1 } mx_act_mode;
 
 /*
@@ -79,11 +88,13 @@ typedef enum { MX_A16 = 0, MX_A4 = 1 } mx_act_mode;
  *  block      : block size along k, one of 4, 8, 16, 32, 64, 128, 256; k % block == 0.
  *  fmt        : block-scale format.
  *  tensor_scale: per-tensor fp32 scale g ([MXS] section 3.1 item 3; 1.0 for none).
+ *  layout     : MX_LAYOUT_ROWMAJOR or MX_LAYOUT_TILED (scale order, above).
  *  codes      : output, rows x k/2 bytes (layout above).
- *  scales     : output, rows x k/block bytes.
+ *  scales     : output, mx_scale_bytes(rows, k, block, layout) bytes.
  * Errors: MX_ERR_INVALID_ARG for a null pointer, rows/k/ld_x negative or ld_x < k, k odd,
  * a block size outside the list, k % block != 0, an unknown fmt/x_type/layout, or g not a
- * finite normal positive number; MX_ERR_ALIGNMENT for a misaligned pointer.
+ * finite normal positive number; MX_ERR_UNSUPPORTED for MX_LAYOUT_TILED with block != 32
+ * or k > 4,194,304; MX_ERR_ALIGNMENT for a misaligned pointer.
  * Codes and scale bytes are bit-exact with the definition above.
  */
 mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
@@ -103,9 +114,16 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
                         void* y, mx_dtype y_type, int64_t ld_y, void* stream);
 
 /*
+ * mx_scale_bytes -- size in bytes of the scale buffer of a rows x k tensor quantized with
+ * this block size and layout (rows * k / block for MX_LAYOUT_ROWMAJOR; the tiled size
+ * above for MX_LAYOUT_TILED).  Returns 0 for arguments mx_quantize would reject.
+ */
+size_t mx_scale_bytes(int64_t rows, int64_t k, int block, mx_layout layout);
+
+/*
  * mx_gemm_workspace_size -- bytes of device workspace mx_gemm needs for this shape and mode
- * (0 when none).  MX_A4 needs room for the quantized activations:
- * m*k/2 code bytes + m*k/32 scale bytes, each rounded up to 256 bytes.
+ * (0 when none).  MX_A4 needs room for the quantized activations: m*k/2 code bytes and
+ * mx_scale_bytes(m, k, 32, MX_LAYOUT_TILED) scale bytes, each rounded up to 256 bytes.
  * Returns 0 for arguments mx_gemm would reject.
  */
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode);
@@ -113,9 +131,11 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act
 /*
  * mx_gemm -- Y = X . dequant(Wq)^T with fp32 accumulation.
  *  x          : activations, bf16, m x k, row stride ld_x >= k.
- *  w_codes    : weight codes, n x k/2 bytes; w_scales: n x k/block bytes (mx_quantize
- *               output for an n x k weight).
- *  block, fmt, tensor_scale, layout: those of the weight.
+ *  w_codes    : weight codes, n x k/2 bytes; w_scales: mx_scale_bytes(n, k, block, layout)
+ *               bytes (mx_quantize output for an n x k weight).
+ *  block, fmt, tensor_scale, layout: those of the weight.  MX_LAYOUT_TILED weights are
+ *               accepted in MX_A4 mode with k % 128 == 0 (MX_ERR_UNSUPPORTED otherwise);
+ *               they make the W4A4 product faster.
  *  mode       : MX_A16 -- X is used as given (bf16 x dequantized weight);
  *               MX_A4  -- X is first MX-quantized along k with block 32, E8M0 scales and
  *               g = 1 (bit-identical to mx_quantize with those arguments) into `workspace`,

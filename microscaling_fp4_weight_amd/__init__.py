@@ -17,8 +17,8 @@ import os
 
 import torch
 
-__all__ = ["mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
-           "mx_status_string", "MXError", "lib", "FMT", "MODE", "DTYPE", "STATUS"]
+__all__ = ["mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_scale_bytes",
+           "mx_status_string", "MXError", "lib", "FMT", "MODE", "DTYPE", "LAYOUT", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmx.so")
@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libmx.so")
 FMT = {"e4m3": 0, "ue5m3": 1, "e8m0": 2}
 DTYPE = {"f32": 0, "bf16": 1}
 MODE = {"a16": 0, "a4": 1}
-LAYOUT = {"rowmajor": 0}
+LAYOUT = {"rowmajor": 0, "tiled": 1}
 STATUS = {0: "MX_OK", -1: "MX_ERR_INVALID_ARG", -2: "MX_ERR_UNSUPPORTED", -3: "MX_ERR_ALIGNMENT",
           -4: "MX_ERR_HIP"}
 
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.mx_quantize.restype = i32
     L.mx_dequantize.argtypes = [vp, vp, i64, i64, i32, i32, f32, i32, vp, i32, i64, vp]
     L.mx_dequantize.restype = i32
+    L.mx_scale_bytes.argtypes = [i64, i64, i32, i32]
+    L.mx_scale_bytes.restype = sz
     L.mx_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     L.mx_gemm_workspace_size.restype = sz
     L.mx_gemm.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp,
@@ -101,12 +103,17 @@ def mx_quantize(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0
                 layout: str = "rowmajor", codes: torch.Tensor | None = None,
                 scales: torch.Tensor | None = None, stream=None):
     """MX-quantize a 2-D bf16/fp32 GPU tensor (rows x k) along k.
-    Returns (codes uint8 rows x k/2, scales uint8 rows x k/block)."""
+    Returns (codes uint8 rows x k/2, scales uint8: rows x k/block for layout "rowmajor", a
+    flat buffer of mx_scale_bytes(...) bytes for layout "tiled")."""
     rows, k, ld = _rows_ld(x, "x")
     if codes is None:
         codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((rows, k // max(block, 1)), dtype=torch.uint8, device=x.device)
+        if layout == "rowmajor":
+            scales = torch.empty((rows, k // max(block, 1)), dtype=torch.uint8, device=x.device)
+        else:
+            scales = torch.empty(max(mx_scale_bytes(rows, k, block, layout), 1), dtype=torch.uint8,
+                                 device=x.device)
     st = lib().mx_quantize(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt],
                            tensor_scale, LAYOUT[layout], _ptr(codes), _ptr(scales), _stream(stream))
     _check(st, "mx_quantize")
@@ -125,6 +132,10 @@ def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, k: int, block: int,
                              LAYOUT[layout], _ptr(y), _dtype_code(y.dtype), ld, _stream(stream))
     _check(st, "mx_dequantize")
     return y
+
+
+def mx_scale_bytes(rows: int, k: int, block: int, layout: str = "rowmajor") -> int:
+    return int(lib().mx_scale_bytes(rows, k, block, LAYOUT[layout]))
 
 
 def mx_gemm_workspace_size(m: int, n: int, k: int, block: int, mode: str) -> int:

@@ -44,14 +44,39 @@ mx_status check_quantized(int64_t rows, int64_t k, int block, mx_scale_fmt fmt, 
         return MX_ERR_INVALID_ARG;
     if (fmt != MX_SCALE_E4M3 && fmt != MX_SCALE_UE5M3 && fmt != MX_SCALE_E8M0)
         return MX_ERR_INVALID_ARG;
-    if (layout != MX_LAYOUT_ROWMAJOR) return MX_ERR_INVALID_ARG;
+    if (layout != MX_LAYOUT_ROWMAJOR && layout != MX_LAYOUT_TILED) return MX_ERR_INVALID_ARG;
     if (!valid_g(g)) return MX_ERR_INVALID_ARG;
+    // the tiled scale layout is defined for 32-element blocks, and rows are processed in
+    // whole 256-row tiles per launch, which bounds k as for the matmul
+    if (layout == MX_LAYOUT_TILED && (block != 32 || k > kMaxGemmK)) return MX_ERR_UNSUPPORTED;
     return MX_OK;
+}
+
+// Rows per launch for a quantized tensor: whole 256-row tiles for tiled scales.
+int64_t launch_rows(int64_t k, mx_layout layout)
+{
+    int64_t step = chunk_rows(k);
+    if (layout == MX_LAYOUT_TILED) step = step < mxk::kTileRows ? mxk::kTileRows : step / mxk::kTileRows * mxk::kTileRows;
+    return step;
+}
+
+// Offset of row r0's scales (r0 a multiple of 256 for tiled scales).
+int64_t scale_offset(int64_t r0, int64_t k, int block, mx_layout layout)
+{
+    return layout == MX_LAYOUT_TILED ? r0 / mxk::kTileRows * mxk::tiled_stages(k) * mxk::kTileBytes : r0 * (k / block);
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t mx_scale_bytes(int64_t rows, int64_t k, int block, mx_layout layout)
+{
+    if (rows < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;
+    if (layout == MX_LAYOUT_ROWMAJOR) return (size_t)rows * (size_t)(k / block);
+    if (layout == MX_LAYOUT_TILED && block == 32 && k <= kMaxGemmK) return (size_t)mxk::tiled_scale_bytes(rows, k);
+    return 0;
+}
 
 const char* mx_status_string(mx_status s)
 {
@@ -90,12 +115,13 @@ mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, i
     a.codes = codes;
     a.scales = scales;
     a.fast = (k % 32 == 0) && ((ld_x * esize) % 16 == 0);
-    const int64_t step = chunk_rows(k);
+    a.ts_ks = layout == MX_LAYOUT_TILED ? (uint32_t)mxk::tiled_stages(k) : 0u;
+    const int64_t step = launch_rows(k, layout);
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         mxk::QuantArgs c = a;
         c.x = static_cast<const uint8_t*>(x) + r0 * ld_x * esize;
         c.codes = codes + r0 * (k / 2);
-        c.scales = scales + r0 * (k / block);
+        c.scales = scales + scale_offset(r0, k, block, layout);
         c.rows = rows - r0 < step ? rows - r0 : step;
         if (mxk::launch_quantize(c, static_cast<hipStream_t>(stream)) != hipSuccess) return MX_ERR_HIP;
     }
@@ -127,11 +153,12 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
     a.bf16 = y_type == MX_BF16;
     a.ldy = ld_y;
     a.fast = (k % 32 == 0) && ((ld_y * esize) % 16 == 0);
-    const int64_t step = chunk_rows(k);
+    a.ts_ks = layout == MX_LAYOUT_TILED ? (uint32_t)mxk::tiled_stages(k) : 0u;
+    const int64_t step = launch_rows(k, layout);
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         mxk::DequantArgs c = a;
         c.codes = codes + r0 * (k / 2);
-        c.scales = scales + r0 * (k / block);
+        c.scales = scales + scale_offset(r0, k, block, layout);
         c.y = static_cast<uint8_t*>(y) + r0 * ld_y * esize;
         c.rows = rows - r0 < step ? rows - r0 : step;
         if (mxk::launch_dequantize(c, static_cast<hipStream_t>(stream)) != hipSuccess) return MX_ERR_HIP;
@@ -144,7 +171,8 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act
     if (m < 0 || n < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;
     if (mode != MX_A4) return 0;
     if (block != 32) return 0;
-    return round256((size_t)m * (size_t)(k / 2)) + round256((size_t)m * (size_t)(k / 32));
+    // activation scales in the tiled layout (never smaller than row-major ones)
+    return round256((size_t)m * (size_t)(k / 2)) + round256((size_t)mxk::tiled_scale_bytes(m, k));
 }
 
 mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
@@ -187,14 +215,20 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     a.y = y;
     a.y_bf16 = y_type == MX_BF16;
     a.ldy = ld_y;
+    a.ws_tiled = layout == MX_LAYOUT_TILED;
     a.xq_codes = nullptr;
     a.xq_scales = nullptr;
+    // weight scales in the tiled layout are read by the W4A4 matrix-core kernel only
+    const bool mfma_a4 = mode == MX_A4 && mxk::a4_uses_mfma(a);
+    if (a.ws_tiled && !mfma_a4) return MX_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    // rows of Y per launch: keeps per-launch unit counts (outputs, pre-pass pairs) < 2^29
+    // rows of Y per launch: keeps per-launch unit counts (outputs, pre-pass pairs) < 2^29;
+    // W4A4 launches take whole 256-row tiles (the activation scales are tiled)
     const int64_t per_row = n > k / 2 ? n : k / 2;
     int64_t step = kMaxUnitsPerLaunch / (per_row > 0 ? per_row : 1);
     step = step < 1 ? 1 : (step > 256 ? step & ~int64_t(255) : step);
+    if (mode == MX_A4 && step < 256) step = 256;
     for (int64_t r0 = 0; r0 < m; r0 += step) {
         mxk::GemmArgs c = a;
         c.m = m - r0 < step ? m - r0 : step;
@@ -207,7 +241,8 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
         // W4A4: MX-quantize the activations (block 32, E8M0, g = 1) into the workspace with
         // the quantize kernel itself, then run the FP4 matrix-core product.
         c.xq_codes = ws + r0 * (k / 2);
-        c.xq_scales = ws + round256((size_t)m * (size_t)(k / 2)) + r0 * (k / 32);
+        const mx_layout xl = mfma_a4 ? MX_LAYOUT_TILED : MX_LAYOUT_ROWMAJOR;
+        c.xq_scales = ws + round256((size_t)m * (size_t)(k / 2)) + scale_offset(r0, k, 32, xl);
         mxk::QuantArgs q;
         q.x = c.x;
         q.bf16 = true;
@@ -220,6 +255,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
         q.codes = c.xq_codes;
         q.scales = c.xq_scales;
         q.fast = (ld_x * 2) % 16 == 0;  // k % 32 == 0 holds (block 32)
+        q.ts_ks = mfma_a4 ? (uint32_t)mxk::tiled_stages(k) : 0u;
         if (mxk::launch_quantize(q, s) != hipSuccess) return MX_ERR_HIP;
         if (mxk::launch_gemm_a4(c, s) != hipSuccess) return MX_ERR_HIP;
     }

@@ -293,6 +293,15 @@ __device__ __forceinline__ uint32_t enc_elem_g(uint32_t xbits32, const EncG& p)
     return c | ((xbits32 >> 28) & 8u);
 }
 
+// Byte offset of the scale of (row, 32-element block kb) in the tiled scale layout with ks
+// 256-k stages per row tile (the layout is described with kTileBytes in mx_internal.h).
+__device__ __forceinline__ uint64_t tiled_scale_off(uint32_t row, uint32_t kb, uint32_t ks)
+{
+    const uint32_t r = row & 255u;
+    return ((uint64_t)(row >> 8) * ks + (kb >> 3)) * 2048u + ((r >> 7) << 10) + ((r & 31u) << 5) +
+           (((r >> 5) & 3u) << 3) + (kb & 7u);
+}
+
 // ---------------------------------------------------------------------------------------
 // Buffer loads: a resource descriptor carries a byte range, and lanes whose offset is out of
 // range read zero without a branch (used for masked rows and k-tails).

@@ -557,9 +557,8 @@ hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t st)
 hipError_t launch_gemm_a4(const GemmArgs& a, hipStream_t st)
 {
     // activations were quantized into the workspace (block 32, E8M0) by the caller
-    // the tiled kernel needs k in whole stages of 128 and 32-bit offsets within an output tile
-    const int64_t tile_span = (255 * a.ldy + 256) * (a.y_bf16 ? 2 : 4);
-    if (a.k % 128 == 0 && tile_span < 0x7FFFFFFF) return launch_gemm_a4_mfma(a, st);
+    if (a4_uses_mfma(a)) return launch_gemm_a4_mfma(a, st);
+    if (a.ws_tiled) return hipErrorInvalidValue;  // the direct kernel reads row-major scales
     const dim3 grid((unsigned)((a.n + TN - 1) / TN), (unsigned)((a.m + TM - 1) / TM));
     if (a.y_bf16) hipLaunchKernelGGL((gemm_a4_kernel<true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((gemm_a4_kernel<false>), grid, dim3(256), 0, st, a);

@@ -4,18 +4,18 @@
 // here the matrix cores apply the E8M0 block scales themselves; hotelren.com/news/2192771
 // article "量化技术演进与微缩量化原理", section 6 item 1: FP4 activations with block scales).
 //
-// Tiling: a workgroup computes a 256 x 256 output tile with 4 waves (2 x 2), each a 128 x 128
-// sub-tile of 4 x 4 v_mfma_scale_f32_32x32x64_f8f6f4 results (FP4 operands, fp32
-// accumulators in AGPRs).  The k loop advances 256 elements per stage; each stage's operand
-// tiles (256 rows x 128 code bytes for X and for W, plus 8 E8M0 bytes per row) travel
-// HBM -> LDS with buffer_load ... lds (no register round trip; rows or k beyond the tensor
-// read as zero), double-buffered.  A stage row is one whole 128-byte cache line, which halves
-// the number of L2 requests against 64-byte row pieces.  In LDS, the eight 16-byte chunks of
-// each row are permuted by XOR with (row / 2) % 8 so that the fragment reads (16 rows x 16
-// bytes per group of lanes) hit distinct banks.  In the row-major layout a lane's 16 code
-// bytes (32 consecutive k of one row) and its scale byte are exactly one MFMA operand slice
-// and the scale that goes with it.  Workgroups are mapped so that the m-tiles sharing a
-// weight tile run on the same XCD.
+// Tiling: a workgroup of 8 waves (two per SIMD, so that one wave's matrix work covers the
+// other's waits) computes a 256 x 256 output tile; each wave a 128 x 64 sub-tile of 4 x 2
+// v_mfma_scale_f32_32x32x64_f8f6f4 results (FP4 operands, fp32 accumulators).  The k loop
+// advances 256 elements per stage; each stage's operand tiles (256 rows x 128 code bytes for
+// X and for W, plus 8 E8M0 bytes per row) travel HBM -> LDS with buffer_load ... lds (no
+// register round trip; rows or k beyond the tensor read as zero), double-buffered.  A stage
+// row is one whole 128-byte cache line, which halves the number of L2 requests against
+// 64-byte row pieces.  In LDS, the eight 16-byte chunks of each row are permuted by XOR with
+// (row / 2) % 8 so that the fragment reads (16 rows x 16 bytes per group of lanes) hit
+// distinct banks.  In the row-major layout a lane's 16 code bytes (32 consecutive k of one
+// row) and its scale byte are exactly one MFMA operand slice and the scale that goes with it.
+// Workgroups are mapped so that the m-tiles sharing a weight tile run on the same XCD.
 #include "mx_device.h"
 #include "mx_internal.h"
 
@@ -24,13 +24,15 @@ namespace mxk {
 namespace a4 {
 
 constexpr int BM = 256, BN = 256, BK = 256, STAGES = 2;
+constexpr int WAVES = 8, THREADS = 64 * WAVES;
+constexpr int MI = 4, NJ = 2;                      // per wave: 4 x 2 tiles of 32 x 32 (128 m x 64 n)
 constexpr int ROWB = BK / 2;                       // code bytes per row per stage (128)
 constexpr int SROW = BK / 32;                      // scale bytes per row per stage (8)
 constexpr int CODE_BYTES = BM * ROWB;              // 32 KB per operand per stage
 constexpr int SCALE_BYTES = BM * SROW;             // 2 KB per operand per stage
 constexpr int STAGE_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;    // 139264 (of 160 KB)
-constexpr int LOADS_PER_STAGE = 20;                // per wave: 8 + 8 code loads, 2 + 2 scale loads
+constexpr int LOADS_PER_STAGE = 10;                // per wave: 4 + 4 code loads, 1 + 1 scale loads
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -39,15 +41,19 @@ __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) { return c
 // Issue this wave's share of one stage's loads into the LDS stage buffer at `st`.
 // Codes: each load covers 8 rows x 128 bytes (lane: row lane/8, LDS chunk lane%8).
 // Scales: LDS dword p (of 512 per operand) holds dword p%2 (k 128 (p%2) .. +127 of the
-// stage) of row 128 (p / 256) + 32 ((p / 2) % 4) + (p / 8) % 32, so that the eight dwords a
-// lane needs (rows i*32 + r, i = 0..3, of its 128-row half) are 32 contiguous bytes.
-__device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uint32_t k0,
+// stage) of row 128 (p / 256) + 32 ((p / 2) % 4) + (p / 8) % 32, so that the dwords a lane
+// needs (rows i*32 + r of a 128-row half) are contiguous.  That is the order of one (row
+// tile, stage) block of the tiled scale layout, so tiled scales arrive with one contiguous
+// 256-byte load per wave and operand; row-major scales take one dword per lane from 32 rows
+// per load.  The stage index s is also the block index in the tiled layout.
+template <bool W_TILED>
+__device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uint32_t s,
                                             rsrc_t ac, rsrc_t bc, rsrc_t as, rsrc_t bs, uint32_t K)
 {
-    const uint32_t rowb = K / 2, srow = K / 32;
+    const uint32_t rowb = K / 2, srow = K / 32, k0 = s * BK;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const uint32_t grp = (uint32_t)(wave * 8 + q);           // 8-row group, 0..31
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t grp = (uint32_t)(wave * 4 + q);           // 8-row group, 0..31
         const uint32_t row = grp * 8 + (lane >> 3);
         const uint32_t c = swz(row, lane & 7);                   // global chunk for this LDS slot
         const uint32_t kk = k0 + 32 * c;
@@ -55,18 +61,19 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uin
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ac, (lds_void*)(st + grp * 1024), 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(bc, (lds_void*)(st + CODE_BYTES + grp * 1024), 16, off, 0, 0, 0);
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint32_t p = (uint32_t)(wave * 2 + t) * 64 + lane;
+    const uint32_t p = (uint32_t)wave * 64 + lane;
+    const uint32_t toff = s * 2048u + 4 * p;                     // stages past the end are out of range
+    uint32_t soff = toff;
+    if constexpr (!W_TILED) {
         const uint32_t row = (p >> 8) * 128 + ((p >> 1) & 3) * 32 + ((p >> 3) & 31);
         const uint32_t kk = k0 + 128 * (p & 1);
         // beyond k: set the top bit (out of every range) arithmetically rather than by a
         // select, which the compiler would otherwise turn into a branch around the load
         const uint32_t beyond = (uint32_t)((int32_t)(K - 1 - kk) >> 31);
-        const uint32_t soff = (row * srow + kk / 32) | (beyond & kOOB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_void*)(st + 2 * CODE_BYTES + (wave * 2 + t) * 256), 4, soff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_void*)(st + 2 * CODE_BYTES + SCALE_BYTES + (wave * 2 + t) * 256), 4, soff, 0, 0, 0);
+        soff = (row * srow + kk / 32) | (beyond & kOOB);
     }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_void*)(st + 2 * CODE_BYTES + wave * 256), 4, toff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_void*)(st + 2 * CODE_BYTES + SCALE_BYTES + wave * 256), 4, soff, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -84,36 +91,34 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 // s_waitcnt lgkmcnt(0) with the other counters left alone: this wave's LDS reads are done.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// Scale dwords of one operand for a lane: s[0] = {row i=0 k-dword 0, 1; i=1 dword 0, 1},
-// s[1] = the same for i = 2, 3.
-struct Scales { u32x4 s[2]; };
+// Scale dwords of a lane: A rows i*32 + r (i = 0..3) as a[0] = {i0 dword 0, i0 dword 1,
+// i1 dword 0, i1 dword 1}, a[1] the same for i = 2, 3; B rows jn*32 + r (jn = 0, 1) as b.
+struct Scales { u32x4 a[2]; u32x4 b; };
 
-__device__ __forceinline__ int scale_byte(const Scales& sc, int i, int j, uint32_t h)
+__device__ __forceinline__ int pick_byte(const u32x4 v, int odd, int j, uint32_t h)
 {
-    const u32x4 v = sc.s[i >> 1];
     const int d = j >> 1;                                    // k-steps 0, 1 -> dword 0; 2, 3 -> 1
-    const uint32_t w = (i & 1) ? (d ? v.w : v.z) : (d ? v.y : v.x);
+    const uint32_t w = odd ? (d ? v.w : v.z) : (d ? v.y : v.x);
     return (int)((w >> (8 * ((2 * j + h) & 3))) & 0xFFu);
 }
 
-// One k-step (64 k) of this wave's 4 x 4 block of 32 x 32 MFMA tiles.
+// One k-step (64 k) of this wave's 4 x 2 block of 32 x 32 MFMA tiles.
 // The weight fragment is the MFMA's A operand and the activation fragment its B operand, so
 // each tile is computed transposed (rows n, columns m): a lane then holds four consecutive n
-// of one output row per group, which the epilogue writes with one vector store.
+// of one output row per group, which the epilogue stages in LDS as one 8- or 16-byte write.
 template <int J>
-__device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const u32x4 (&fa)[4], const u32x4 (&fb)[4],
-                                          const Scales& sa, const Scales& sb, uint32_t h)
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NJ], const u32x4 (&fa)[MI], const u32x4 (&fb)[NJ],
+                                          const Scales& sc, uint32_t h)
 {
-    int asx[4], bsx[4];
+    int asx[MI], bsx[NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        asx[i] = scale_byte(sa, i, J, h);
-        bsx[i] = scale_byte(sb, i, J, h);
-    }
+    for (int i = 0; i < MI; ++i) asx[i] = pick_byte(sc.a[i >> 1], i & 1, J, h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int jn = 0; jn < NJ; ++jn) bsx[jn] = pick_byte(sc.b, jn, J, h);
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jn = 0; jn < NJ; ++jn) {
             // FP4 operands occupy the low four registers of the 8-register operand; the upper
             // four are not read, so they are left undefined rather than zeroed
             const i32x8 av = __builtin_shufflevector((i32x4)fa[i], (i32x4)fa[i], 0, 1, 2, 3, -1, -1, -1, -1);
@@ -122,42 +127,40 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[4][4], const u32x4 (&fa)
         }
 }
 
-// Fragment reads of k-step J from a stage buffer: rows i*32 further are 4096 bytes apart and
-// share the chunk permutation, so one base offset per operand serves all four.
+// Fragment reads of k-step J from a stage buffer: rows 32 further are 4096 bytes apart and
+// share the chunk permutation, so one base offset per operand serves all of them.
 template <int J>
 __device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t baseA, uint32_t baseB, uint32_t perm,
-                                           u32x4 (&fa)[4], u32x4 (&fb)[4])
+                                           u32x4 (&fa)[MI], u32x4 (&fb)[NJ])
 {
     const uint32_t chunk = 16 * ((2 * J) ^ perm);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const u32x4*>(st + baseA + chunk + i * 32 * ROWB);
-        fb[i] = *reinterpret_cast<const u32x4*>(st + CODE_BYTES + baseB + chunk + i * 32 * ROWB);
-    }
+    for (int i = 0; i < MI; ++i) fa[i] = *reinterpret_cast<const u32x4*>(st + baseA + chunk + i * 32 * ROWB);
+#pragma unroll
+    for (int jn = 0; jn < NJ; ++jn) fb[jn] = *reinterpret_cast<const u32x4*>(st + CODE_BYTES + baseB + chunk + jn * 32 * ROWB);
 }
 
-__device__ __forceinline__ void read_scales(const uint8_t* st, uint32_t offSA, uint32_t offSB, Scales& sa, Scales& sb)
+__device__ __forceinline__ void read_scales(const uint8_t* st, uint32_t offSA, uint32_t offSB, Scales& sc)
 {
-    sa.s[0] = *reinterpret_cast<const u32x4*>(st + offSA);
-    sa.s[1] = *reinterpret_cast<const u32x4*>(st + offSA + 16);
-    sb.s[0] = *reinterpret_cast<const u32x4*>(st + offSB);
-    sb.s[1] = *reinterpret_cast<const u32x4*>(st + offSB + 16);
+    sc.a[0] = *reinterpret_cast<const u32x4*>(st + offSA);
+    sc.a[1] = *reinterpret_cast<const u32x4*>(st + offSA + 16);
+    sc.b = *reinterpret_cast<const u32x4*>(st + offSB);
 }
 
 // scheduling: within a k-step, one MFMA, then the fragment reads for the next k-step, then
-// the remaining fifteen MFMAs, so that the reads' latency hides behind matrix work
-#define A4_SCHED_STEP(ID)                                  \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);    \
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, ID);    \
-    __builtin_amdgcn_sched_group_barrier(0x008, 15, ID)
+// the remaining MFMAs, so that the reads' latency hides behind matrix work
+#define A4_SCHED_STEP(ID)                                          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);            \
+    __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, ID);      \
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - 1, ID)
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_a4_kernel(const GemmArgs a)
+template <bool OUT_BF16, bool W_TILED>
+__global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // the wave index is uniform across the wave; saying so keeps LDS-DMA destinations scalar
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const uint32_t K = (uint32_t)a.k;
 
     // tile mapping: with the n-tile count a multiple of 8, XCD x (= block % 8) takes n-tiles
@@ -177,14 +180,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t nrows = (uint32_t)(a.n - n0 < BN ? a.n - n0 : BN);
     const rsrc_t ac = make_rsrc(a.xq_codes + m0 * (a.k / 2), mrows * (K / 2));
     const rsrc_t bc = make_rsrc(a.wc + n0 * (a.k / 2), nrows * (K / 2));
-    const rsrc_t as = make_rsrc(a.xq_scales + m0 * (a.k / 32), mrows * (K / 32));
-    const rsrc_t bs = make_rsrc(a.ws + n0 * (a.k / 32), nrows * (K / 32));
+    // activation scales are tiled; weight scales tiled or row-major
+    const uint32_t KS = (K + BK - 1) / BK;
+    const rsrc_t as = make_rsrc(a.xq_scales + (int64_t)mt * KS * 2048, KS * 2048);
+    const rsrc_t bs = W_TILED ? make_rsrc(a.ws + (int64_t)nt * KS * 2048, KS * 2048)
+                              : make_rsrc(a.ws + n0 * (a.k / 32), nrows * (K / 32));
 
-    f32x16 acc[4][4];
+    f32x16 acc[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -195,73 +201,70 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // after next.  Stages past the end of k load as zeros (their offsets are out of range),
     // so every iteration has the same shape.
     const int S = (int)((K + BK - 1) / BK);
-    issue_stage(lds, wave, lane, 0, ac, bc, as, bs, K);
-    issue_stage(lds + STAGE_BYTES, wave, lane, BK, ac, bc, as, bs, K);
+    issue_stage<W_TILED>(lds, wave, lane, 0, ac, bc, as, bs, K);
+    issue_stage<W_TILED>(lds + STAGE_BYTES, wave, lane, 1, ac, bc, as, bs, K);
 
     const uint32_t r32 = lane & 31, h = lane >> 5;
     const uint32_t perm = h ^ ((r32 >> 1) & 7u);              // chunk (2j + h) -> slot (2j) ^ perm
     const uint32_t baseA = (wm * 128 + r32) * ROWB;
-    const uint32_t baseB = (wn * 128 + r32) * ROWB;
+    const uint32_t baseB = (wn * 64 + r32) * ROWB;
     const uint32_t offSA = 2 * CODE_BYTES + (wm * 256 + r32 * 8) * 4;
-    const uint32_t offSB = 2 * CODE_BYTES + SCALE_BYTES + (wn * 256 + r32 * 8) * 4;
+    const uint32_t offSB = 2 * CODE_BYTES + SCALE_BYTES + ((wn >> 1) * 256 + r32 * 8 + 4 * (wn & 1)) * 4;
 
-    u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
-    Scales sa, sb;
+    u32x4 f0a[MI], f0b[NJ], f1a[MI], f1b[NJ];
+    Scales sc;
     wait_vmcnt<LOADS_PER_STAGE>();
     barrier_only();
     read_frags<0>(lds, baseA, baseB, perm, f0a, f0b);
-    read_scales(lds, offSA, offSB, sa, sb);
+    read_scales(lds, offSA, offSB, sc);
 
     uint32_t cur = 0;  // byte offset of stage s's buffer
     for (int s = 0; s < S; ++s) {
         const uint32_t nxt = cur ^ (uint32_t)STAGE_BYTES;
         read_frags<1>(lds + cur, baseA, baseB, perm, f1a, f1b);
-        mfma_step<0>(acc, f0a, f0b, sa, sb, h);
+        mfma_step<0>(acc, f0a, f0b, sc, h);
         A4_SCHED_STEP(0);
         __builtin_amdgcn_sched_barrier(0);
         read_frags<2>(lds + cur, baseA, baseB, perm, f0a, f0b);
-        mfma_step<1>(acc, f1a, f1b, sa, sb, h);
+        mfma_step<1>(acc, f1a, f1b, sc, h);
         A4_SCHED_STEP(1);
         __builtin_amdgcn_sched_barrier(0);
         read_frags<3>(lds + cur, baseA, baseB, perm, f1a, f1b);
-        mfma_step<2>(acc, f0a, f0b, sa, sb, h);
+        mfma_step<2>(acc, f0a, f0b, sc, h);
         A4_SCHED_STEP(2);
-        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm0();
         wait_vmcnt<0>();
         barrier_only();
         __builtin_amdgcn_sched_barrier(0);
-        issue_stage(lds + cur, wave, lane, (uint32_t)(s + STAGES) * BK, ac, bc, as, bs, K);
-        Scales sa_n, sb_n;
+        issue_stage<W_TILED>(lds + cur, wave, lane, (uint32_t)(s + STAGES), ac, bc, as, bs, K);
+        Scales sc_n;
         read_frags<0>(lds + nxt, baseA, baseB, perm, f0a, f0b);
-        read_scales(lds + nxt, offSA, offSB, sa_n, sb_n);
-        mfma_step<3>(acc, f1a, f1b, sa, sb, h);
-        // next stage's first fragments and scales first, then the twenty stage loads spread
+        read_scales(lds + nxt, offSA, offSB, sc_n);
+        mfma_step<3>(acc, f1a, f1b, sc, h);
+        // next stage's first fragments and scales first, then the ten stage loads spread
         // between MFMAs so that the matrix pipe stays busy while they are issued
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 3);
+        __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ + 3, 3);
 #pragma unroll
         for (int g = 0; g < 5; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-            __builtin_amdgcn_sched_group_barrier(0x020, 4, 3);
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 3);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 10, 3);
+        __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - 6, 3);
         // keep the next stage's reads in this iteration (not sunk into the next one)
         asm volatile("" ::: "memory");
-        sa = sa_n;
-        sb = sb_n;
+        sc = sc_n;
         cur = nxt;
     }
     wait_vmcnt<0>();
 
     // Epilogue.  Transposed 32x32 result layout: for tile (i, jn) a lane holds output row
     // m = i*32 + lane%32 and, for group q = e/4, columns n = jn*32 + 8q + 4*(lane/32) + e%4.
-    // Rows of a wave's 128 x 128 block are staged through LDS (each wave in a region of its
-    // own, rows padded against bank conflicts) and written back as whole 16-byte chunks, 256
-    // or 512 contiguous bytes per output row, so that every store fills whole cache lines.
-    // Stores go through a buffer descriptor; out-of-range chunks get an out-of-range offset
-    // and are dropped.
+    // Rows of a wave's 128 x 64 block are staged through LDS (each wave in a region of its
+    // own, rows padded against bank conflicts) and written back as whole 16-byte chunks, 128
+    // or 256 contiguous bytes per output row.  Stores go through a buffer descriptor;
+    // out-of-range chunks get an out-of-range offset and are dropped.
     constexpr uint32_t ESZ = OUT_BF16 ? 2 : 4;
     const rsrc_t yr = make_rsrc(static_cast<uint8_t*>(a.y) + (m0 * a.ldy + n0) * ESZ, 0x7FFFFFFFu);
     const uint32_t ldy = (uint32_t)a.ldy;
@@ -271,13 +274,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bool vec = (ldy % CE) == 0 && (nlim % CE) == 0;
     if (vec) {
         constexpr int PASSES = OUT_BF16 ? 1 : 2;             // 128 or 64 rows per pass
-        constexpr int IPP = 4 / PASSES;                       // 32-row blocks per pass
-        constexpr uint32_t RB = 128 * ESZ;                    // bytes of a wave row
+        constexpr int IPP = MI / PASSES;                      // 32-row blocks per pass
+        constexpr uint32_t RB = 32 * NJ * ESZ;                // bytes of a wave row (64 columns)
         constexpr uint32_t PITCH = RB + (OUT_BF16 ? 8 : 16);
-        constexpr uint32_t CPR = RB / 16;                     // chunks per row (16 or 32)
+        constexpr uint32_t CPR = RB / 16;                     // chunks per row (8 or 16)
         constexpr uint32_t RPI = 64 / CPR;                    // rows per store instruction
-        constexpr uint32_t PASS_ROWS = 128 / PASSES;
-        static_assert(4 * PASS_ROWS * PITCH <= (uint32_t)LDS_BYTES, "epilogue staging exceeds LDS");
+        constexpr uint32_t PASS_ROWS = 32 * IPP;
+        static_assert(WAVES * PASS_ROWS * PITCH <= (uint32_t)LDS_BYTES, "epilogue staging exceeds LDS");
         uint8_t* stg = lds + wave * PASS_ROWS * PITCH;
         barrier_only();  // every wave is done reading the stage buffers
 #pragma unroll
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int ii = 0; ii < IPP; ++ii)
 #pragma unroll
-                for (int jn = 0; jn < 4; ++jn)
+                for (int jn = 0; jn < NJ; ++jn)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const f32x16& c = acc[pass * IPP + ii][jn];
@@ -304,21 +307,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (uint32_t t = 0; t < PASS_ROWS / RPI; ++t) {
                 const uint32_t row = t * RPI + lane / CPR, chunk = lane % CPR;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * PITCH + chunk * 16);
-                const uint32_t mm = wm * 128 + pass * PASS_ROWS + row, nn = wn * 128 + chunk * CE;
+                const uint32_t mm = wm * 128 + pass * PASS_ROWS + row, nn = wn * 64 + chunk * CE;
                 const uint32_t off = (mm < mlim && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
                 bstore128(yr, off, v);
             }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MI; ++i) {
             const uint32_t mm = wm * 128 + i * 32 + r32;
             const bool mok = mm < mlim;
 #pragma unroll
-            for (int jn = 0; jn < 4; ++jn)
+            for (int jn = 0; jn < NJ; ++jn)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const uint32_t nn = wn * 128 + jn * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                    const uint32_t nn = wn * 64 + jn * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
                     const uint32_t off = (mok && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
                     const float v = acc[i][jn][e] * a.g;
                     if constexpr (OUT_BF16) bstore16(yr, off, __builtin_bit_cast(uint16_t, (__bf16)v));
@@ -330,21 +333,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 }  // namespace a4
 
+template <bool OUT_BF16, bool W_TILED>
+static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st)
+{
+    // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
+    // (thread-safe function-local static initialisation)
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)a4::gemm_a4_kernel<OUT_BF16, W_TILED>, hipFuncAttributeMaxDynamicSharedMemorySize, a4::LDS_BYTES);
+    if (attr != hipSuccess) return attr;
+    const unsigned tiles = (unsigned)(((a.m + a4::BM - 1) / a4::BM) * ((a.n + a4::BN - 1) / a4::BN));
+    hipLaunchKernelGGL((a4::gemm_a4_kernel<OUT_BF16, W_TILED>), dim3(tiles), dim3(a4::THREADS), a4::LDS_BYTES, st, a);
+    return hipGetLastError();
+}
+
+bool a4_uses_mfma(const GemmArgs& a)
+{
+    // k in whole 128-element halves of a stage, 32-bit offsets within an output tile
+    const int64_t tile_span = ((int64_t)(a4::BM - 1) * a.ldy + a4::BN) * (a.y_bf16 ? 2 : 4);
+    return a.k % 128 == 0 && tile_span < 0x7FFFFFFF;
+}
+
 hipError_t launch_gemm_a4_mfma(const GemmArgs& a, hipStream_t st)
 {
-    // the LDS ring exceeds the default 64 KB dynamic limit; raise it once (thread-safe
-    // function-local static initialisation)
-    static const hipError_t attr_bf16 = hipFuncSetAttribute(
-        (const void*)a4::gemm_a4_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, a4::LDS_BYTES);
-    static const hipError_t attr_f32 = hipFuncSetAttribute(
-        (const void*)a4::gemm_a4_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, a4::LDS_BYTES);
-    if (attr_bf16 != hipSuccess || attr_f32 != hipSuccess) return attr_bf16 != hipSuccess ? attr_bf16 : attr_f32;
-    // output offsets within a tile are 32-bit: (BM - 1) * ldy + BN elements must fit
-    if (((int64_t)(a4::BM - 1) * a.ldy + a4::BN) * (a.y_bf16 ? 2 : 4) >= (int64_t)0x7FFFFFFF) return hipErrorInvalidValue;
-    const unsigned tiles = (unsigned)(((a.m + a4::BM - 1) / a4::BM) * ((a.n + a4::BN - 1) / a4::BN));
-    if (a.y_bf16) hipLaunchKernelGGL(a4::gemm_a4_kernel<true>, dim3(tiles), dim3(256), a4::LDS_BYTES, st, a);
-    else hipLaunchKernelGGL(a4::gemm_a4_kernel<false>, dim3(tiles), dim3(256), a4::LDS_BYTES, st, a);
-    return hipGetLastError();
+    if (!a4_uses_mfma(a)) return hipErrorInvalidValue;
+    if (a.y_bf16) return a.ws_tiled ? launch_tiled<true, true>(a, st) : launch_tiled<true, false>(a, st);
+    return a.ws_tiled ? launch_tiled<false, true>(a, st) : launch_tiled<false, false>(a, st);
 }
 
 }  // namespace mxk

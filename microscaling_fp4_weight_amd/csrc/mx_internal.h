@@ -40,6 +40,7 @@ struct QuantArgs {
     uint8_t* codes;
     uint8_t* scales;
     bool fast;        // k % 32 == 0 and 16-byte aligned rows
+    uint32_t ts_ks;   // 0: row-major scales; else tiled scales with this many 256-k stages
 };
 
 struct DequantArgs {
@@ -53,6 +54,7 @@ struct DequantArgs {
     bool bf16;        // output element type
     int64_t ldy;
     bool fast;
+    uint32_t ts_ks;   // 0: row-major scales; else tiled scales with this many 256-k stages
 };
 
 struct GemmArgs {
@@ -66,10 +68,25 @@ struct GemmArgs {
     void* y;
     bool y_bf16;
     int64_t ldy;
-    // W4A4: quantized activations (m x k/2 codes, m x k/32 scales) in the workspace
+    bool ws_tiled;            // weight scales in the tiled layout (else row-major)
+    // W4A4: quantized activations in the workspace (m x k/2 codes; scales tiled for the
+    // matrix-core kernel, row-major for the direct one)
     uint8_t* xq_codes;
     uint8_t* xq_scales;
 };
+
+// Tiled scale layout (block 32): rows in tiles of 256, k in stages of 256 (8 blocks); the
+// 2048 bytes of a (row tile, stage) pair are contiguous, tile-major then stage, and inside
+// them the byte of row r (0..255 in the tile), block b (0..7 in the stage) sits at
+// 1024 (r / 128) + 32 (r % 32) + 8 ((r / 32) % 4) + b.
+constexpr int64_t kTileRows = 256, kTileK = 256, kTileBytes = 2048;
+inline int64_t tiled_stages(int64_t k) { return (k + kTileK - 1) / kTileK; }
+inline int64_t tiled_scale_bytes(int64_t rows, int64_t k)
+{
+    return (rows + kTileRows - 1) / kTileRows * tiled_stages(k) * kTileBytes;
+}
+// whether the W4A4 product runs on the matrix-core kernel (else the direct one)
+bool a4_uses_mfma(const GemmArgs& a);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);

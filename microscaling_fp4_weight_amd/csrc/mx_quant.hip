@@ -29,7 +29,7 @@ template <int BLOCK, int FMT, bool BF16, bool G1>
 __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, FastDiv groups_per_row, uint32_t gpr,
     uint32_t total_groups, double g, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t k)
+    uint8_t* __restrict__ scales, int64_t k, uint32_t ts_ks)
 {
     constexpr int NW = BF16 ? 16 : 32;                    // 32-bit words holding 32 elements
     constexpr int NB = BLOCK <= 32 ? 32 / BLOCK : 1;      // blocks (or block parts) per lane
@@ -93,7 +93,13 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
 #pragma unroll
     for (int b = 0; b < NB; ++b) sbyte[b] = G1 ? scale_code_g1<FMT>(amax[b]) : scale_code_g<FMT>(amax[b], six_g);
 
-    if (active) {
+    if (BLOCK == 32 && ts_ks != 0) {  // tiled scale layout (block 32 only)
+        if (active) {
+            scales[tiled_scale_off(row, gc, ts_ks)] = (uint8_t)sbyte[0];
+            // the blocks that pad the row's last stage read as scale byte 0
+            for (uint32_t kb = gpr + gc; kb < 8 * ts_ks; kb += gpr) scales[tiled_scale_off(row, kb, ts_ks)] = 0;
+        }
+    } else if (active) {
         uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
         if constexpr (NB == 1) {
             if (LANES == 1 || (gc % LANES) == 0) sp[gc / LANES] = (uint8_t)sbyte[0];
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
 template <int FMT, bool BF16, bool G1>
 __global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
     const uint8_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t k, int block, double g,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t ts_ks)
 {
     const int64_t nb = k / block;
     const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -214,7 +220,12 @@ __global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
         amax = a > amax ? a : amax;
     }
     const uint32_t sb = G1 ? scale_code_g1<FMT>(amax) : scale_code_g<FMT>(amax, 6.0 * g);
-    scales[r * nb + b] = (uint8_t)sb;
+    if (ts_ks != 0) {  // tiled scale layout (block 32 only)
+        scales[tiled_scale_off((uint32_t)r, (uint32_t)b, ts_ks)] = (uint8_t)sb;
+        for (int64_t kb = nb + b; kb < 8 * (int64_t)ts_ks; kb += nb) scales[tiled_scale_off((uint32_t)r, (uint32_t)kb, ts_ks)] = 0;
+    } else {
+        scales[r * nb + b] = (uint8_t)sb;
+    }
     uint8_t* cp = codes + r * (k / 2) + b * (block / 2);
     if constexpr (G1) {
         const EncG1 p = enc_params_g1<FMT>(sb);
@@ -256,7 +267,7 @@ template <int BLOCK, int FMT, bool G1, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     FastDiv units_per_row, uint32_t upr, uint32_t total_units, int64_t k, double g,
-    uint8_t* __restrict__ y, int64_t ldy_bytes)
+    uint8_t* __restrict__ y, int64_t ldy_bytes, uint32_t ts_ks)
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wbase = (blockIdx.x * kThreads + (threadIdx.x & ~63u)) * kDeqUnits;
@@ -278,6 +289,8 @@ __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
                 const uint32_t v = *reinterpret_cast<const uint16_t*>(sp + c8[h] * 2);
                 sb[h][0] = v & 0xFF;
                 sb[h][1] = v >> 8;
+            } else if (BLOCK == 32 && ts_ks != 0) {  // tiled scale layout
+                sb[h][0] = sb[h][1] = scales[tiled_scale_off(row[h], c8[h] / 4, ts_ks)];
             } else {
                 sb[h][0] = sb[h][1] = sp[(c8[h] * 8) / BLOCK];
             }
@@ -339,14 +352,15 @@ __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
 template <int FMT, bool G1, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_generic_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
-    int64_t k, int block, double g, uint8_t* __restrict__ y, int64_t ldy)
+    int64_t k, int block, double g, uint8_t* __restrict__ y, int64_t ldy, uint32_t ts_ks)
 {
     const int64_t pairs = k / 2;
     const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (id >= rows * pairs) return;
     const int64_t r = id / pairs, j = id - r * pairs;
     const uint32_t cb = codes[r * pairs + j];
-    const uint32_t sb = scales[r * (k / block) + (2 * j) / block];
+    const uint32_t sb = ts_ks != 0 ? scales[tiled_scale_off((uint32_t)r, (uint32_t)(j / 16), ts_ks)]
+                                   : scales[r * (k / block) + (2 * j) / block];
     float pow2 = 1.0f, mant = 1.0f;
     double sg = 0.0;
     if constexpr (G1) {
@@ -382,7 +396,7 @@ static hipError_t launch_quantize_fmt(const QuantArgs& a, hipStream_t st)
         const int64_t ldb = a.ldx * (BF16 ? 2 : 4);
         switch (a.block) {
 #define MXQ(B) case B: hipLaunchKernelGGL((quantize_fast_kernel<B, FMT, BF16, G1>), grid, dim3(kThreads), 0, st, \
-                   (const uint8_t*)a.x, ldb, FastDiv::make(gpr), gpr, total, a.g, a.codes, a.scales, a.k); break;
+                   (const uint8_t*)a.x, ldb, FastDiv::make(gpr), gpr, total, a.g, a.codes, a.scales, a.k, a.ts_ks); break;
             MXQ(4) MXQ(8) MXQ(16) MXQ(32) MXQ(64) MXQ(128) MXQ(256)
 #undef MXQ
             default: return hipErrorInvalidValue;
@@ -391,7 +405,7 @@ static hipError_t launch_quantize_fmt(const QuantArgs& a, hipStream_t st)
         const int64_t n = a.rows * (a.k / a.block);
         const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
         hipLaunchKernelGGL((quantize_generic_kernel<FMT, BF16, G1>), grid, dim3(kThreads), 0, st,
-                           (const uint8_t*)a.x, a.ldx, a.rows, a.k, a.block, a.g, a.codes, a.scales);
+                           (const uint8_t*)a.x, a.ldx, a.rows, a.k, a.block, a.g, a.codes, a.scales, a.ts_ks);
     }
     return hipGetLastError();
 }
@@ -420,7 +434,7 @@ static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
         const int64_t ldb = a.ldy * (OUT_BF16 ? 2 : 4);
         switch (a.block) {
 #define MXD(B) case B: hipLaunchKernelGGL((dequantize_fast_kernel<B, FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st, \
-                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb); break;
+                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb, a.ts_ks); break;
             MXD(4) MXD(8) MXD(16) MXD(32) MXD(64) MXD(128) MXD(256)
 #undef MXD
             default: return hipErrorInvalidValue;
@@ -429,7 +443,7 @@ static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
         const int64_t n = a.rows * (a.k / 2);
         const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
         hipLaunchKernelGGL((dequantize_generic_kernel<FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st,
-                           a.codes, a.scales, a.rows, a.k, a.block, a.g, (uint8_t*)a.y, a.ldy);
+                           a.codes, a.scales, a.rows, a.k, a.block, a.g, (uint8_t*)a.y, a.ldy, a.ts_ks);
     }
     return hipGetLastError();
 }

@@ -111,3 +111,26 @@ def assert_gemm_close(y_gpu: np.ndarray, y_ref: np.ndarray, a_ref: np.ndarray, b
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance; worst "
                              f"idx {np.unravel_index(i, y.shape)} got {y.flat[i]!r} ref "
                              f"{y_ref.flat[i]!r} tol {tol.flat[i]!r}")
+
+
+# Tiled scale layout (include/mx.h, MX_LAYOUT_TILED), written out from its definition.
+def tiled_positions(rows: int, k: int) -> np.ndarray:
+    """Byte position of the scale of (r, b) for every row r and 32-element block b."""
+    ks = -(-k // 256)
+    r = np.arange(rows)[:, None]
+    b = np.arange(k // 32)[None, :]
+    t = r % 256
+    return (2048 * ((r // 256) * ks + b // 8) + 1024 * (t // 128) + 32 * (t % 32)
+            + 8 * ((t // 32) % 4) + b % 8)
+
+
+def padding_positions(rows: int, k: int) -> np.ndarray:
+    ks = -(-k // 256)
+    nb = k // 32
+    pads = []
+    for b in range(nb, 8 * ks):
+        r = np.arange(rows)
+        t = r % 256
+        pads.append(2048 * ((r // 256) * ks + b // 8) + 1024 * (t // 128) + 32 * (t % 32)
+                    + 8 * ((t // 32) % 4) + b % 8)
+    return np.concatenate(pads) if pads else np.zeros(0, dtype=np.int64)

@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_match_header(L):
     names = declared_functions()
     assert names == ["mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_quantize",
-                     "mx_status_string"]
+                     "mx_scale_bytes", "mx_status_string"]
     for n in names:
         assert hasattr(L, n)
     so = os.path.join(ROOT, "microscaling_fp4_weight_amd", "libmx.so")
@@ -59,7 +59,9 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on thes
     ((FAKE, BF16, 4, 64, 32, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # ld < k
     ((FAKE, 7, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),        # dtype
     ((FAKE, BF16, 4, 64, 64, 32, 3, 1.0, 0, FAKE, FAKE), INVALID),        # fmt
-    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 1, FAKE, FAKE), INVALID),     # layout
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 2, FAKE, FAKE), INVALID),     # layout
+    ((FAKE, BF16, 4, 64, 64, 16, E8M0, 1.0, 1, FAKE, FAKE), UNSUPPORTED), # tiled needs block 32
+    ((FAKE, BF16, 4, 1 << 23, 1 << 23, 32, E8M0, 1.0, 1, FAKE, FAKE), UNSUPPORTED),  # tiled k bound
     ((FAKE, BF16, 4, 64, 64, 32, E8M0, 0.0, 0, FAKE, FAKE), INVALID),     # g = 0
     ((FAKE, BF16, 4, 64, 64, 32, E8M0, -1.0, 0, FAKE, FAKE), INVALID),    # g < 0
     ((FAKE, BF16, 4, 64, 64, 32, E8M0, float("inf"), 0, FAKE, FAKE), INVALID),
@@ -87,18 +89,39 @@ def test_dequantize_validation(L):
     assert L.mx_dequantize(None, None, 0, 64, 32, E8M0, 1.0, 0, None, F32, 64, None) == OK
 
 
+def test_scale_bytes(L):
+    sb = L.mx_scale_bytes
+    assert sb(4, 64, 32, 0) == 8
+    assert sb(5, 96, 4, 0) == 5 * 24
+    # tiled: ceil(rows / 256) * ceil(k / 256) * 2048
+    assert sb(4, 64, 32, 1) == 2048
+    assert sb(300, 8192, 32, 1) == 2 * 32 * 2048
+    assert sb(256, 4224, 32, 1) == 1 * 17 * 2048
+    assert sb(0, 64, 32, 1) == 0
+    assert sb(4, 64, 16, 1) == 0          # tiled is defined for block 32 only
+    assert sb(4, 48, 32, 0) == 0          # k % block
+    assert sb(4, 64, 32, 2) == 0          # unknown layout
+
+
 def test_gemm_validation_and_workspace(L):
     ws = L.mx_gemm_workspace_size
     assert ws(2048, 28672, 8192, 32, A16) == 0
     assert ws(2048, 28672, 8192, 32, A4) == 2048 * 4096 + 2048 * 256
-    assert ws(3, 5, 64, 32, A4) == 256 + 256  # each part rounded up to 256 bytes
+    assert ws(3, 5, 64, 32, A4) == 256 + 2048  # codes rounded to 256 bytes; one tiled scale block
+    assert ws(300, 5, 4224, 32, A4) == 300 * 2112 + 2 * 17 * 2048
     assert ws(3, 5, 64, 16, A4) == 0          # W4A4 needs block 32
     assert ws(3, 5, 63, 32, A4) == 0
 
     def gemm(m=4, n=8, k=64, ldx=64, block=32, fmt=E8M0, g=1.0, mode=A16, yt=F32, ldy=8,
-             work=None, wbytes=0, x=FAKE, wc=FAKE, wsc=FAKE, y=FAKE):
-        return L.mx_gemm(x, m, n, k, ldx, wc, wsc, block, fmt, g, 0, mode, y, yt, ldy, work,
+             work=None, wbytes=0, x=FAKE, wc=FAKE, wsc=FAKE, y=FAKE, layout=0):
+        return L.mx_gemm(x, m, n, k, ldx, wc, wsc, block, fmt, g, layout, mode, y, yt, ldy, work,
                          wbytes, None)
+
+    # tiled weight scales: W4A4 matrix-core path only (k % 128 == 0)
+    assert gemm(layout=1) == UNSUPPORTED                                    # W4A16
+    assert gemm(layout=1, mode=A4, work=FAKE, wbytes=1 << 20) == UNSUPPORTED  # k = 64
+    assert gemm(layout=1, mode=A4, block=16, k=128, ldx=128) == UNSUPPORTED
+    assert gemm(layout=2) == INVALID
 
     assert gemm(mode=A4, fmt=E4M3) == UNSUPPORTED      # W4A4 is E8M0-only
     assert gemm(mode=A4, block=64) == UNSUPPORTED      # and block 32 only

@@ -14,7 +14,7 @@ import torch
 import microscaling_fp4_weight_amd as mx
 import oracle
 import synth
-from gpu_util import DEV, assert_gemm_close, bf16_dev, f32_dev, to_host_bits
+from gpu_util import DEV, assert_gemm_close, bf16_dev, f32_dev, padding_positions, tiled_positions, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -127,11 +127,14 @@ def test_gemm_a4(mnk):
         check(x, c, s, cd, sd, 32, "e8m0", 1.0, "a4", out)
 
 
-def test_gemm_a4_prepass_matches_quantize():
+@pytest.mark.parametrize("k", [512, 4224, 160])
+def test_gemm_a4_prepass_matches_quantize(k):
     """The activations quantized inside mx_gemm (workspace) are byte-identical to
-    mx_quantize(X, 32, E8M0) and to the oracle."""
-    m, n, k = 37, 64, 512
-    x = synth.normal((m, k), "bf16", "gw.x", 1.0, 0.01, 20.0)
+    mx_quantize(X, 32, E8M0) and to the oracle.  With k % 128 == 0 the matrix-core kernel
+    runs and the workspace holds the scales in the tiled layout (mx_quantize with
+    layout "tiled"); otherwise row-major."""
+    m, n = 37, 64
+    x = synth.normal((m, k), "bf16", f"gw.x.{k}", 1.0, 0.01, 20.0)
     w = synth.normal((n, k), "bf16", "gw.w", 0.02)
     c, s, cd, sd = quantize_ref(w, 32, "e8m0")
     xd = bf16_dev(x)
@@ -142,13 +145,16 @@ def test_gemm_a4_prepass_matches_quantize():
     wsh = to_host_bits(ws)
     codes = wsh[: m * k // 2].reshape(m, k // 2)
     off = (m * k // 2 + 255) // 256 * 256
-    scales = wsh[off: off + m * k // 32].reshape(m, k // 32)
     rc, rs = oracle.quantize(x, 32, "e8m0")
     np.testing.assert_array_equal(codes, rc)
-    np.testing.assert_array_equal(scales, rs)
-    qc, qs = mx.mx_quantize(xd, 32, "e8m0")
+    qc, _ = mx.mx_quantize(xd, 32, "e8m0")
     np.testing.assert_array_equal(to_host_bits(qc), codes)
-    np.testing.assert_array_equal(to_host_bits(qs), scales)
+    wsc = wsh[off:]
+    if k % 128 == 0:
+        np.testing.assert_array_equal(wsc[tiled_positions(m, k)], rs)
+        assert np.all(wsc[padding_positions(m, k)] == 0)
+    else:
+        np.testing.assert_array_equal(wsc[: m * k // 32].reshape(m, k // 32), rs)
 
 
 # ------------------------------------------------------------------------ full-size workloads
