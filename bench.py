@@ -2,6 +2,7 @@
 """Benchmark of the MX FP4 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+    python bench.py --pmc-run      # launches for rocprofv3 --pmc traffic counters (see below)
 
 One step = the whole block-size/scale sweep on the Llama-7B FFN-shaped weight
 (4096 x 11008 bf16 ~ N(0, sigma^2), 0.1% entries x20): for every sigma in {0.005, 0.02, 0.1},
@@ -18,6 +19,11 @@ M=256, 4096).  `roofline` is for the dominant kernel, the B=32 E8M0 quantize; `c
 times the single-threaded CPU oracle on a bounded sample of the same sweep.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
+
+`--pmc-run` only launches the dominant kernel (five times) and a plain device copy of known
+size (five times, the calibration for the HBM byte counters), for
+`rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`; the resulting per-launch bytes are kept in
+profiles/traffic.json and reported as `roofline.traffic` while the kernel source is unchanged.
 """
 from __future__ import annotations
 
@@ -62,6 +68,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the GEMV/GEMM rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="only the launches that the traffic counters are read on")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
@@ -80,6 +88,9 @@ def main():
     L = mx.lib()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    if args.pmc_run:
+        pmc_run(mx, torch, np, synth, dev)
+        return
 
     # ---------------------------------------------------------------- C2 sweep setup
     t0 = time.time()
@@ -105,15 +116,18 @@ def main():
         dcalls.append((codes[i].data_ptr(), scales[i].data_ptr(), C2_ROWS, C2_K, b, mx.FMT[f], 1.0,
                        0, deq_out[i % 6].data_ptr(), 1, C2_K, sp))
         step_bytes += 2 * quant_bytes(n, b)
-    dom = next(i for i, c in enumerate(configs) if c[1] == 32 and c[2] == "e8m0")
+    # the dominant kernel's three launches (one per sigma) are consecutive in the step; one
+    # event pair around them gives its average launch duration inside the timed region
+    dom = [i for i, c in enumerate(configs) if c[1] == 32 and c[2] == "e8m0"]
+    assert dom == list(range(dom[0], dom[0] + len(SIGMAS)))
     q, dq = L.mx_quantize, L.mx_dequantize
 
     def step(ev=None):
         for i, c in enumerate(qcalls):
-            if ev is not None and i == dom:
+            if ev is not None and i == dom[0]:
                 ev[0].record(stream)
             st = q(*c)
-            if ev is not None and i == dom:
+            if ev is not None and i == dom[-1]:
                 ev[1].record(stream)
             if st:
                 raise mx.MXError(st, "mx_quantize")
@@ -139,7 +153,7 @@ def main():
     gpu_ms = start.elapsed_time(end)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dom_ms = sorted(a.elapsed_time(b) for a, b in dom_events)
+    dom_ms = sorted(a.elapsed_time(b) / len(dom) for a, b in dom_events)
     dom_avg_ms = sum(dom_ms) / len(dom_ms)
     dom_bytes = quant_bytes(n, 32)
     log(f"C2 sweep: {ms_per_step:.3f} ms/step, {value:.0f} GB/s; dominant kernel avg {dom_avg_ms * 1e3:.2f} us")
@@ -205,6 +219,30 @@ def main():
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
+
+
+COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written per launch
+
+
+def pmc_run(mx, torch, np, synth, dev):
+    """Five launches of the dominant kernel (block-32 E8M0 quantize of the sigma = 0.02
+    weight) and five plain copies of COPY_BYTES, for the HBM byte counters."""
+    w = synth.c2_weight(0.02)
+    x = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)
+    codes = torch.empty((C2_ROWS, C2_K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((C2_ROWS, C2_K // 32), dtype=torch.uint8, device=dev)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for _ in range(5):
+        flush.fill_(1)  # evict the previous launch's data from the Infinity Cache
+        mx.mx_quantize(x, 32, "e8m0", codes=codes, scales=scales)
+    for _ in range(5):
+        flush.fill_(1)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"pmc run: 5 x quantize ({quant_bytes(C2_ROWS * C2_K, 32)} algorithmic bytes), "
+        f"5 x copy ({COPY_BYTES} bytes read, {COPY_BYTES} written)")
 
 
 def load_traffic(kernel: str):
@@ -275,23 +313,27 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     # 70B-FFN prefill: W4A16 and W4A4
     w = dev_bf16(synth.c4_weight())
     c4, s4 = mx.mx_quantize(w, 32, "e8m0")
+    _, s4t = mx.mx_quantize(w, 32, "e8m0", layout="tiled")  # same codes, tiled scale order
     del w
     x = dev_bf16(synth.c4_x())
     M, N, K = 2048, 28672, 8192
     flops = 2 * M * N * K
     y = torch.empty((M, N), dtype=bf, device=dev)
     ws = torch.empty(mx.mx_gemm_workspace_size(M, N, K, 32, "a4"), dtype=torch.uint8, device=dev)
-    for mode, peak in (("a16", PEAK_BF16), ("a4", PEAK_FP4)):
-        fn = lambda: mx.mx_gemm(x, c4, s4, 32, "e8m0", 1.0, mode, y=y, workspace=ws)
+    for mode, layout, peak in (("a16", "rowmajor", PEAK_BF16), ("a4", "rowmajor", PEAK_FP4),
+                               ("a4", "tiled", PEAK_FP4)):
+        sc = s4t if layout == "tiled" else s4
+        fn = lambda: mx.mx_gemm(x, c4, sc, 32, "e8m0", 1.0, mode, y=y, workspace=ws, layout=layout)
         time_launches(torch, stream, [fn], reps=2)
         ts = time_launches(torch, stream, [fn], reps=5)
         t = sorted(ts)[len(ts) // 2]
         tf = flops / (t * 1e-3) / 1e12
-        rows[f"gemm_{mode}.m{M}.n{N}.k{K}"] = {"TFLOP/s": round(tf, 1),
-                                                "frac_peak": round(tf * 1e12 / peak, 4),
-                                                "peak_TFLOP/s": peak / 1e12, "ms": round(t, 3)}
-        log(f"C4 {mode}: {t:.3f} ms, {tf:.0f} TFLOP/s")
-    del c4, s4, x, y, ws
+        key = f"gemm_{mode}.m{M}.n{N}.k{K}" + (".tiled_scales" if layout == "tiled" else "")
+        rows[key] = {"TFLOP/s": round(tf, 1), "frac_peak": round(tf * 1e12 / peak, 4),
+                     "peak_TFLOP/s": peak / 1e12, "ms": round(t, 3),
+                     "includes": "activation pre-pass" if mode == "a4" else "-"}
+        log(f"C4 {mode} {layout}: {t:.3f} ms, {tf:.0f} TFLOP/s")
+    del c4, s4, s4t, x, y, ws
     torch.cuda.empty_cache()
 
     # 405B-FFN: offline two-level quantize, GEMV M=1, GEMM M=256 / 4096
@@ -339,7 +381,7 @@ def cpu_baseline(np, synth):
     sweep: the first 192 of 4096 rows of each sigma's weight, every block size and format,
     quantize + dequantize."""
     import oracle
-    sample_rows = 192
+    sample_rows = 448
     t0 = time.perf_counter()
     byt = 0
     for sigma in SIGMAS:
