@@ -287,7 +287,10 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     def dev_bf16(a):
         return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
 
-    # decode GEMV: distinct weight copies (>= 512 MB) launched back to back
+    # decode GEMV: distinct weight copies (>= 512 MB) launched back to back, as a decode step
+    # across layers would.  The launches are captured once in a HIP graph and replayed, so that
+    # the GPU sees them back to back (from Python, each call's host overhead exceeds a small
+    # GEMV's duration).
     for nn, copies in ((4096, 64), (14336, 20)):
         w = dev_bf16(synth.c3_weight(nn))
         c0, s0 = mx.mx_quantize(w, 32, "e8m0")
@@ -296,17 +299,40 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
         for m in (1, 4, 16):
             x = dev_bf16(synth.c3_x(m))
             y = torch.empty((m, nn), dtype=bf, device=dev)
-            launches = [lambda c=c, s=s: mx.mx_gemm(x, c, s, 32, "e8m0", 1.0, "a16", y=y)
-                        for c, s in cs]
-            time_launches(torch, stream, launches)  # warm-up
-            ts = time_launches(torch, stream, launches, reps=3)
-            tot = sum(ts) / 3
+
+            def decode_step():
+                sp = torch.cuda.current_stream().cuda_stream
+                for c, s in cs:
+                    st = L.mx_gemm(x.data_ptr(), m, nn, 4096, 4096, c.data_ptr(), s.data_ptr(), 32,
+                                   mx.FMT["e8m0"], 1.0, 0, 0, y.data_ptr(), 1, nn, None, 0, sp)
+                    if st:
+                        raise mx.MXError(st, "mx_gemm")
+
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                decode_step()  # eager warm-up
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                decode_step()
+            graph.replay()
+            torch.cuda.synchronize()
+            reps = 5
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot = e0.elapsed_time(e1) / reps  # ms per decode step (copies launches)
             byt = gemv_bytes(m, nn, 4096, 32)
             gbs = byt * copies / (tot * 1e-3) / 1e9
             rows[f"gemv_a16.m{m}.n{nn}.k4096"] = {
                 "GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
-                "median_launch_us": round(sorted(ts)[len(ts) // 2] * 1e3, 2),
-                "TFLOP/s": round(2 * m * nn * 4096 * copies / (tot * 1e-3) / 1e12, 2)}
+                "us_per_launch": round(tot * 1e3 / copies, 2),
+                "TFLOP/s": round(2 * m * nn * 4096 * copies / (tot * 1e-3) / 1e12, 2),
+                "launches": f"{copies} distinct weights back to back (graph replay)"}
+            del graph
         del cs, c0, s0
         log(f"decode GEMV n={nn} done")
 

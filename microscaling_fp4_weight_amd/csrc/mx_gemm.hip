@@ -185,22 +185,6 @@ __global__ __launch_bounds__(256) void gemm_a16_kernel(const GemmArgs a)
         }
 }
 
-// ---------------------------------------------------------------------------------------
-// W4A16 GEMV (m <= 16): one MFMA row-tile.  A workgroup owns 16 output columns; its
-// GEMV_WAVES waves take contiguous k ranges.  Each wave keeps GEMV_DEPTH k-tiles of weight
-// and activation loads in flight (a rolling prefetch: tile t + GEMV_DEPTH is requested as
-// soon as tile t has been consumed); the waves' partial sums are added through LDS.
-// ---------------------------------------------------------------------------------------
-constexpr int GEMV_WAVES = 4;
-constexpr int GEMV_DEPTH = 4;
-
-template <int BLOCK>
-struct GemvTile {
-    u32x4 cw;         // 32 weight codes of row n
-    uint64_t sb;      // their scale byte(s)
-    u32x4 xv[4];      // 32 activations of row lr (zero for rows >= m)
-};
-
 // Scales covering one lane's 32 k through a buffer resource (zero when out of range).
 template <int BLOCK>
 __device__ __forceinline__ uint64_t bload_lane_scales(rsrc_t r, uint32_t off)
@@ -211,80 +195,172 @@ __device__ __forceinline__ uint64_t bload_lane_scales(rsrc_t r, uint32_t off)
     else return bload64(r, off);
 }
 
-struct GemvRows {
-    rsrc_t w, s, x;          // this workgroup's 16 weight rows, their scales, the activations
-    uint32_t woff, soff, xoff;  // this lane's row offsets (bytes)
-    uint32_t K;
-};
+// ---------------------------------------------------------------------------------------
+// W4A16 GEMV for 2 <= m <= 16 with the activations in LDS.  The activations (m rows of X)
+// are what every workgroup needs in full while it needs only its own weight rows, so they are
+// brought into LDS once per workgroup and 4096-element chunk (LDS-DMA, 1 KB per load) instead
+// of being re-read per 16-row weight tile through the load unit.  A workgroup owns up to 16
+// weight tiles of 16 rows (tile t of workgroup b is b + t * grid); its 8 waves split each
+// chunk's k four ways.  For a tile, a lane holds weight row lane%16 and the 32 consecutive k
+// 32*(lane/16) .. +31 of every 128-k step (one 16-byte code load), dequantizes them in
+// registers, and feeds 16x16x32 bf16 MFMAs with the matching activations from LDS: k is
+// permuted the same way for both operands, which leaves the dot product unchanged.  The next
+// tile's weight loads are in flight while a tile is computed.  Partial sums of the 8 waves
+// meet in LDS at the end.
+// ---------------------------------------------------------------------------------------
+constexpr int GL_WAVES = 8;                       // two per SIMD
+constexpr int GL_KC = 4096;                       // k per LDS chunk of X
+constexpr int GL_PITCH = 2 * GL_KC + 16;          // LDS bytes per X row (padded: rows start 4 banks apart)
+constexpr int GL_TMAX = 16;                       // 16-row weight tiles per workgroup
+constexpr int GL_KTW = GL_KC / TK / GL_WAVES;     // 128-k steps per wave per chunk
+constexpr int GL_RED = GL_WAVES * GL_TMAX * 64 * 16;  // bytes of the cross-wave reduction
 
 template <int BLOCK>
-__device__ __forceinline__ void gemv_load(GemvTile<BLOCK>& t, int64_t tile, int64_t t1, int kq,
-                                          const GemvRows& r)
+struct GlW {
+    u32x4 cw[GL_KTW];      // 32 codes of the lane's row per 128-k step
+    uint64_t sb[GL_KTW];   // their scale byte(s) (blocks below 32)
+    u32x4 srow;            // blocks of 32 and more: the row's scale bytes of the wave's k range
+};
+
+// Scale byte(s) of the lane's 32 k in 128-k step kt (kq = lane / 16).  For blocks of 32 and
+// more, the 512 k of a wave's range have at most 16 scale bytes per row, which one load per
+// lane brings at once (the four lanes of a row read the same bytes) instead of one scattered
+// byte per step; k past the end gets a neutral byte (its codes are zero).
+template <int BLOCK>
+__device__ __forceinline__ uint64_t gl_scale(const GlW<BLOCK>& w, int kt, int kq, bool ok)
 {
-    const uint32_t kk = (uint32_t)tile * TK + 32 * kq;
-    const bool ok = tile < t1 && kk < r.K;
-    t.cw = bload128(r.w, ok ? r.woff + kk / 2 : kOOB);
-    t.sb = bload_lane_scales<BLOCK>(r.s, ok ? r.soff + kk / BLOCK : kOOB);
+    if constexpr (BLOCK >= 32) {
+        const int dw = (kt * TK / BLOCK) / 4;                     // dword holding the byte (constant once kt is)
+        const uint32_t idx = (uint32_t)(kt * TK + 32 * kq) / BLOCK;
+        const uint32_t v = dw == 0 ? w.srow.x : dw == 1 ? w.srow.y : dw == 2 ? w.srow.z : w.srow.w;
+        return ok ? (v >> (8 * (idx & 3))) & 0xFFu : 127u;
+    } else {
+        return w.sb[kt];
+    }
+}
+
+template <int BLOCK>
+__device__ __forceinline__ void gl_load(GlW<BLOCK>& w, const GemmArgs& a, uint32_t tile, uint32_t k0,
+                                        int lr, int kq)
+{
+    const uint32_t K = (uint32_t)a.k;
+    const int64_t n0 = (int64_t)tile * 16;
+    const uint32_t rows = (uint32_t)(a.n - n0 < 16 ? a.n - n0 : 16);
+    const rsrc_t wr = make_rsrc(a.wc + n0 * (a.k / 2), rows * (K / 2));
+    // the scale range is rounded up to whole dwords: the dword holding a tile's last scale byte
+    // lies in the same page as that byte, and bytes past the end are never used
+    const rsrc_t sr = make_rsrc(a.ws + n0 * (a.k / BLOCK), (rows * (K / BLOCK) + 3) & ~3u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) t.xv[j] = bload128(r.x, ok ? r.xoff + (kk + 8 * j) * 2 : kOOB);
+    for (int kt = 0; kt < GL_KTW; ++kt) {
+        const uint32_t kk = k0 + kt * TK + 32 * kq;
+        const bool ok = kk < K;
+        w.cw[kt] = bload128(wr, ok ? lr * (K / 2) + kk / 2 : kOOB);
+        if constexpr (BLOCK < 32) w.sb[kt] = bload_lane_scales<BLOCK>(sr, ok ? lr * (K / BLOCK) + kk / BLOCK : kOOB);
+    }
+    if constexpr (BLOCK >= 32) {
+        static_assert(GL_KTW * TK / BLOCK <= 16, "scale bytes of a wave's range exceed one load");
+        constexpr int NB = GL_KTW * TK / BLOCK;                    // 16, 8, 4 or 2 bytes
+        // rows of scales need not start on a dword: load whole dwords from the aligned address
+        // below and shift the wanted bytes down with v_alignbyte
+        const bool in = k0 < K;
+        const uint32_t off = lr * (K / BLOCK) + k0 / BLOCK, a0 = off & ~3u, sh = off & 3u;
+        if constexpr (NB == 16) {
+            const u32x4 lo = bload128(sr, in ? a0 : kOOB);
+            const uint32_t hi = bload32(sr, in ? a0 + 16 : kOOB);
+            w.srow = u32x4{__builtin_amdgcn_alignbyte(lo.y, lo.x, sh), __builtin_amdgcn_alignbyte(lo.z, lo.y, sh),
+                           __builtin_amdgcn_alignbyte(lo.w, lo.z, sh), __builtin_amdgcn_alignbyte(hi, lo.w, sh)};
+        } else if constexpr (NB == 8) {
+            const uint64_t lo = bload64(sr, in ? a0 : kOOB);
+            const uint32_t hi = bload32(sr, in ? a0 + 8 : kOOB);
+            const uint32_t l0 = (uint32_t)lo, l1 = (uint32_t)(lo >> 32);
+            w.srow = u32x4{__builtin_amdgcn_alignbyte(l1, l0, sh), __builtin_amdgcn_alignbyte(hi, l1, sh), 0u, 0u};
+        } else {
+            const uint32_t l0 = bload32(sr, in ? a0 : kOOB), l1 = bload32(sr, in ? a0 + 4 : kOOB);
+            w.srow = u32x4{__builtin_amdgcn_alignbyte(l1, l0, sh), 0u, 0u, 0u};
+        }
+    }
 }
 
 template <int BLOCK, int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_a16_kernel(const GemmArgs a)
+__global__ __launch_bounds__(64 * GL_WAVES) void gemv_lds_kernel(const GemmArgs a)
 {
-    __shared__ f32x4 red[GEMV_WAVES - 1][64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, kq = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t n = n0 + lr;
-    const uint32_t K = (uint32_t)a.k;
-    const int64_t KT = (a.k + TK - 1) / TK;
-    const int64_t per = (KT + GEMV_WAVES - 1) / GEMV_WAVES;
-    const int64_t t0 = wave * per;
-    const int64_t t1 = t0 + per < KT ? t0 + per : KT;
-    const uint32_t rows = (uint32_t)(a.n - n0 < 16 ? a.n - n0 : 16);
+    const uint32_t K = (uint32_t)a.k, M = (uint32_t)a.m;
+    const uint32_t T = (uint32_t)((a.n + 15) / 16), G = gridDim.x;
+    const uint32_t ntiles = (T - blockIdx.x + G - 1) / G;  // at most GL_TMAX (launch)
+    const rsrc_t xr = make_rsrc(a.x, (uint32_t)(((int64_t)(M - 1) * a.ldx + K) * 2));
+    const uint32_t ldx = (uint32_t)a.ldx;
+    const uint32_t xrow = (uint32_t)lr < M ? (uint32_t)lr : 0u;  // rows >= m feed outputs never stored
 
-    GemvRows r;
-    r.w = make_rsrc(a.wc + n0 * (a.k / 2), rows * (K / 2));
-    r.s = make_rsrc(a.ws + n0 * (a.k / BLOCK), rows * (K / BLOCK));
-    r.x = make_rsrc(a.x, (uint32_t)(a.m * a.ldx * 2));
-    r.woff = lr * (K / 2);
-    r.soff = lr * (K / BLOCK);
-    r.xoff = (uint32_t)(lr * a.ldx * 2);
-    r.K = K;
+    f32x4 acc[GL_TMAX];
+#pragma unroll
+    for (int t = 0; t < GL_TMAX; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    GemvTile<BLOCK> buf[GEMV_DEPTH];
+    for (uint32_t kc = 0; kc < K; kc += GL_KC) {
+        __syncthreads();  // the previous chunk's activations have been read
+        // activations k = kc .. kc+4095 of rows m < M: 8 loads of 1 KB per row; k past the end
+        // reads as zero, so the weight zeros beyond k never meet stale LDS data
+        // every workgroup reads the same activations: start each at a different 1 KB piece so
+        // that the requests of concurrent workgroups spread over the L2 channels
+        const uint32_t pieces = M * 8, rot = (blockIdx.x * 13u) % pieces;
+        for (uint32_t c = (uint32_t)wave; c < pieces; c += GL_WAVES) {
+            const uint32_t i = c + rot < pieces ? c + rot : c + rot - pieces;
+            const uint32_t m = i >> 3, j = i & 7;
+            const uint32_t k = kc + j * 512 + lane * 8;
+            const uint32_t off = k < K ? (m * ldx + k) * 2 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(lds + m * GL_PITCH + j * 1024), 16, off, 0, 0, 0);
+        }
+        // the first tile's weights travel together with the activations
+        const uint32_t kw = (uint32_t)wave * (GL_KC / GL_WAVES);  // this wave's k offset in the chunk
+        GlW<BLOCK> buf[2];
+        gl_load<BLOCK>(buf[0], a, blockIdx.x, kc + kw, lr, kq);
+        __syncthreads();  // (waits for this wave's loads first) every wave's loads have landed
 #pragma unroll
-    for (int p = 0; p < GEMV_DEPTH; ++p) gemv_load<BLOCK>(buf[p], t0 + p, t1, kq, r);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t tb = t0; tb < t1; tb += GEMV_DEPTH) {
+        for (int t = 0; t < GL_TMAX; ++t) {
+            if ((uint32_t)t >= ntiles) continue;
+            if ((uint32_t)t + 1 < ntiles) gl_load<BLOCK>(buf[(t + 1) & 1], a, blockIdx.x + (t + 1) * G, kc + kw, lr, kq);
+            const GlW<BLOCK>& w = buf[t & 1];
 #pragma unroll
-        for (int p = 0; p < GEMV_DEPTH; ++p) {
-            uint32_t bw[16];
-            dequant32<BLOCK, FMT>(buf[p].cw, buf[p].sb, bw);
-            const u32x4 x0 = buf[p].xv[0], x1 = buf[p].xv[1], x2 = buf[p].xv[2], x3 = buf[p].xv[3];
-            gemv_load<BLOCK>(buf[p], tb + p + GEMV_DEPTH, t1, kq, r);
-            const uint32_t xf[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
-                                     x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+            for (int kt = 0; kt < GL_KTW; ++kt) {
+                uint32_t bw[16];
+                dequant32<BLOCK, FMT>(w.cw[kt], gl_scale<BLOCK>(w, kt, kq, kc + kw + kt * TK + 32 * kq < K), bw);
+                const uint8_t* xp = lds + xrow * GL_PITCH + (kw + kt * TK + 32 * kq) * 2;
+                uint32_t xf[16];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc = mfma_bf16(&xf[4 * j], &bw[4 * j], acc);
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(xp + 16 * q);
+                    xf[4 * q] = v.x; xf[4 * q + 1] = v.y; xf[4 * q + 2] = v.z; xf[4 * q + 3] = v.w;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[t] = mfma_bf16(&xf[4 * j], &bw[4 * j], acc[t]);
+            }
         }
     }
-    if (wave > 0) red[wave - 1][lane] = acc;
+    // the waves' partial sums meet in LDS ([wave][tile][lane]); wave w finishes tiles w, w+8, ...
     __syncthreads();
-    if (wave == 0) {
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
 #pragma unroll
-        for (int w = 0; w < GEMV_WAVES - 1; ++w) acc += red[w][lane];
+    for (int t = 0; t < GL_TMAX; ++t)
+        if ((uint32_t)t < ntiles) red[(wave * GL_TMAX + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    for (uint32_t t = (uint32_t)wave; t < ntiles; t += GL_WAVES) {
+        f32x4 v = red[t * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < GL_WAVES; ++w) v += red[(w * GL_TMAX + t) * 64 + lane];
+        const int64_t n = (int64_t)(blockIdx.x + t * G) * 16 + lr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t m = 4 * kq + i;
-            if (m < a.m && n < a.n) store_y<OUT_BF16>(a.y, a.ldy, m, n, acc[i] * a.g);
+            if (m < a.m && n < a.n) store_y<OUT_BF16>(a.y, a.ldy, m, n, v[i] * a.g);
         }
     }
 }
 
 // ---------------------------------------------------------------------------------------
-// W4A16 GEMV for m <= 4 on the vector ALUs.  A workgroup owns DOT_ROWS weight rows; its 4
+// W4A16 GEMV for m = 1 (the template takes up to 4 rows of X) on the vector ALUs.  A workgroup owns DOT_ROWS weight rows; its 4
 // waves split k into contiguous ranges of 2048-element chunks.  In a chunk, lane l holds the
 // 32 activations k = c*2048 + 32 l .. +31 of every row of X in registers (reused for all
 // DOT_ROWS weight rows) and, per weight row, loads that row's 16 code bytes for the same k
@@ -513,25 +589,33 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
                            dim3(256), 0, st, a);
         return hipGetLastError();
     }
-    if (a.m <= 4) {
-        const dim3 grid((unsigned)((a.n + DOT_ROWS - 1) / DOT_ROWS));
+    if (a.m >= 2 && a.m <= 16) {
+        const unsigned tiles = (unsigned)((a.n + 15) / 16);
+        unsigned g = tiles < 256 ? tiles : 256;                       // one workgroup per CU
+        if (g * GL_TMAX < tiles) g = (tiles + GL_TMAX - 1) / GL_TMAX;  // at most 16 tiles each
+        const int need = (int)a.m * GL_PITCH;
+        const int lds_bytes = need > GL_RED ? need : GL_RED;
         switch (a.block) {
-#define MXD1(B) case B: \
-    if (a.m == 1) hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
-    else hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 4, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
-    break;
-            MXD1(4) MXD1(8) MXD1(16) MXD1(32) MXD1(64) MXD1(128) MXD1(256)
-#undef MXD1
+#define MXL(B) case B: { \
+    static const hipError_t attr = hipFuncSetAttribute((const void*)gemv_lds_kernel<B, FMT, OUT_BF16>, \
+        hipFuncAttributeMaxDynamicSharedMemorySize, 16 * GL_PITCH > GL_RED ? 16 * GL_PITCH : GL_RED); \
+    if (attr != hipSuccess) return attr; \
+    hipLaunchKernelGGL((gemv_lds_kernel<B, FMT, OUT_BF16>), dim3(g), dim3(64 * GL_WAVES), lds_bytes, st, a); \
+    break; }
+            MXL(4) MXL(8) MXL(16) MXL(32) MXL(64) MXL(128) MXL(256)
+#undef MXL
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
     }
-    if (a.m <= 16) {
-        const dim3 grid((unsigned)((a.n + 15) / 16));
+    if (a.m == 1) {
+        const dim3 grid((unsigned)((a.n + DOT_ROWS - 1) / DOT_ROWS));
         switch (a.block) {
-#define MXV(B) case B: hipLaunchKernelGGL((gemv_a16_kernel<B, FMT, OUT_BF16>), grid, dim3(64 * GEMV_WAVES), 0, st, a); break;
-            MXV(4) MXV(8) MXV(16) MXV(32) MXV(64) MXV(128) MXV(256)
-#undef MXV
+#define MXD1(B) case B: \
+    hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
+    break;
+            MXD1(4) MXD1(8) MXD1(16) MXD1(32) MXD1(64) MXD1(128) MXD1(256)
+#undef MXD1
             default: return hipErrorInvalidValue;
         }
         return hipGetLastError();
