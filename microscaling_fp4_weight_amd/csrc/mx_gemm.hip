@@ -16,47 +16,10 @@
 // lane's 16 code bytes and its E8M0 byte are exactly one MFMA operand slice and its scale.
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "mx_wdeq.h"
 
 namespace mxk {
 
-
-// ---------------------------------------------------------------------------------------
-// Weight fragment: 16 code bytes (32 k of one row) -> 16 dwords of bf16 pairs.
-// ---------------------------------------------------------------------------------------
-template <int FMT>
-struct WScale {
-    float pow2;
-    float mant;
-};
-
-template <int FMT>
-__device__ __forceinline__ WScale<FMT> wscale(uint32_t byte)
-{
-    WScale<FMT> s;
-    if constexpr (FMT == FMT_E8M0) {
-        s.pow2 = e8m0_value(byte);
-        s.mant = 1.0f;
-    } else {
-        const DecG1 p = dec_params_g1<FMT>(byte);
-        s.pow2 = p.pow2;
-        s.mant = p.mant;
-    }
-    return s;
-}
-
-template <int FMT, int SEL>
-__device__ __forceinline__ uint32_t deq_pair_bf16(uint32_t cw, const WScale<FMT>& s)
-{
-    if constexpr (FMT == FMT_E8M0) {
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, s.pow2, SEL));
-    } else {
-        const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, s.pow2, SEL);
-        bf16x2 h;
-        h.x = (__bf16)(f.x * s.mant);  // e * s is exact in bf16 (<= 6 significant bits)
-        h.y = (__bf16)(f.y * s.mant);
-        return __builtin_bit_cast(uint32_t, h);
-    }
-}
 
 // Scales covering one lane's 32 k: BLOCK >= 32 -> one byte; else 32/BLOCK bytes packed.
 template <int BLOCK>
@@ -66,28 +29,6 @@ __device__ __forceinline__ uint64_t load_lane_scales(const uint8_t* p)
     else if constexpr (BLOCK == 16) return *reinterpret_cast<const uint16_t*>(p);
     else if constexpr (BLOCK == 8) return *reinterpret_cast<const uint32_t*>(p);
     else return *reinterpret_cast<const uint64_t*>(p);
-}
-
-template <int BLOCK, int FMT>
-__device__ __forceinline__ void dequant32(const u32x4 cw, uint64_t sbytes, uint32_t d[16])
-{
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int sel = 0; sel < 4; ++sel) {
-            const int pair = 4 * w + sel;  // elements 2*pair, 2*pair+1 of the 32
-            const int sidx = BLOCK >= 32 ? 0 : (2 * pair) / BLOCK;
-            const WScale<FMT> s = wscale<FMT>((uint32_t)(sbytes >> (8 * sidx)) & 0xFFu);
-            uint32_t v;
-            switch (sel) {
-                case 0: v = deq_pair_bf16<FMT, 0>(cw[w], s); break;
-                case 1: v = deq_pair_bf16<FMT, 1>(cw[w], s); break;
-                case 2: v = deq_pair_bf16<FMT, 2>(cw[w], s); break;
-                default: v = deq_pair_bf16<FMT, 3>(cw[w], s); break;
-            }
-            d[pair] = v;
-        }
-    }
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(const uint32_t* a4, const uint32_t* b4, f32x4 c)
@@ -620,6 +561,7 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
         }
         return hipGetLastError();
     }
+    if (a16_uses_tiled(a)) return launch_gemm_a16_tiled(a, st);
     const dim3 grid((unsigned)((a.n + TN - 1) / TN), (unsigned)((a.m + TM - 1) / TM));
     switch (a.block) {
 #define MXG(B) case B: hipLaunchKernelGGL((gemm_a16_kernel<B, FMT, OUT_BF16>), grid, dim3(256), 0, st, a); break;

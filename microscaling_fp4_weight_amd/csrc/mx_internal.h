@@ -87,6 +87,9 @@ inline int64_t tiled_scale_bytes(int64_t rows, int64_t k)
 }
 // whether the W4A4 product runs on the matrix-core kernel (else the direct one)
 bool a4_uses_mfma(const GemmArgs& a);
+// whether the large-m W4A16 product runs on the pipelined kernel (else the simple one)
+bool a16_uses_tiled(const GemmArgs& a);
+hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);

@@ -71,6 +71,34 @@ def test_gemm_a16_ragged(fmt, block):
         check(x, c, s, cd, sd, block, fmt, 1.0, "a16", out)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mnk", [(200, 300, 1024), (17, 256, 512), (300, 520, 2048), (256, 512, 1536)])
+def test_gemm_a16_pipelined(fmt, mnk):
+    """Block 32 and k a multiple of 512: the pipelined kernel (128 x 256 tiles, 3-stage LDS
+    ring, 512-k scale windows) -- ragged m and n, one to several scale windows."""
+    m, n, k = mnk
+    x = synth.normal((m, k), "bf16", f"gp.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", f"gp.w.{n}", 0.02, 0.01, 20.0)
+    c, s, cd, sd = quantize_ref(w, 32, fmt)
+    for out in ("f32", "bf16"):
+        check(x, c, s, cd, sd, 32, fmt, 1.0, "a16", out)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_a16_pipelined_tensor_scale_and_stride(fmt):
+    """Two-level scaling (g != 1) and an activation row stride larger than k."""
+    m, n, k, g = 130, 260, 1024, float(np.float32(0.37))
+    x = synth.normal((m, k + 64), "bf16", "gps.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gps.w", 0.05)
+    c, s = oracle.quantize(w, 32, fmt, g)
+    cd, sd = torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV)
+    xd = bf16_dev(x)[:, :k]
+    y = mx.mx_gemm(xd, cd, sd, 32, fmt, g, "a16", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm(np.ascontiguousarray(x[:, :k]), c, s, 32, fmt, g, "a16")
+    assert_gemm_close(to_host_bits(y), yref, aref, False, f"a16 pipelined g {fmt}")
+
+
 def test_gemm_a16_k_tail_32():
     m, n, k = 40, 70, 160  # k % 128 == 32
     x = synth.normal((m, k), "bf16", "gt.x", 1.0)
