@@ -121,6 +121,30 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
 size_t mx_scale_bytes(int64_t rows, int64_t k, int block, mx_layout layout);
 
 /*
+ * mx_quant_error -- the error of MX quantization, decomposed ([MXS] section 2.2 items 1-3),
+ * computed on the device in one pass over x: every block is quantized exactly as by
+ * mx_quantize (row-major, same block, fmt, tensor_scale), dequantized in fp64
+ * (x^ = e(code) * s * g), and each squared error (x^ - x)^2 is added to one of three sums:
+ *   zero-scale term: every element of a block whose scale is 0 (flushed);
+ *   max term:        in the other blocks, the element holding the block's largest |x|
+ *                    (its first occurrence);
+ *   element term:    every other element.
+ *  out        : device, 7 doubles: MSE_elem, MSE_max, MSE_zero (each sum divided by
+ *               rows * k), MSE_total (a separate sum of all squared errors, / (rows * k)),
+ *               number of blocks, number of flushed blocks, number of non-flushed blocks
+ *               whose maximum is not coded +-6.
+ *  workspace  : device buffer of at least mx_quant_error_workspace_size(rows, k, block) bytes
+ *               (per-workgroup partial sums).
+ * Sums are accumulated in fp64 in an order fixed by the shape, so repeated calls return the
+ * same bits.  Errors as for mx_quantize, plus MX_ERR_INVALID_ARG for a null out or a missing
+ * or short workspace.  For an empty tensor nothing is launched and out is not written.
+ */
+size_t mx_quant_error_workspace_size(int64_t rows, int64_t k, int block);
+mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
+                         int block, mx_scale_fmt fmt, float tensor_scale, double* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mx_gemm_workspace_size -- bytes of device workspace mx_gemm needs for this shape and mode
  * (0 when none).  MX_A4 needs room for the quantized activations: m*k/2 code bytes and
  * mx_scale_bytes(m, k, 32, MX_LAYOUT_TILED) scale bytes, each rounded up to 256 bytes.

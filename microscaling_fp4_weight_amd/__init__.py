@@ -18,6 +18,7 @@ import os
 import torch
 
 __all__ = ["mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_scale_bytes",
+           "mx_quant_error", "mx_quant_error_workspace_size",
            "mx_status_string", "MXError", "lib", "FMT", "MODE", "DTYPE", "LAYOUT", "STATUS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,10 @@ def lib() -> ctypes.CDLL:
     L.mx_dequantize.restype = i32
     L.mx_scale_bytes.argtypes = [i64, i64, i32, i32]
     L.mx_scale_bytes.restype = sz
+    L.mx_quant_error_workspace_size.argtypes = [i64, i64, i32]
+    L.mx_quant_error_workspace_size.restype = sz
+    L.mx_quant_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, vp, sz, vp]
+    L.mx_quant_error.restype = i32
     L.mx_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     L.mx_gemm_workspace_size.restype = sz
     L.mx_gemm.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp,
@@ -136,6 +141,28 @@ def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, k: int, block: int,
 
 def mx_scale_bytes(rows: int, k: int, block: int, layout: str = "rowmajor") -> int:
     return int(lib().mx_scale_bytes(rows, k, block, LAYOUT[layout]))
+
+
+def mx_quant_error_workspace_size(rows: int, k: int, block: int) -> int:
+    return int(lib().mx_quant_error_workspace_size(rows, k, block))
+
+
+def mx_quant_error(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Error split of MX-quantizing x (rows x k, bf16/fp32 on the GPU), computed on the device.
+    Returns a float64 device tensor of 7 values: MSE_elem, MSE_max, MSE_zero, MSE_total,
+    blocks, flushed blocks, non-flushed blocks whose maximum is not coded +-6."""
+    rows, k, ld = _rows_ld(x, "x")
+    if out is None:
+        out = torch.zeros(8, dtype=torch.float64, device=x.device)  # 7 used; 16-byte aligned
+    need = mx_quant_error_workspace_size(rows, k, block)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    st = lib().mx_quant_error(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt], tensor_scale,
+                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "mx_quant_error")
+    return out[:7]
 
 
 def mx_gemm_workspace_size(m: int, n: int, k: int, block: int, mode: str) -> int:

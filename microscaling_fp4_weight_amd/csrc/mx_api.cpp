@@ -166,6 +166,41 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
     return MX_OK;
 }
 
+size_t mx_quant_error_workspace_size(int64_t rows, int64_t k, int block)
+{
+    if (rows < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;
+    if (rows == 0 || k == 0) return 0;
+    return round256((size_t)mxk::quant_error_groups(rows, k, block) * 6 * sizeof(double));
+}
+
+mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
+                         int block, mx_scale_fmt fmt, float tensor_scale, double* out,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    mx_status st = check_quantized(rows, k, block, fmt, tensor_scale, MX_LAYOUT_ROWMAJOR);
+    if (st != MX_OK) return st;
+    if (x_type != MX_F32 && x_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_x < k) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return MX_OK;
+    if (!x || !out) return MX_ERR_INVALID_ARG;
+    const size_t need = mx_quant_error_workspace_size(rows, k, block);
+    if (!workspace || workspace_bytes < need) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return MX_ERR_ALIGNMENT;
+    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
+    mxk::ErrArgs a;
+    a.x = x;
+    a.bf16 = x_type == MX_BF16;
+    a.rows = rows;
+    a.k = k;
+    a.ldx = ld_x;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = (double)tensor_scale;
+    a.partials = static_cast<double*>(workspace);
+    a.out = out;
+    return from_hip(mxk::launch_quant_error(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode)
 {
     if (m < 0 || n < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;

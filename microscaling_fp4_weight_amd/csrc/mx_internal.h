@@ -91,7 +91,22 @@ bool a4_uses_mfma(const GemmArgs& a);
 bool a16_uses_tiled(const GemmArgs& a);
 hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st);
 
+struct ErrArgs {
+    const void* x;
+    bool bf16;        // input element type
+    int64_t rows, k, ldx;
+    int block;
+    int fmt;
+    double g;
+    double* partials; // workspace: ERR_NP doubles per workgroup
+    double* out;      // 7 doubles
+};
+
+constexpr int kErrMaxGroups = 2048;  // workgroups of the error reduction (fixed grid cap)
+int quant_error_groups(int64_t rows, int64_t k, int block);
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+hipError_t launch_quant_error(const ErrArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_a4(const GemmArgs& a, hipStream_t st);

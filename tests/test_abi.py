@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_exports_match_header(L):
     names = declared_functions()
-    assert names == ["mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_quantize",
-                     "mx_scale_bytes", "mx_status_string"]
+    assert names == ["mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_quant_error",
+                     "mx_quant_error_workspace_size", "mx_quantize", "mx_scale_bytes", "mx_status_string"]
     for n in names:
         assert hasattr(L, n)
     so = os.path.join(ROOT, "microscaling_fp4_weight_amd", "libmx.so")
@@ -139,3 +139,27 @@ def test_gemm_validation_and_workspace(L):
     assert gemm(m=0, x=None, y=None) == OK
     assert gemm(n=0, wc=None, wsc=None, y=None) == OK
     assert gemm(k=0, y=FAKE + 2) == ALIGN
+
+
+def test_quant_error_validation(L):
+    ws = L.mx_quant_error_workspace_size
+    assert ws(4, 64, 32) == 256            # one workgroup: 6 doubles, rounded to 256 bytes
+    assert ws(4096, 11008, 4) == 2048 * 6 * 8  # the grid is capped at 2048 workgroups
+    assert ws(0, 64, 32) == 0
+    assert ws(4, 48, 32) == 0              # k % block
+
+    def qe(x=FAKE, xt=BF16, rows=4, k=64, ldx=64, block=32, fmt=E8M0, g=1.0, out=FAKE, work=FAKE,
+           wbytes=256):
+        return L.mx_quant_error(x, xt, rows, k, ldx, block, fmt, g, out, work, wbytes, None)
+
+    assert qe(out=None) == INVALID
+    assert qe(work=None) == INVALID
+    assert qe(wbytes=255) == INVALID
+    assert qe(block=12) == INVALID
+    assert qe(fmt=3) == INVALID
+    assert qe(xt=7) == INVALID
+    assert qe(ldx=63) == INVALID
+    assert qe(g=0.0) == INVALID
+    assert qe(out=FAKE + 8) == ALIGN
+    assert qe(x=FAKE + 2) == ALIGN
+    assert qe(rows=0, x=None, out=None, work=None, wbytes=0) == OK  # empty: nothing launched
