@@ -196,6 +196,8 @@ def main():
                 "traffic": traffic, "bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_avg_ms * 1e3, 3)}
 
+    error_split = measure_error_split(mx, L, torch, inputs, configs, dev, stream)
+
     # free the sweep buffers before the GEMM rows
     del inputs, codes, scales, deq_out, qcalls, dcalls
     torch.cuda.empty_cache()
@@ -216,9 +218,87 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "per_config": per_config,
+        "error_split": error_split,
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
+
+
+def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
+    """The sweep's error split computed on the device (mx_quant_error: quantize, dequantize and
+    the fp64 MSE_elem / MSE_max / MSE_zero sums in one pass over the weight): per-config
+    kernel time (median of 3, one event pair per launch), the whole 63-config sweep, and the
+    device MSE terms; plus the fake-quant variant that also writes x^ (block 32, E4M3)."""
+    n = C2_ROWS * C2_K
+    sp = stream.cuda_stream
+    need = max(mx.mx_quant_error_workspace_size(C2_ROWS, C2_K, b) for b in BLOCKS)
+    work = torch.empty(need, dtype=torch.uint8, device=dev)
+    outs = torch.zeros((len(configs), 8), dtype=torch.float64, device=dev)
+    calls = []
+    for i, (si, b, f) in enumerate(configs):
+        x = inputs[2 * si + (i // len(SIGMAS)) % 2]
+        calls.append((x.data_ptr(), 1, C2_ROWS, C2_K, C2_K, b, mx.FMT[f], 1.0, None, 0,
+                       outs[i].data_ptr(), work.data_ptr(), need, sp))
+    qe = L.mx_quant_error
+
+    def run(c):
+        st = qe(*c)
+        if st:
+            raise mx.MXError(st, "mx_quant_error")
+
+    for c in calls:  # warm-up
+        run(c)
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for c in calls:
+        run(c)
+    b_.record(stream)
+    evs = []
+    for rep in range(3):
+        for i, c in enumerate(calls):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run(c)
+            e1.record(stream)
+            evs.append((i, e0, e1))
+    # fake quantization: the error split plus x^ written (sigma 0.02, block 32, E4M3)
+    fi = configs.index((1, 32, "e4m3"))
+    xh = torch.empty((C2_ROWS, C2_K), dtype=torch.bfloat16, device=dev)
+    fq = list(calls[fi])
+    fq[8], fq[9] = xh.data_ptr(), C2_K
+    run(fq)
+    fevs = []
+    for rep in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(fq)
+        e1.record(stream)
+        fevs.append((e0, e1))
+    torch.cuda.synchronize()
+    sweep_ms = a.elapsed_time(b_)
+    acc = {}
+    for i, e0, e1 in evs:
+        acc.setdefault(i, []).append(e0.elapsed_time(e1))
+    vals = outs.cpu().numpy()
+    per = {}
+    for i, ts in acc.items():
+        si, b, f = configs[i]
+        t = sorted(ts)[1]
+        gbs = 2 * n / (t * 1e-3) / 1e9
+        per[f"s{SIGMAS[si]}.B{b}.{f}"] = {
+            "us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
+            "mse_elem": float(vals[i, 0]), "mse_max": float(vals[i, 1]), "mse_zero": float(vals[i, 2]),
+            "flushed_blocks": int(vals[i, 5])}
+    ft = sorted(e0.elapsed_time(e1) for e0, e1 in fevs)[2]
+    fgbs = 4 * n / (ft * 1e-3) / 1e9
+    log(f"error split: 63-config sweep {sweep_ms:.3f} ms; B32 E4M3 {per['s0.02.B32.e4m3']['us']} us; "
+        f"fake quant {ft * 1e3:.1f} us")
+    return {"kernel": "quant_error_fast_kernel", "bytes_per_launch": 2 * n,
+            "sweep_ms": round(sweep_ms, 3),
+            "sweep_GB/s": round(2 * n * len(calls) / (sweep_ms * 1e-3) / 1e9, 1),
+            "fake_quant.s0.02.B32.e4m3": {"us": round(ft * 1e3, 2), "bytes": 4 * n, "GB/s": round(fgbs, 1),
+                                          "frac_hbm": round(fgbs * 1e9 / PEAK_HBM, 3)},
+            "per_config": per}
 
 
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written per launch

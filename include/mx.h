@@ -123,26 +123,32 @@ size_t mx_scale_bytes(int64_t rows, int64_t k, int block, mx_layout layout);
 /*
  * mx_quant_error -- the error of MX quantization, decomposed ([MXS] section 2.2 items 1-3),
  * computed on the device in one pass over x: every block is quantized exactly as by
- * mx_quantize (row-major, same block, fmt, tensor_scale), dequantized in fp64
- * (x^ = e(code) * s * g), and each squared error (x^ - x)^2 is added to one of three sums:
+ * mx_quantize (row-major, same block, fmt, tensor_scale), dequantized (x^ = e(code) * s * g,
+ * exact in fp64), and each squared error (x^ - x)^2 is added to one of three sums:
  *   zero-scale term: every element of a block whose scale is 0 (flushed);
- *   max term:        in the other blocks, the element holding the block's largest |x|
- *                    (its first occurrence);
+ *   max term:        in the other blocks, one element holding the block's largest |x|
+ *                    (elements tied at the maximum share its code and its error);
  *   element term:    every other element.
+ *  x_hat      : optional device output (NULL: not written), rows x k, element type x_type,
+ *               row stride ld_x_hat >= k: the dequantized tensor, rounded exactly as
+ *               mx_dequantize rounds it (the forward pass of fake quantization).
  *  out        : device, 7 doubles: MSE_elem, MSE_max, MSE_zero (each sum divided by
- *               rows * k), MSE_total (a separate sum of all squared errors, / (rows * k)),
+ *               rows * k), MSE_total (its own sum of all squared errors, / (rows * k)),
  *               number of blocks, number of flushed blocks, number of non-flushed blocks
  *               whose maximum is not coded +-6.
  *  workspace  : device buffer of at least mx_quant_error_workspace_size(rows, k, block) bytes
  *               (per-workgroup partial sums).
- * Sums are accumulated in fp64 in an order fixed by the shape, so repeated calls return the
- * same bits.  Errors as for mx_quantize, plus MX_ERR_INVALID_ARG for a null out or a missing
- * or short workspace.  For an empty tensor nothing is launched and out is not written.
+ * Sums are accumulated in fp64 in an order fixed by the shape and the alignment of x and
+ * x_hat, so repeated calls return the same bits.  Errors as for mx_quantize (x_hat must be
+ * 16-byte aligned too), plus MX_ERR_INVALID_ARG for a null out, a missing or short
+ * workspace, or ld_x_hat < k with x_hat given.  For an empty tensor nothing is launched and
+ * out is not written.
  */
 size_t mx_quant_error_workspace_size(int64_t rows, int64_t k, int block);
 mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
-                         int block, mx_scale_fmt fmt, float tensor_scale, double* out,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         int block, mx_scale_fmt fmt, float tensor_scale, void* x_hat,
+                         int64_t ld_x_hat, double* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /*
  * mx_gemm_workspace_size -- bytes of device workspace mx_gemm needs for this shape and mode

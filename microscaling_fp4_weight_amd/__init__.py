@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
     L.mx_scale_bytes.restype = sz
     L.mx_quant_error_workspace_size.argtypes = [i64, i64, i32]
     L.mx_quant_error_workspace_size.restype = sz
-    L.mx_quant_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, vp, sz, vp]
+    L.mx_quant_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, i64, vp, vp, sz, vp]
     L.mx_quant_error.restype = i32
     L.mx_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     L.mx_gemm_workspace_size.restype = sz
@@ -148,19 +148,26 @@ def mx_quant_error_workspace_size(rows: int, k: int, block: int) -> int:
 
 
 def mx_quant_error(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0,
-                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                   stream=None) -> torch.Tensor:
+                   x_hat: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Error split of MX-quantizing x (rows x k, bf16/fp32 on the GPU), computed on the device.
     Returns a float64 device tensor of 7 values: MSE_elem, MSE_max, MSE_zero, MSE_total,
-    blocks, flushed blocks, non-flushed blocks whose maximum is not coded +-6."""
+    blocks, flushed blocks, non-flushed blocks whose maximum is not coded +-6.  When x_hat
+    (same shape and dtype as x) is given, the dequantized tensor is written into it."""
     rows, k, ld = _rows_ld(x, "x")
+    ldh = 0
+    if x_hat is not None:
+        if x_hat.dtype != x.dtype or tuple(x_hat.shape) != tuple(x.shape):
+            raise ValueError("x_hat must have the shape and dtype of x")
+        _, _, ldh = _rows_ld(x_hat, "x_hat")
     if out is None:
         out = torch.zeros(8, dtype=torch.float64, device=x.device)  # 7 used; 16-byte aligned
     need = mx_quant_error_workspace_size(rows, k, block)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     st = lib().mx_quant_error(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt], tensor_scale,
-                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+                              _ptr(x_hat), ldh, _ptr(out), _ptr(workspace), workspace.numel(),
+                              _stream(stream))
     _check(st, "mx_quant_error")
     return out[:7]
 

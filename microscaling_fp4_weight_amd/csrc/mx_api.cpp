@@ -174,19 +174,22 @@ size_t mx_quant_error_workspace_size(int64_t rows, int64_t k, int block)
 }
 
 mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
-                         int block, mx_scale_fmt fmt, float tensor_scale, double* out,
-                         void* workspace, size_t workspace_bytes, void* stream)
+                         int block, mx_scale_fmt fmt, float tensor_scale, void* x_hat,
+                         int64_t ld_x_hat, double* out, void* workspace, size_t workspace_bytes,
+                         void* stream)
 {
     mx_status st = check_quantized(rows, k, block, fmt, tensor_scale, MX_LAYOUT_ROWMAJOR);
     if (st != MX_OK) return st;
     if (x_type != MX_F32 && x_type != MX_BF16) return MX_ERR_INVALID_ARG;
-    if (ld_x < k) return MX_ERR_INVALID_ARG;
+    if (ld_x < k || (x_hat && ld_x_hat < k)) return MX_ERR_INVALID_ARG;
     if (rows == 0 || k == 0) return MX_OK;
     if (!x || !out) return MX_ERR_INVALID_ARG;
     const size_t need = mx_quant_error_workspace_size(rows, k, block);
     if (!workspace || workspace_bytes < need) return MX_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return MX_ERR_ALIGNMENT;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace) || (x_hat && !aligned16(x_hat)))
+        return MX_ERR_ALIGNMENT;
     if (k > kMaxK) return MX_ERR_UNSUPPORTED;
+    const int64_t esize = x_type == MX_BF16 ? 2 : 4;
     mxk::ErrArgs a;
     a.x = x;
     a.bf16 = x_type == MX_BF16;
@@ -196,6 +199,10 @@ mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k
     a.block = block;
     a.fmt = (int)fmt;
     a.g = (double)tensor_scale;
+    a.xhat = x_hat;
+    a.ldxh = x_hat ? ld_x_hat : 0;
+    a.fast = (k % 32 == 0) && ((ld_x * esize) % 16 == 0) && (!x_hat || (ld_x_hat * esize) % 16 == 0) &&
+             rows * (k / 32) < (int64_t(1) << 31);
     a.partials = static_cast<double*>(workspace);
     a.out = out;
     return from_hip(mxk::launch_quant_error(a, static_cast<hipStream_t>(stream)));

@@ -98,11 +98,14 @@ struct ErrArgs {
     int block;
     int fmt;
     double g;
+    void* xhat;       // optional x^ output (element type of x), row stride ldxh
+    int64_t ldxh;
+    bool fast;        // k % 32 == 0, 16-byte aligned rows, rows * k / 32 < 2^31
     double* partials; // workspace: ERR_NP doubles per workgroup
     double* out;      // 7 doubles
 };
 
-constexpr int kErrMaxGroups = 2048;  // workgroups of the error reduction (fixed grid cap)
+constexpr int kErrMaxGroups = 1024;  // workgroups of the error reduction (fixed grid cap)
 int quant_error_groups(int64_t rows, int64_t k, int block);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);

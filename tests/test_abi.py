@@ -144,13 +144,14 @@ def test_gemm_validation_and_workspace(L):
 def test_quant_error_validation(L):
     ws = L.mx_quant_error_workspace_size
     assert ws(4, 64, 32) == 256            # one workgroup: 6 doubles, rounded to 256 bytes
-    assert ws(4096, 11008, 4) == 2048 * 6 * 8  # the grid is capped at 2048 workgroups
+    assert ws(4096, 11008, 4) == 1024 * 6 * 8  # the grid is capped at 1024 workgroups
     assert ws(0, 64, 32) == 0
     assert ws(4, 48, 32) == 0              # k % block
 
-    def qe(x=FAKE, xt=BF16, rows=4, k=64, ldx=64, block=32, fmt=E8M0, g=1.0, out=FAKE, work=FAKE,
-           wbytes=256):
-        return L.mx_quant_error(x, xt, rows, k, ldx, block, fmt, g, out, work, wbytes, None)
+    def qe(x=FAKE, xt=BF16, rows=4, k=64, ldx=64, block=32, fmt=E8M0, g=1.0, xh=None, ldh=0,
+           out=FAKE, work=FAKE, wbytes=256):
+        return L.mx_quant_error(x, xt, rows, k, ldx, block, fmt, g, xh, ldh, out, work, wbytes,
+                                None)
 
     assert qe(out=None) == INVALID
     assert qe(work=None) == INVALID
@@ -160,6 +161,8 @@ def test_quant_error_validation(L):
     assert qe(xt=7) == INVALID
     assert qe(ldx=63) == INVALID
     assert qe(g=0.0) == INVALID
+    assert qe(xh=FAKE, ldh=63) == INVALID    # x_hat row stride below k
+    assert qe(xh=FAKE + 4, ldh=64) == ALIGN
     assert qe(out=FAKE + 8) == ALIGN
     assert qe(x=FAKE + 2) == ALIGN
     assert qe(rows=0, x=None, out=None, work=None, wbytes=0) == OK  # empty: nothing launched

@@ -10,7 +10,7 @@ import torch
 import microscaling_fp4_weight_amd as mx
 import oracle
 import synth
-from gpu_util import DEV, bf16_dev
+from gpu_util import DEV, bf16_dev, edge_tensor, f32_dev, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -23,9 +23,9 @@ def _gpu():
     mx.lib()
 
 
-def check(x_host, xd, block, fmt, g=1.0):
+def check(x_host, xd, block, fmt, g=1.0, x_hat=None):
     ref = oracle.mse_split(x_host, block, fmt, g)
-    out = mx.mx_quant_error(xd, block, fmt, g).cpu().numpy()
+    out = mx.mx_quant_error(xd, block, fmt, g, x_hat=x_hat).cpu().numpy()
     for i, key in enumerate(KEYS):
         assert out[i] == pytest.approx(ref[key], rel=1e-12, abs=1e-300), (key, block, fmt, g)
     assert int(out[4]) == ref["blocks"]
@@ -74,3 +74,74 @@ def test_error_split_llama7b_ffn_full():
     # the full sweep tensor at one configuration (sigma 0.02, block 32, E4M3)
     w = synth.c2_weight(0.02)
     check(w, bf16_dev(w), 32, "e4m3")
+
+
+def dev(x):
+    return bf16_dev(x) if x.dtype == np.uint16 else f32_dev(x)
+
+
+def check_fake_quant(x, block, fmt, g, ld=None):
+    """Error split plus x^ (the dequantized tensor) bit-exact against the oracle's quantize
+    then dequantize; ld > k puts x and x^ in wider buffers (row stride ld)."""
+    rows, k = x.shape
+    if ld is None:
+        xd = dev(x)
+    else:
+        wide = np.zeros((rows, ld), dtype=x.dtype)
+        wide[:, :k] = x
+        xd = dev(wide)[:, :k]
+    xh_full = torch.full((rows, ld or k), -1.0, dtype=xd.dtype, device=DEV)
+    xh = xh_full[:, :k]
+    check(x, xd, block, fmt, g, x_hat=xh)
+    codes, scales = oracle.quantize(x, block, fmt, g)
+    ref = oracle.dequantize(codes, scales, k, block, fmt, g, "bf16" if x.dtype == np.uint16 else "f32")
+    got = to_host_bits(xh.contiguous())
+    if x.dtype == np.uint16:
+        np.testing.assert_array_equal(got, ref)
+    else:
+        np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    if ld is not None:  # the padding columns are untouched
+        assert torch.all(xh_full[:, k:] == -1.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e8m0"])
+@pytest.mark.parametrize("block", [4, 32, 256])
+@pytest.mark.parametrize("g", [1.0, 0.0137])
+def test_fake_quant_fast_path(dtype, fmt, block, g):
+    g = float(np.float32(g))
+    x = synth.normal((48, 1024), dtype, f"fq.{dtype}", 0.02, 0.01, 20.0)
+    check_fake_quant(x, block, fmt, g)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e8m0"])
+@pytest.mark.parametrize("block,k,ld", [(8, 504, None), (4, 36, None), (32, 512, 516), (64, 512, 514)])
+@pytest.mark.parametrize("g", [1.0, 0.37])
+def test_fake_quant_generic_path(dtype, fmt, block, k, ld, g):
+    # k % 32 != 0 or a row stride that is not a multiple of 16 bytes: one thread per block
+    g = float(np.float32(g))
+    x = synth.normal((37, k), dtype, f"fqg.{dtype}.{k}", 0.05, 0.02, 20.0)
+    check_fake_quant(x, block, fmt, g, ld)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e8m0"])
+@pytest.mark.parametrize("block", [8, 32, 128])
+@pytest.mark.parametrize("ld", [None, 516])
+def test_error_split_edge_values(fmt, block, ld):
+    # every scale byte, ties at the maximum with both signs, signed zeros, flush boundaries,
+    # subnormals and near-overflow blocks; ld = 516 takes the generic path
+    check_fake_quant(edge_tensor(512), block, fmt, 1.0, ld)
+
+
+@pytest.mark.parametrize("block", [4, 64, 256])
+def test_error_split_all_ties(block):
+    # every element at +-amax: the whole block's error is one value; the max term takes one
+    # element per block and the element term the rest
+    rng = np.random.default_rng(7)
+    mags = (rng.integers(1, 100, size=(16, 1)) * 0.0173).astype(np.float32)
+    signs = np.where(rng.random((16, 512)) < 0.5, -1.0, 1.0).astype(np.float32)
+    x = (mags * signs).astype(np.float32)
+    for fmt in ("e4m3", "ue5m3", "e8m0"):
+        check_fake_quant(x, block, fmt, 1.0)
+        check_fake_quant(x, block, fmt, 1.0, ld=516)
