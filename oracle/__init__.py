@@ -176,3 +176,39 @@ def mse_split(x: np.ndarray, block: int, fmt: str, g: float = 1.0) -> dict:
         raise ValueError("oracle mse_split: bad arguments")
     return {"elem": out[0], "max": out[1], "zero": out[2], "total": out[3],
             "blocks": int(out[4]), "zero_blocks": int(out[5]), "max_not6": int(out[6])}
+
+
+# ----------------------------------------------------------------------------------------
+# Block-size policy (hotelren.com/news/2192771, article "量化技术演进与微缩量化原理",
+# section 6 item 2: the block size follows the tensor's standard deviation; section 5.1 item
+# 1: a block size per layer kind).
+# ----------------------------------------------------------------------------------------
+
+def tensor_stats(x: np.ndarray) -> dict:
+    """Mean, standard deviation and max |x| of a whole tensor, in fp64, by the textbook two
+    passes: mean = sum(x) / n, then std = sqrt(sum((x - mean)^2) / (n - 1)) (the sample
+    standard deviation, n - 1 in the denominator; NaN for a single element)."""
+    v = x.astype(np.float64) if x.dtype != np.uint16 else (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    v = v.ravel()
+    n = v.size
+    mean = float(np.sum(v)) / n
+    m2 = float(np.sum((v - mean) ** 2))
+    std = float(np.sqrt(m2 / (n - 1))) if n > 1 else float("nan")
+    return {"mean": mean, "std": std, "absmax": float(np.max(np.abs(v))), "n": n}
+
+
+def adaptive_block_size(sigma: float) -> int:
+    """Section 6 item 2: sigma < 0.01 -> 128; sigma < 0.1 -> 64; otherwise 32."""
+    if sigma < 0.01:
+        return 128
+    if sigma < 0.1:
+        return 64
+    return 32
+
+
+LAYER_BLOCK = {"qkv": 64, "ffn_gate_up": 32, "output": 128}  # section 5.1 item 1
+
+
+def layer_block_size(kind: str) -> int:
+    """Section 5.1 item 1: Q/K/V projections 64, FFN gate/up 32, output projection 128."""
+    return LAYER_BLOCK[kind]
