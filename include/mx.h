@@ -151,6 +151,39 @@ mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k
                          void* stream);
 
 /*
+ * Block-size policy ([MXS] section 6 item 2: the block size follows the tensor's standard
+ * deviation; section 5.1 item 1: a block size per layer kind).
+ *
+ * mx_tensor_stats -- mean, sample standard deviation and max |x| of a whole rows x k tensor
+ * (element type x_type, row stride ld_x >= k), on the device, in two fp64 passes:
+ * mean = sum(x) / n, std = sqrt(sum((x - mean)^2) / (n - 1)) (NaN when n == 1).
+ *  out        : device, 3 doubles: mean, std, max |x|.
+ *  workspace  : device buffer of at least mx_tensor_stats_workspace_size(rows, k) bytes.
+ * The sums run in an order fixed by the shape and alignment, so repeated calls return the
+ * same bits.  Errors: MX_ERR_INVALID_ARG for negative sizes, ld_x < k, an unknown x_type, a
+ * null x/out or a missing or short workspace; MX_ERR_ALIGNMENT unless x, out and workspace
+ * are 16-byte aligned; MX_ERR_UNSUPPORTED beyond 2^31 - 1 load units (8 elements each for
+ * k % 8 == 0 and 16-byte row strides, else single elements).  An empty tensor launches
+ * nothing and leaves out unwritten.
+ */
+size_t mx_tensor_stats_workspace_size(int64_t rows, int64_t k);
+mx_status mx_tensor_stats(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x, double* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mx_adaptive_block_size -- block size for a tensor of standard deviation sigma (host):
+ * 128 when sigma < 0.01, 64 when sigma < 0.1, otherwise 32 (NaN included).
+ */
+int mx_adaptive_block_size(double sigma);
+
+/*
+ * mx_layer_block_size -- block size by layer kind (host): Q/K/V projections 64, FFN gate and
+ * up projections 32, output projection 128; 0 for an unknown kind.
+ */
+typedef enum { MX_LAYER_QKV = 0, MX_LAYER_FFN_GATE_UP = 1, MX_LAYER_OUTPUT = 2 } mx_layer_kind;
+int mx_layer_block_size(mx_layer_kind kind);
+
+/*
  * mx_gemm_workspace_size -- bytes of device workspace mx_gemm needs for this shape and mode
  * (0 when none).  MX_A4 needs room for the quantized activations: m*k/2 code bytes and
  * mx_scale_bytes(m, k, 32, MX_LAYOUT_TILED) scale bytes, each rounded up to 256 bytes.

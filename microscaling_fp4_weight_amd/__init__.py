@@ -60,6 +60,14 @@ def lib() -> ctypes.CDLL:
     L.mx_quant_error_workspace_size.restype = sz
     L.mx_quant_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, i64, vp, vp, sz, vp]
     L.mx_quant_error.restype = i32
+    L.mx_tensor_stats_workspace_size.argtypes = [i64, i64]
+    L.mx_tensor_stats_workspace_size.restype = sz
+    L.mx_tensor_stats.argtypes = [vp, i32, i64, i64, i64, vp, vp, sz, vp]
+    L.mx_tensor_stats.restype = i32
+    L.mx_adaptive_block_size.argtypes = [ctypes.c_double]
+    L.mx_adaptive_block_size.restype = i32
+    L.mx_layer_block_size.argtypes = [i32]
+    L.mx_layer_block_size.restype = i32
     L.mx_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     L.mx_gemm_workspace_size.restype = sz
     L.mx_gemm.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp,
@@ -170,6 +178,33 @@ def mx_quant_error(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 
                               _stream(stream))
     _check(st, "mx_quant_error")
     return out[:7]
+
+
+def mx_tensor_stats(x: torch.Tensor, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Mean, sample standard deviation and max |x| of a rows x k bf16/fp32 GPU tensor, computed
+    on the device; returns a float64 device tensor of 3 values."""
+    rows, k, ld = _rows_ld(x, "x")
+    if out is None:
+        out = torch.zeros(4, dtype=torch.float64, device=x.device)  # 3 used; 16-byte aligned
+    need = int(lib().mx_tensor_stats_workspace_size(rows, k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    st = lib().mx_tensor_stats(_ptr(x), _dtype_code(x.dtype), rows, k, ld, _ptr(out), _ptr(workspace),
+                               workspace.numel(), _stream(stream))
+    _check(st, "mx_tensor_stats")
+    return out[:3]
+
+
+LAYER_KIND = {"qkv": 0, "ffn_gate_up": 1, "output": 2}
+
+
+def mx_adaptive_block_size(sigma: float) -> int:
+    return int(lib().mx_adaptive_block_size(sigma))
+
+
+def mx_layer_block_size(kind: str) -> int:
+    return int(lib().mx_layer_block_size(LAYER_KIND[kind]))
 
 
 def mx_gemm_workspace_size(m: int, n: int, k: int, block: int, mode: str) -> int:

@@ -208,6 +208,54 @@ mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k
     return from_hip(mxk::launch_quant_error(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t mx_tensor_stats_workspace_size(int64_t rows, int64_t k)
+{
+    if (rows <= 0 || k <= 0) return 0;
+    return round256((size_t)mxk::stats_groups(rows, k) * 2 * sizeof(double));
+}
+
+mx_status mx_tensor_stats(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x, double* out,
+                          void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (rows < 0 || k < 0 || ld_x < k) return MX_ERR_INVALID_ARG;
+    if (x_type != MX_F32 && x_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return MX_OK;
+    if (!x || !out) return MX_ERR_INVALID_ARG;
+    const size_t need = mx_tensor_stats_workspace_size(rows, k);
+    if (!workspace || workspace_bytes < need) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(out) || !aligned16(workspace)) return MX_ERR_ALIGNMENT;
+    const int64_t esize = x_type == MX_BF16 ? 2 : 4;
+    const bool vec = (k % 8 == 0) && ((ld_x * esize) % 16 == 0);
+    if (rows * (vec ? k / 8 : k) >= (int64_t(1) << 31)) return MX_ERR_UNSUPPORTED;
+    mxk::StatsArgs a;
+    a.x = x;
+    a.bf16 = x_type == MX_BF16;
+    a.rows = rows;
+    a.k = k;
+    a.ldx = ld_x;
+    a.vec = vec;
+    a.partials = static_cast<double*>(workspace);
+    a.out = out;
+    return from_hip(mxk::launch_tensor_stats(a, static_cast<hipStream_t>(stream)));
+}
+
+int mx_adaptive_block_size(double sigma)
+{
+    if (sigma < 0.01) return 128;
+    if (sigma < 0.1) return 64;
+    return 32;  // also NaN
+}
+
+int mx_layer_block_size(mx_layer_kind kind)
+{
+    switch (kind) {
+        case MX_LAYER_QKV: return 64;
+        case MX_LAYER_FFN_GATE_UP: return 32;
+        case MX_LAYER_OUTPUT: return 128;
+        default: return 0;
+    }
+}
+
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode)
 {
     if (m < 0 || n < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;

@@ -108,7 +108,20 @@ struct ErrArgs {
 constexpr int kErrMaxGroups = 1024;  // workgroups of the error reduction (fixed grid cap)
 int quant_error_groups(int64_t rows, int64_t k, int block);
 
+struct StatsArgs {
+    const void* x;
+    bool bf16;        // element type
+    int64_t rows, k, ldx;
+    bool vec;         // k % 8 == 0 and 16-byte aligned rows: 16-byte loads
+    double* partials; // workspace: 2 doubles per workgroup
+    double* out;      // mean, standard deviation, max |x|
+};
+
+constexpr int kStatsMaxGroups = 1024;  // workgroups of each statistics pass (fixed grid cap)
+int stats_groups(int64_t rows, int64_t k);
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
+hipError_t launch_tensor_stats(const StatsArgs& a, hipStream_t st);
 hipError_t launch_quant_error(const ErrArgs& a, hipStream_t st);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t st);
 hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t st);

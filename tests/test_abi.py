@@ -30,8 +30,10 @@ def declared_functions():
 
 def test_exports_match_header(L):
     names = declared_functions()
-    assert names == ["mx_dequantize", "mx_gemm", "mx_gemm_workspace_size", "mx_quant_error",
-                     "mx_quant_error_workspace_size", "mx_quantize", "mx_scale_bytes", "mx_status_string"]
+    assert names == ["mx_adaptive_block_size", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
+                     "mx_layer_block_size", "mx_quant_error", "mx_quant_error_workspace_size",
+                     "mx_quantize", "mx_scale_bytes", "mx_status_string", "mx_tensor_stats",
+                     "mx_tensor_stats_workspace_size"]
     for n in names:
         assert hasattr(L, n)
     so = os.path.join(ROOT, "microscaling_fp4_weight_amd", "libmx.so")
@@ -166,3 +168,34 @@ def test_quant_error_validation(L):
     assert qe(out=FAKE + 8) == ALIGN
     assert qe(x=FAKE + 2) == ALIGN
     assert qe(rows=0, x=None, out=None, work=None, wbytes=0) == OK  # empty: nothing launched
+
+
+def test_block_size_policy_matches_oracle(L):
+    import oracle
+    for sigma in (0.0, 0.005, 0.00999999, 0.01, 0.02, 0.0999999, 0.1, 0.118, 2.0, float("nan"),
+                  float("inf")):
+        assert L.mx_adaptive_block_size(sigma) == oracle.adaptive_block_size(sigma), sigma
+    for i, kind in enumerate(("qkv", "ffn_gate_up", "output")):
+        assert L.mx_layer_block_size(i) == oracle.layer_block_size(kind)
+    assert L.mx_layer_block_size(3) == 0 and L.mx_layer_block_size(-1) == 0
+
+
+def test_tensor_stats_validation(L):
+    ws = L.mx_tensor_stats_workspace_size
+    assert ws(4, 64) == 256                   # one workgroup: 2 doubles, rounded up
+    assert ws(4096, 11008) == 1024 * 2 * 8    # capped grid
+    assert ws(0, 64) == 0
+
+    def ts(x=FAKE, xt=BF16, rows=4, k=64, ldx=64, out=FAKE, work=FAKE, wbytes=256):
+        return L.mx_tensor_stats(x, xt, rows, k, ldx, out, work, wbytes, None)
+
+    assert ts(ldx=63) == INVALID
+    assert ts(rows=-1) == INVALID
+    assert ts(xt=5) == INVALID
+    assert ts(out=None) == INVALID
+    assert ts(work=None) == INVALID
+    assert ts(wbytes=255) == INVALID
+    assert ts(x=FAKE + 4) == ALIGN
+    assert ts(out=FAKE + 8) == ALIGN
+    assert ts(rows=0, x=None, out=None, work=None, wbytes=0) == OK
+    assert ts(rows=1 << 20, k=1 << 15, ldx=1 << 15, wbytes=1 << 20) == UNSUPPORTED
