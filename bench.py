@@ -197,6 +197,7 @@ def main():
                 "avg_launch_us": round(dom_avg_ms * 1e3, 3)}
 
     error_split = measure_error_split(mx, L, torch, inputs, configs, dev, stream)
+    block_policy = measure_block_policy(mx, torch, inputs, error_split, dev, stream)
 
     # free the sweep buffers before the GEMM rows
     del inputs, codes, scales, deq_out, qcalls, dcalls
@@ -219,6 +220,7 @@ def main():
         "cpu_baseline": cpu,
         "per_config": per_config,
         "error_split": error_split,
+        "block_policy": block_policy,
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
@@ -288,6 +290,7 @@ def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
         per[f"s{SIGMAS[si]}.B{b}.{f}"] = {
             "us": round(t * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
             "mse_elem": float(vals[i, 0]), "mse_max": float(vals[i, 1]), "mse_zero": float(vals[i, 2]),
+            "mse_total": float(vals[i, 3]),
             "flushed_blocks": int(vals[i, 5])}
     ft = sorted(e0.elapsed_time(e1) for e0, e1 in fevs)[2]
     fgbs = 4 * n / (ft * 1e-3) / 1e9
@@ -299,6 +302,43 @@ def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
             "fake_quant.s0.02.B32.e4m3": {"us": round(ft * 1e3, 2), "bytes": 4 * n, "GB/s": round(fgbs, 1),
                                           "frac_hbm": round(fgbs * 1e9 / PEAK_HBM, 3)},
             "per_config": per}
+
+
+def measure_block_policy(mx, torch, inputs, error_split, dev, stream):
+    """The sigma-driven block size on the sweep tensors: the standard deviation measured on the
+    device (mx_tensor_stats, two fp64 passes; timed), the block size the policy picks from it,
+    and that block's total MSE next to block 32's and the sweep's best, per scale format (the
+    MSEs are the device error split's)."""
+    n = C2_ROWS * C2_K
+    out = torch.zeros(4, dtype=torch.float64, device=dev)
+    work = torch.empty(mx.mx_tensor_stats_workspace_size(C2_ROWS, C2_K), dtype=torch.uint8, device=dev)
+    per = error_split["per_config"]
+    res = {}
+    times = []
+    for si, sigma in enumerate(SIGMAS):
+        x = inputs[2 * si]
+        mx.mx_tensor_stats(x, out=out, workspace=work, stream=stream)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        st = mx.mx_tensor_stats(x, out=out, workspace=work, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        mean, std, amax = (float(v) for v in st.cpu().numpy())
+        b = mx.mx_adaptive_block_size(std)
+        ent = {"std": std, "mean": mean, "absmax": amax, "policy_block": b}
+        for f in FMTS:
+            tot = {bb: per[f"s{sigma}.B{bb}.{f}"]["mse_total"] for bb in BLOCKS}
+            best = min(tot, key=tot.get)
+            ent[f] = {"mse_policy": tot[b], "mse_b32": tot[32], "best_block": best, "mse_best": tot[best]}
+        res[f"s{sigma}"] = ent
+    t = sorted(times)[len(times) // 2]
+    res["stats_kernel"] = {"us": round(t * 1e3, 2), "bytes": 2 * 2 * n,
+                           "GB/s": round(4 * n / (t * 1e-3) / 1e9, 1)}
+    res["layer_blocks"] = {k: mx.mx_layer_block_size(k) for k in ("qkv", "ffn_gate_up", "output")}
+    log(f"block policy: " + ", ".join(f"s{sg}: std {res[f's{sg}']['std']:.4f} -> B{res[f's{sg}']['policy_block']}"
+                                       for sg in SIGMAS) + f"; stats {t * 1e3:.1f} us")
+    return res
 
 
 COPY_BYTES = 256 << 20  # calibration copy: 256 MiB read + 256 MiB written per launch

@@ -180,6 +180,10 @@ def mx_quant_error(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 
     return out[:7]
 
 
+def mx_tensor_stats_workspace_size(rows: int, k: int) -> int:
+    return int(lib().mx_tensor_stats_workspace_size(rows, k))
+
+
 def mx_tensor_stats(x: torch.Tensor, out: torch.Tensor | None = None,
                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Mean, sample standard deviation and max |x| of a rows x k bf16/fp32 GPU tensor, computed
@@ -187,7 +191,7 @@ def mx_tensor_stats(x: torch.Tensor, out: torch.Tensor | None = None,
     rows, k, ld = _rows_ld(x, "x")
     if out is None:
         out = torch.zeros(4, dtype=torch.float64, device=x.device)  # 3 used; 16-byte aligned
-    need = int(lib().mx_tensor_stats_workspace_size(rows, k))
+    need = mx_tensor_stats_workspace_size(rows, k)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     st = lib().mx_tensor_stats(_ptr(x), _dtype_code(x.dtype), rows, k, ld, _ptr(out), _ptr(workspace),
