@@ -23,16 +23,28 @@ namespace mxk {
 
 namespace a4 {
 
-constexpr int BM = 256, BN = 256, BK = 256, STAGES = 2;
+constexpr int BM = 256, BK = 256, STAGES = 2;
 constexpr int WAVES = 8, THREADS = 64 * WAVES;
-constexpr int MI = 4, NJ = 2;                      // per wave: 4 x 2 tiles of 32 x 32 (128 m x 64 n)
+constexpr int MI = 4;                              // per wave: 4 x NJ tiles of 32 x 32 (128 m x 32 NJ n)
 constexpr int ROWB = BK / 2;                       // code bytes per row per stage (128)
 constexpr int SROW = BK / 32;                      // scale bytes per row per stage (8)
-constexpr int CODE_BYTES = BM * ROWB;              // 32 KB per operand per stage
-constexpr int SCALE_BYTES = BM * SROW;             // 2 KB per operand per stage
-constexpr int STAGE_BYTES = 2 * CODE_BYTES + 2 * SCALE_BYTES;
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;    // 139264 (of 160 KB)
-constexpr int LOADS_PER_STAGE = 10;                // per wave: 4 + 4 code loads, 1 + 1 scale loads
+constexpr int CODE_BYTES = BM * ROWB;              // 32 KB of activation codes per stage
+constexpr int SCALE_BYTES = BM * SROW;             // 2 KB of activation scales per stage
+
+// Weight-side sizes for a tile 128 NJ wide: NJ = 2 is the full 256 x 256 tile, NJ = 1 the
+// 256 x 128 half tile that runs the last, partial round of tiles.
+template <int NJ>
+struct Cfg {
+    static constexpr int BN = 128 * NJ;
+    static constexpr int WCODE = BN * ROWB;        // weight codes per stage
+    static constexpr int WSCALE = BN * SROW;       // weight scales per stage
+    static constexpr int SCALE_OFF = CODE_BYTES + WCODE;
+    static constexpr int DUMMY = NJ == 1 ? 256 : 0;  // sink of the idle waves' scale loads
+    static constexpr int STAGE_BYTES = SCALE_OFF + SCALE_BYTES + WSCALE + DUMMY;
+    static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 139264 (NJ 2) or 104960 (NJ 1)
+    static constexpr int LOADS_PER_STAGE = 4 + 2 * NJ + 2;  // codes X, codes W, two scale loads
+};
+constexpr int BN = Cfg<2>::BN;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -46,10 +58,15 @@ __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) { return c
 // tile, stage) block of the tiled scale layout, so tiled scales arrive with one contiguous
 // 256-byte load per wave and operand; row-major scales take one dword per lane from 32 rows
 // per load.  The stage index s is also the block index in the tiled layout.
-template <bool W_TILED>
+// A half tile (NJ = 1) loads 128 weight rows: two code loads per wave, and its 1 KB of weight
+// scales (the half `whalf` of each tiled 2 KB block) by waves 0..3; waves 4..7 issue their
+// scale load into a sink region, so that every wave counts the same loads per stage.
+template <int NJ, bool W_TILED>
 __device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uint32_t s,
-                                            rsrc_t ac, rsrc_t bc, rsrc_t as, rsrc_t bs, uint32_t K)
+                                            rsrc_t ac, rsrc_t bc, rsrc_t as, rsrc_t bs, uint32_t K,
+                                            uint32_t whalf)
 {
+    using C = Cfg<NJ>;
     const uint32_t rowb = K / 2, srow = K / 32, k0 = s * BK;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -59,21 +76,33 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uin
         const uint32_t kk = k0 + 32 * c;
         const uint32_t off = kk < K ? row * rowb + kk / 2 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ac, (lds_void*)(st + grp * 1024), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2 * NJ; ++q) {
+        const uint32_t grp = (uint32_t)(wave * 2 * NJ + q);      // 8-row group, 0..16 NJ - 1
+        const uint32_t row = grp * 8 + (lane >> 3);
+        const uint32_t c = swz(row, lane & 7);
+        const uint32_t kk = k0 + 32 * c;
+        const uint32_t off = kk < K ? row * rowb + kk / 2 : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(bc, (lds_void*)(st + CODE_BYTES + grp * 1024), 16, off, 0, 0, 0);
     }
     const uint32_t p = (uint32_t)wave * 64 + lane;
     const uint32_t toff = s * 2048u + 4 * p;                     // stages past the end are out of range
-    uint32_t soff = toff;
+    // weight scales: dword pw of this tile's (half) block; idle waves (NJ = 1) use the sink
+    const bool wact = NJ == 2 || wave < 4;
+    const uint32_t pw = wact ? p : (uint32_t)lane;
+    uint32_t soff = s * 2048u + 1024u * whalf + 4 * pw;
     if constexpr (!W_TILED) {
-        const uint32_t row = (p >> 8) * 128 + ((p >> 1) & 3) * 32 + ((p >> 3) & 31);
-        const uint32_t kk = k0 + 128 * (p & 1);
+        const uint32_t row = (pw >> 8) * 128 + ((pw >> 1) & 3) * 32 + ((pw >> 3) & 31);
+        const uint32_t kk = k0 + 128 * (pw & 1);
         // beyond k: set the top bit (out of every range) arithmetically rather than by a
         // select, which the compiler would otherwise turn into a branch around the load
         const uint32_t beyond = (uint32_t)((int32_t)(K - 1 - kk) >> 31);
         soff = (row * srow + kk / 32) | (beyond & kOOB);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_void*)(st + 2 * CODE_BYTES + wave * 256), 4, toff, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_void*)(st + 2 * CODE_BYTES + SCALE_BYTES + wave * 256), 4, soff, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(as, (lds_void*)(st + C::SCALE_OFF + wave * 256), 4, toff, 0, 0, 0);
+    uint8_t* wdst = wact ? st + C::SCALE_OFF + SCALE_BYTES + wave * 256 : st + C::SCALE_OFF + SCALE_BYTES + C::WSCALE;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(bs, (lds_void*)wdst, 4, soff, 0, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
@@ -93,7 +122,7 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 
 // Scale dwords of a lane: A rows i*32 + r (i = 0..3) as a[0] = {i0 dword 0, i0 dword 1,
 // i1 dword 0, i1 dword 1}, a[1] the same for i = 2, 3; B rows jn*32 + r (jn = 0, 1) as b.
-struct Scales { u32x4 a[2]; u32x4 b; };
+struct Scales { u32x4 a[2]; u32x4 b; };  // b: for NJ = 1 only the first two dwords are used
 
 __device__ __forceinline__ int pick_byte(const u32x4 v, int odd, int j, uint32_t h)
 {
@@ -106,7 +135,7 @@ __device__ __forceinline__ int pick_byte(const u32x4 v, int odd, int j, uint32_t
 // The weight fragment is the MFMA's A operand and the activation fragment its B operand, so
 // each tile is computed transposed (rows n, columns m): a lane then holds four consecutive n
 // of one output row per group, which the epilogue stages in LDS as one 8- or 16-byte write.
-template <int J>
+template <int J, int NJ>
 __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NJ], const u32x4 (&fa)[MI], const u32x4 (&fb)[NJ],
                                           const Scales& sc, uint32_t h)
 {
@@ -129,7 +158,7 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NJ], const u32x4 (&f
 
 // Fragment reads of k-step J from a stage buffer: rows 32 further are 4096 bytes apart and
 // share the chunk permutation, so one base offset per operand serves all of them.
-template <int J>
+template <int J, int NJ>
 __device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t baseA, uint32_t baseB, uint32_t perm,
                                            u32x4 (&fa)[MI], u32x4 (&fb)[NJ])
 {
@@ -140,11 +169,17 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, uint32_t baseA, ui
     for (int jn = 0; jn < NJ; ++jn) fb[jn] = *reinterpret_cast<const u32x4*>(st + CODE_BYTES + baseB + chunk + jn * 32 * ROWB);
 }
 
+template <int NJ>
 __device__ __forceinline__ void read_scales(const uint8_t* st, uint32_t offSA, uint32_t offSB, Scales& sc)
 {
     sc.a[0] = *reinterpret_cast<const u32x4*>(st + offSA);
     sc.a[1] = *reinterpret_cast<const u32x4*>(st + offSA + 16);
-    sc.b = *reinterpret_cast<const u32x4*>(st + offSB);
+    if constexpr (NJ == 2) {
+        sc.b = *reinterpret_cast<const u32x4*>(st + offSB);
+    } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(st + offSB);
+        sc.b = u32x4{v.x, v.y, 0u, 0u};
+    }
 }
 
 // scheduling: within a k-step, one MFMA, then the fragment reads for the next k-step, then
@@ -154,28 +189,38 @@ __device__ __forceinline__ void read_scales(const uint8_t* st, uint32_t offSA, u
     __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, ID);      \
     __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - 1, ID)
 
-template <bool OUT_BF16, bool W_TILED>
-__global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
+template <bool OUT_BF16, bool W_TILED, int NJ>
+__global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a, uint32_t tile_base)
 {
+    using C = Cfg<NJ>;
+    constexpr int BN = C::BN;
+    constexpr int STAGE_BYTES = C::STAGE_BYTES;
+    constexpr int LOADS_PER_STAGE = C::LOADS_PER_STAGE;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     // the wave index is uniform across the wave; saying so keeps LDS-DMA destinations scalar
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const uint32_t K = (uint32_t)a.k;
 
-    // tile mapping: with the n-tile count a multiple of 8, XCD x (= block % 8) takes n-tiles
-    // x, x+8, ... and, for each, every m-tile in turn
-    const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + BN - 1) / BN);
+    // tile mapping over full 256 x 256 tiles: with the n-tile count a multiple of 8, XCD x
+    // (= tile % 8) takes n-tiles x, x+8, ... and, for each, every m-tile in turn.  A half-tile
+    // launch (NJ = 1) covers full tiles tile_base.. with two workgroups each.
+    const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + 255) / 256);
+    const uint32_t tile = tile_base + (NJ == 2 ? blockIdx.x : blockIdx.x >> 1);
+    const uint32_t whalf = NJ == 2 ? 0u : (blockIdx.x & 1u);
     uint32_t mt, nt;
     if ((NT & 7) == 0) {
-        const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3;
+        const uint32_t x = tile & 7, local = tile >> 3;
         mt = local % MT;
         nt = (local / MT) * 8 + x;
     } else {
-        mt = blockIdx.x % MT;
-        nt = blockIdx.x / MT;
+        mt = tile % MT;
+        nt = tile / MT;
     }
-    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * 256 + 128 * whalf;
+    // the second half of a last n-tile with at most 128 columns holds no column at all: the
+    // whole workgroup leaves (uniformly) before it computes any buffer range
+    if (n0 >= a.n) return;
     const uint32_t mrows = (uint32_t)(a.m - m0 < BM ? a.m - m0 : BM);
     const uint32_t nrows = (uint32_t)(a.n - n0 < BN ? a.n - n0 : BN);
     const rsrc_t ac = make_rsrc(a.xq_codes + m0 * (a.k / 2), mrows * (K / 2));
@@ -201,57 +246,61 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
     // after next.  Stages past the end of k load as zeros (their offsets are out of range),
     // so every iteration has the same shape.
     const int S = (int)((K + BK - 1) / BK);
-    issue_stage<W_TILED>(lds, wave, lane, 0, ac, bc, as, bs, K);
-    issue_stage<W_TILED>(lds + STAGE_BYTES, wave, lane, 1, ac, bc, as, bs, K);
+    issue_stage<NJ, W_TILED>(lds, wave, lane, 0, ac, bc, as, bs, K, whalf);
+    issue_stage<NJ, W_TILED>(lds + STAGE_BYTES, wave, lane, 1, ac, bc, as, bs, K, whalf);
 
     const uint32_t r32 = lane & 31, h = lane >> 5;
     const uint32_t perm = h ^ ((r32 >> 1) & 7u);              // chunk (2j + h) -> slot (2j) ^ perm
     const uint32_t baseA = (wm * 128 + r32) * ROWB;
-    const uint32_t baseB = (wn * 64 + r32) * ROWB;
-    const uint32_t offSA = 2 * CODE_BYTES + (wm * 256 + r32 * 8) * 4;
-    const uint32_t offSB = 2 * CODE_BYTES + SCALE_BYTES + ((wn >> 1) * 256 + r32 * 8 + 4 * (wn & 1)) * 4;
+    const uint32_t baseB = (wn * 32 * NJ + r32) * ROWB;
+    const uint32_t offSA = C::SCALE_OFF + (wm * 256 + r32 * 8) * 4;
+    // weight scale dwords of rows wn*32NJ + jn*32 + r: NJ = 2 four from p = 256 (wn/2) + 8 r +
+    // 4 (wn%2); NJ = 1 two from p = 8 r + 2 wn
+    const uint32_t offSB = C::SCALE_OFF + SCALE_BYTES +
+                           (NJ == 2 ? ((wn >> 1) * 256 + r32 * 8 + 4 * (wn & 1)) : (r32 * 8 + 2 * wn)) * 4;
 
     u32x4 f0a[MI], f0b[NJ], f1a[MI], f1b[NJ];
     Scales sc;
     wait_vmcnt<LOADS_PER_STAGE>();
     barrier_only();
-    read_frags<0>(lds, baseA, baseB, perm, f0a, f0b);
-    read_scales(lds, offSA, offSB, sc);
+    read_frags<0, NJ>(lds, baseA, baseB, perm, f0a, f0b);
+    read_scales<NJ>(lds, offSA, offSB, sc);
 
     uint32_t cur = 0;  // byte offset of stage s's buffer
     for (int s = 0; s < S; ++s) {
         const uint32_t nxt = cur ^ (uint32_t)STAGE_BYTES;
-        read_frags<1>(lds + cur, baseA, baseB, perm, f1a, f1b);
-        mfma_step<0>(acc, f0a, f0b, sc, h);
+        read_frags<1, NJ>(lds + cur, baseA, baseB, perm, f1a, f1b);
+        mfma_step<0, NJ>(acc, f0a, f0b, sc, h);
         A4_SCHED_STEP(0);
         __builtin_amdgcn_sched_barrier(0);
-        read_frags<2>(lds + cur, baseA, baseB, perm, f0a, f0b);
-        mfma_step<1>(acc, f1a, f1b, sc, h);
+        read_frags<2, NJ>(lds + cur, baseA, baseB, perm, f0a, f0b);
+        mfma_step<1, NJ>(acc, f1a, f1b, sc, h);
         A4_SCHED_STEP(1);
         __builtin_amdgcn_sched_barrier(0);
-        read_frags<3>(lds + cur, baseA, baseB, perm, f1a, f1b);
-        mfma_step<2>(acc, f0a, f0b, sc, h);
+        read_frags<3, NJ>(lds + cur, baseA, baseB, perm, f1a, f1b);
+        mfma_step<2, NJ>(acc, f0a, f0b, sc, h);
         A4_SCHED_STEP(2);
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm0();
         wait_vmcnt<0>();
         barrier_only();
         __builtin_amdgcn_sched_barrier(0);
-        issue_stage<W_TILED>(lds + cur, wave, lane, (uint32_t)(s + STAGES), ac, bc, as, bs, K);
+        issue_stage<NJ, W_TILED>(lds + cur, wave, lane, (uint32_t)(s + STAGES), ac, bc, as, bs, K, whalf);
         Scales sc_n;
-        read_frags<0>(lds + nxt, baseA, baseB, perm, f0a, f0b);
-        read_scales(lds + nxt, offSA, offSB, sc_n);
-        mfma_step<3>(acc, f1a, f1b, sc, h);
-        // next stage's first fragments and scales first, then the ten stage loads spread
-        // between MFMAs so that the matrix pipe stays busy while they are issued
+        read_frags<0, NJ>(lds + nxt, baseA, baseB, perm, f0a, f0b);
+        read_scales<NJ>(lds + nxt, offSA, offSB, sc_n);
+        mfma_step<3, NJ>(acc, f1a, f1b, sc, h);
+        // next stage's first fragments and scales first, then the stage loads spread between
+        // MFMAs so that the matrix pipe stays busy while they are issued
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
         __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ + 3, 3);
+        constexpr int SPREAD = LOADS_PER_STAGE / 2 < MI * NJ - 1 ? LOADS_PER_STAGE / 2 : MI * NJ - 1;
 #pragma unroll
-        for (int g = 0; g < 5; ++g) {
+        for (int g = 0; g < SPREAD; ++g) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
             __builtin_amdgcn_sched_group_barrier(0x020, 2, 3);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - 6, 3);
+        if constexpr (MI * NJ - 1 - SPREAD > 0) __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - 1 - SPREAD, 3);
         // keep the next stage's reads in this iteration (not sunk into the next one)
         asm volatile("" ::: "memory");
         sc = sc_n;
@@ -275,12 +324,12 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
     if (vec) {
         constexpr int PASSES = OUT_BF16 ? 1 : 2;             // 128 or 64 rows per pass
         constexpr int IPP = MI / PASSES;                      // 32-row blocks per pass
-        constexpr uint32_t RB = 32 * NJ * ESZ;                // bytes of a wave row (64 columns)
+        constexpr uint32_t RB = 32 * NJ * ESZ;                // bytes of a wave row (32 NJ columns)
         constexpr uint32_t PITCH = RB + (OUT_BF16 ? 8 : 16);
         constexpr uint32_t CPR = RB / 16;                     // chunks per row (8 or 16)
         constexpr uint32_t RPI = 64 / CPR;                    // rows per store instruction
         constexpr uint32_t PASS_ROWS = 32 * IPP;
-        static_assert(WAVES * PASS_ROWS * PITCH <= (uint32_t)LDS_BYTES, "epilogue staging exceeds LDS");
+        static_assert(WAVES * PASS_ROWS * PITCH <= (uint32_t)C::LDS_BYTES, "epilogue staging exceeds LDS");
         uint8_t* stg = lds + wave * PASS_ROWS * PITCH;
         barrier_only();  // every wave is done reading the stage buffers
 #pragma unroll
@@ -307,7 +356,7 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
             for (uint32_t t = 0; t < PASS_ROWS / RPI; ++t) {
                 const uint32_t row = t * RPI + lane / CPR, chunk = lane % CPR;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * PITCH + chunk * 16);
-                const uint32_t mm = wm * 128 + pass * PASS_ROWS + row, nn = wn * 64 + chunk * CE;
+                const uint32_t mm = wm * 128 + pass * PASS_ROWS + row, nn = wn * 32 * NJ + chunk * CE;
                 const uint32_t off = (mm < mlim && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
                 bstore128(yr, off, v);
             }
@@ -321,7 +370,7 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
             for (int jn = 0; jn < NJ; ++jn)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const uint32_t nn = wn * 64 + jn * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+                    const uint32_t nn = wn * 32 * NJ + jn * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
                     const uint32_t off = (mok && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
                     const float v = acc[i][jn][e] * a.g;
                     if constexpr (OUT_BF16) bstore16(yr, off, __builtin_bit_cast(uint16_t, (__bf16)v));
@@ -333,17 +382,36 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a)
 
 }  // namespace a4
 
-template <bool OUT_BF16, bool W_TILED>
-static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st)
+template <bool OUT_BF16, bool W_TILED, int NJ>
+static hipError_t launch_part(const GemmArgs& a, uint32_t tile_base, unsigned groups, hipStream_t st)
 {
     // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
     // (thread-safe function-local static initialisation)
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)a4::gemm_a4_kernel<OUT_BF16, W_TILED>, hipFuncAttributeMaxDynamicSharedMemorySize, a4::LDS_BYTES);
+    static const hipError_t attr = hipFuncSetAttribute((const void*)a4::gemm_a4_kernel<OUT_BF16, W_TILED, NJ>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       a4::Cfg<NJ>::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    const unsigned tiles = (unsigned)(((a.m + a4::BM - 1) / a4::BM) * ((a.n + a4::BN - 1) / a4::BN));
-    hipLaunchKernelGGL((a4::gemm_a4_kernel<OUT_BF16, W_TILED>), dim3(tiles), dim3(a4::THREADS), a4::LDS_BYTES, st, a);
+    hipLaunchKernelGGL((a4::gemm_a4_kernel<OUT_BF16, W_TILED, NJ>), dim3(groups), dim3(a4::THREADS),
+                       a4::Cfg<NJ>::LDS_BYTES, st, a, tile_base);
     return hipGetLastError();
+}
+
+// Full 256 x 256 tiles run in whole rounds of kCUs workgroups; when the last round would be at
+// most half full, its tiles run instead as twice as many 256 x 128 half tiles, which fill it.
+constexpr unsigned kCUs = 256;
+
+template <bool OUT_BF16, bool W_TILED>
+static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st)
+{
+    const unsigned tiles = (unsigned)(((a.m + a4::BM - 1) / a4::BM) * ((a.n + 255) / 256));
+    const unsigned rem = tiles % kCUs;
+    const unsigned full = (rem != 0 && rem <= kCUs / 2) ? tiles - rem : tiles;
+    if (full) {
+        const hipError_t e = launch_part<OUT_BF16, W_TILED, 2>(a, 0u, full, st);
+        if (e != hipSuccess) return e;
+    }
+    if (full < tiles) return launch_part<OUT_BF16, W_TILED, 1>(a, full, 2 * (tiles - full), st);
+    return hipSuccess;
 }
 
 bool a4_uses_mfma(const GemmArgs& a)

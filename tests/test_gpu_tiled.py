@@ -90,3 +90,30 @@ def test_gemm_tiled_rejected_where_unsupported():
     with pytest.raises(mx.MXError) as e:
         mx.mx_gemm(xd, ct, st, 32, "e8m0", 1.0, "a16", layout="tiled")
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("mnk", [(256, 66560, 256), (512, 16640, 256), (300, 33000, 128)])
+def test_gemm_a4_full_and_half_tiles(layout, mnk):
+    """Shapes whose 256 x 256 tile count leaves a partial last round over the 256 CUs: 260
+    tiles (256 full + 4 run as 8 half tiles), 130 tiles (all full: the round is more than half
+    used), 258 tiles with a ragged last n-tile (2 run as half tiles).  Weights quantized on
+    the GPU, their sampled rows checked against the oracle; outputs sampled in every kind of
+    tile, including the half tiles at the end of n."""
+    m, n, k = mnk
+    x = synth.normal((m, k), "bf16", f"fh.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", f"fh.w.{n}", 0.02, 0.01, 20.0)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize(wd, 32, "e8m0", layout=layout)
+    del wd
+    cols = np.array([0, 5, 1000, n // 2, n - 300, n - 129, n - 128, n - 1])
+    rows = np.array([0, 1, m // 2, m - 1])
+    rc, rs = oracle.quantize(w[cols], 32, "e8m0", 1.0)
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    xd = bf16_dev(x)
+    yref, aref = oracle.gemm(x[rows], rc, rs, 32, "e8m0", 1.0, "a4")
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm(xd, cd, sd, 32, "e8m0", 1.0, "a4", out_dtype=dt, layout=layout)
+        torch.cuda.synchronize()
+        got = to_host_bits(y.float())[rows][:, cols]
+        assert_gemm_close(got, yref, aref, dt == torch.bfloat16, f"a4 {layout} {mnk} {dt}")
