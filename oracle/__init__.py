@@ -68,6 +68,22 @@ def _load():
     lib.ox_scale_bytes.restype = None
     lib.ox_elem_codes.argtypes = [vp, i64, dbl, dbl, vp]
     lib.ox_elem_codes.restype = None
+    lib.ox_e4m3_value.argtypes = [u32]
+    lib.ox_e4m3_value.restype = dbl
+    lib.ox_scale_byte_fp8.argtypes = [dbl, dbl, i32]
+    lib.ox_scale_byte_fp8.restype = u32
+    lib.ox_elem_code_fp8.argtypes = [dbl, dbl, dbl]
+    lib.ox_elem_code_fp8.restype = u32
+    lib.ox_quantize_fp8.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, vp]
+    lib.ox_quantize_fp8.restype = i32
+    lib.ox_dequantize_fp8.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, i32, i64]
+    lib.ox_dequantize_fp8.restype = i32
+    lib.ox_gemm_fp8.argtypes = [vp, i64, i64, i64, vp, vp, i64, i32, i32, f32, vp, i64, vp, i64, vp, vp]
+    lib.ox_gemm_fp8.restype = i32
+    lib.ox_scale_bytes_fp8.argtypes = [vp, i64, dbl, i32, vp]
+    lib.ox_scale_bytes_fp8.restype = None
+    lib.ox_elem_codes_fp8.argtypes = [vp, i64, dbl, dbl, vp]
+    lib.ox_elem_codes_fp8.restype = None
     _lib = lib
     return lib
 
@@ -212,3 +228,87 @@ LAYER_BLOCK = {"qkv": 64, "ffn_gate_up": 32, "output": 128}  # section 5.1 item 
 def layer_block_size(kind: str) -> int:
     """Section 5.1 item 1: Q/K/V projections 64, FFN gate/up 32, output projection 128."""
     return LAYER_BLOCK[kind]
+
+
+
+# ----------------------------------------------------------------------------------------
+# FP8 weight fallback (hotelren.com/news/2192771, article "量化技术演进与微缩量化原理",
+# section 5.3 item 1: weights with sigma < 1e-4 are lost to FP4 and go to FP8 instead;
+# section 6 item 1: key layers stay in FP8).  E4M3 elements (largest magnitude 448) in the
+# same blocks under the same scale formats; the scale rule divides by 448 instead of 6.
+# ----------------------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return _load().ox_e4m3_value(code)
+
+
+def scale_byte_fp8(a: float, g: float, fmt: str) -> int:
+    return _load().ox_scale_byte_fp8(a, g, FMT[fmt])
+
+
+def elem_code_fp8(x: float, s: float, g: float = 1.0) -> int:
+    return _load().ox_elem_code_fp8(x, s, g)
+
+
+def scale_bytes_fp8(a: np.ndarray, g: float, fmt: str) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    out = np.empty(a.size, dtype=np.uint8)
+    _load().ox_scale_bytes_fp8(a.ctypes.data, a.size, g, FMT[fmt], out.ctypes.data)
+    return out.reshape(a.shape)
+
+
+def elem_codes_fp8(x: np.ndarray, s: float, g: float = 1.0) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.size, dtype=np.uint8)
+    _load().ox_elem_codes_fp8(x.ctypes.data, x.size, s, g, out.ctypes.data)
+    return out.reshape(x.shape)
+
+
+def quantize_fp8(x: np.ndarray, block: int, fmt: str, g: float = 1.0):
+    """x: rows x k float32 or bf16 bits -> (codes rows x k uint8, scales rows x k/block uint8)."""
+    x = np.ascontiguousarray(x)
+    rows, k = x.shape
+    codes = np.empty((rows, k), dtype=np.uint8)
+    scales = np.empty((rows, k // block), dtype=np.uint8)
+    rc = _load().ox_quantize_fp8(x.ctypes.data, DTYPE[_dtype_of(x)], rows, k, k, block, FMT[fmt],
+                                 g, codes.ctypes.data, scales.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle quantize_fp8: bad arguments")
+    return codes, scales
+
+
+def dequantize_fp8(codes: np.ndarray, scales: np.ndarray, block: int, fmt: str, g: float = 1.0,
+                   out: str = "f32") -> np.ndarray:
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    rows, k = codes.shape
+    y = np.empty((rows, k), dtype=np.float32 if out == "f32" else np.uint16)
+    rc = _load().ox_dequantize_fp8(codes.ctypes.data, scales.ctypes.data, rows, k, block, FMT[fmt],
+                                   g, y.ctypes.data, DTYPE[out], k)
+    if rc != 0:
+        raise ValueError("oracle dequantize_fp8: bad arguments")
+    return y
+
+
+def gemm_fp8(x_bf16: np.ndarray, wcodes: np.ndarray, wscales: np.ndarray, block: int, fmt: str,
+             g: float = 1.0, mrows=None, ncols=None):
+    """Y = X . dequant(W8)^T in fp64 and A = sum |x w| (bf16 X), for the selected rows/columns."""
+    x = np.ascontiguousarray(x_bf16)
+    m, k = x.shape
+    n = wcodes.shape[0]
+    mr = np.arange(m, dtype=np.int64) if mrows is None else np.ascontiguousarray(mrows, dtype=np.int64)
+    nc = np.arange(n, dtype=np.int64) if ncols is None else np.ascontiguousarray(ncols, dtype=np.int64)
+    wc = np.ascontiguousarray(wcodes)
+    ws = np.ascontiguousarray(wscales)
+    y = np.empty((mr.size, nc.size), dtype=np.float64)
+    a = np.empty_like(y)
+    rc = _load().ox_gemm_fp8(x.ctypes.data, m, k, k, wc.ctypes.data, ws.ctypes.data, n, block, FMT[fmt],
+                             g, mr.ctypes.data, mr.size, nc.ctypes.data, nc.size, y.ctypes.data, a.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle gemm_fp8: bad arguments")
+    return y, a
+
+
+def use_fp8(sigma: float) -> bool:
+    """Section 5.3 item 1: a weight tensor with sigma < 1e-4 takes the FP8 fallback."""
+    return sigma < 1e-4

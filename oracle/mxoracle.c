@@ -388,3 +388,130 @@ void ox_elem_codes(const double* x, int64_t n, double s, double g, uint8_t* out)
     int64_t i;
     for (i = 0; i < n; ++i) out[i] = (uint8_t)ox_elem_code(x[i], s, g);
 }
+
+/* ------------------------------------------------------------------------ */
+/* FP8 weight fallback ([MXS] section 5.3 item 1: a layer whose weights have  */
+/* sigma < 1e-4 loses everything to FP4; the remedy named there is FP8; and   */
+/* section 6 item 1: key layers kept in FP8).  Elements are E4M3 (the OCP     */
+/* E4M3FN byte, largest magnitude 448) in the same blocks and under the same  */
+/* three scale formats; 448 takes the place of 6 in the scale rule.           */
+/* ------------------------------------------------------------------------ */
+
+/* Decoded E4M3 element byte, sign included (NaN for 0x7F / 0xFF). */
+double ox_e4m3_value(unsigned code)
+{
+    return ox_scale_value(code, OX_E4M3);
+}
+
+/* Block scale: the scale-format value nearest to the exact real a / (448 g). */
+unsigned ox_scale_byte_fp8(double a, double g, int fmt)
+{
+    build_tables();
+    if (fmt < 0 || fmt > 2) abort();
+    return g_scale[fmt].code[nearest(&g_scale[fmt], fabs(a), exact_mul(448.0, g), fmt == OX_E8M0)];
+}
+
+/* Element byte: the E4M3 value nearest to |x| / (s g), clipped at 448, ties
+ * to the even code, with the sign bit of x; a zero scale flushes to +-0. */
+unsigned ox_elem_code_fp8(double x, double s, double g)
+{
+    unsigned sign = signbit(x) ? 0x80u : 0u;
+    build_tables();
+    if (s == 0.0) return sign;
+    return sign | g_scale[OX_E4M3].code[nearest(&g_scale[OX_E4M3], fabs(x), exact_mul(s, g), 0)];
+}
+
+int ox_quantize_fp8(const void* x, int xtype, int64_t rows, int64_t k, int64_t ldx,
+                    int block, int fmt, float g, uint8_t* codes, uint8_t* scales)
+{
+    int64_t r, b, i;
+    const int64_t nb = (block > 0) ? k / block : 0;
+    if (!x || !codes || !scales || rows < 0 || k < 0 || ldx < k || !valid_block(block) ||
+        k % block != 0 || fmt < 0 || fmt > 2 || !(g > 0.0f) || isinf(g))
+        return -1;
+    for (r = 0; r < rows; ++r)
+        for (b = 0; b < nb; ++b) {
+            const int64_t base = r * ldx + b * block;
+            double a = 0.0, s;
+            unsigned sb;
+            for (i = 0; i < block; ++i) {
+                double v = fabs(load_elem(x, xtype, base + i));
+                if (v > a) a = v;
+            }
+            sb = ox_scale_byte_fp8(a, (double)g, fmt);
+            s = ox_scale_value(sb, fmt);
+            scales[r * nb + b] = (uint8_t)sb;
+            for (i = 0; i < block; ++i)
+                codes[r * k + b * block + i] = (uint8_t)ox_elem_code_fp8(load_elem(x, xtype, base + i), s, (double)g);
+        }
+    return 0;
+}
+
+/* e(c) * s * g, exact in double (e has 4 significant bits, s 4, g 24). */
+static double dq_exact_fp8(const uint8_t* codes, const uint8_t* scales, int64_t r, int64_t col,
+                           int64_t k, int block, int fmt, double g)
+{
+    double e = ox_e4m3_value(codes[r * k + col]);
+    double s = ox_scale_value(scales[r * (k / block) + col / block], fmt);
+    return e * s * g;
+}
+
+int ox_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                      int block, int fmt, float g, void* y, int ytype, int64_t ldy)
+{
+    int64_t r, c;
+    if (!codes || !scales || !y || rows < 0 || k < 0 || ldy < k || !valid_block(block) ||
+        k % block != 0 || fmt < 0 || fmt > 2 || !(g > 0.0f) || isinf(g))
+        return -1;
+    for (r = 0; r < rows; ++r)
+        for (c = 0; c < k; ++c) {
+            float f = (float)dq_exact_fp8(codes, scales, r, c, k, block, fmt, (double)g);
+            if (ytype == OX_BF16) ((uint16_t*)y)[r * ldy + c] = ox_f32_to_bf16(f);
+            else ((float*)y)[r * ldy + c] = f;
+        }
+    return 0;
+}
+
+/* Y = X . dequant(W8)^T with bf16 X, fp64 sums in k order, as ox_gemm (A16). */
+int ox_gemm_fp8(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                const uint8_t* wcodes, const uint8_t* wscales, int64_t n,
+                int block, int fmt, float g,
+                const int64_t* mrows, int64_t nm, const int64_t* ncols, int64_t nn,
+                double* y, double* aabs)
+{
+    int64_t i, j, kk;
+    if (!x || !wcodes || !wscales || !mrows || !ncols || !y || !aabs || m < 0 || n < 0 ||
+        k <= 0 || ldx < k || !valid_block(block) || k % block != 0 || fmt < 0 || fmt > 2 ||
+        !(g > 0.0f) || isinf(g))
+        return -1;
+    for (i = 0; i < nm; ++i) {
+        int64_t mi = mrows[i];
+        if (mi < 0 || mi >= m) return -1;
+        for (j = 0; j < nn; ++j) {
+            int64_t nj = ncols[j];
+            double acc = 0.0, accabs = 0.0;
+            if (nj < 0 || nj >= n) return -1;
+            for (kk = 0; kk < k; ++kk) {
+                double p = bf16_value(x[mi * ldx + kk]) * dq_exact_fp8(wcodes, wscales, nj, kk, k, block, fmt, (double)g);
+                acc += p;
+                accabs += fabs(p);
+            }
+            y[i * nn + j] = acc;
+            aabs[i * nn + j] = accabs;
+        }
+    }
+    return 0;
+}
+
+/* Batch forms for exhaustive checks. */
+void ox_scale_bytes_fp8(const double* a, int64_t n, double g, int fmt, uint8_t* out)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = (uint8_t)ox_scale_byte_fp8(a[i], g, fmt);
+}
+
+void ox_elem_codes_fp8(const double* x, int64_t n, double s, double g, uint8_t* out)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i) out[i] = (uint8_t)ox_elem_code_fp8(x[i], s, g);
+}

@@ -71,6 +71,24 @@ int ox_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
 int ox_mse_split(const void* x, int xtype, int64_t rows, int64_t k, int64_t ldx,
                  int block, int fmt, float g, double out[7]);
 
+/* FP8 weight fallback: E4M3 element bytes (OCP E4M3FN, largest magnitude 448)
+ * in blocks of `block` along k under the same scale formats; the block scale is
+ * the value nearest to a / (448 g).  codes: rows x k bytes (one per element). */
+double ox_e4m3_value(unsigned code);
+unsigned ox_scale_byte_fp8(double a, double g, int fmt);
+unsigned ox_elem_code_fp8(double x, double s, double g);
+int ox_quantize_fp8(const void* x, int xtype, int64_t rows, int64_t k, int64_t ldx,
+                    int block, int fmt, float g, uint8_t* codes, uint8_t* scales);
+int ox_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                      int block, int fmt, float g, void* y, int ytype, int64_t ldy);
+int ox_gemm_fp8(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
+                const uint8_t* wcodes, const uint8_t* wscales, int64_t n,
+                int block, int fmt, float g,
+                const int64_t* mrows, int64_t nm, const int64_t* ncols, int64_t nn,
+                double* y, double* aabs);
+void ox_scale_bytes_fp8(const double* a, int64_t n, double g, int fmt, uint8_t* out);
+void ox_elem_codes_fp8(const double* x, int64_t n, double s, double g, uint8_t* out);
+
 #ifdef __cplusplus
 }
 #endif
