@@ -151,6 +151,43 @@ mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k
                          void* stream);
 
 /*
+ * FP8 weight fallback ([MXS] section 5.3 item 1: weights whose standard deviation is below
+ * 1e-4 come out of FP4 quantization as zeros, and FP8 is the remedy named there; section 6
+ * item 1: key layers kept in FP8).  The MX block structure with an 8-bit element: per block
+ * of `block` consecutive elements along a row, the scale s is the scale-format value nearest
+ * to a / (448 g) (448, the largest E4M3 magnitude, in place of 6), and every element becomes
+ * the E4M3 byte (OCP E4M3FN: sign, 4 exponent bits with bias 7 and subnormals, 3 mantissa
+ * bits, largest magnitude 448) nearest to |x| / (s g), clipped at 448, ties to the even
+ * code, with the sign bit of x; a zero scale codes the block as +-0.  Note that E4M3 block
+ * scales (smallest 2^-9) flush blocks with a < 448 * 2^-10 * g; UE5M3 or E8M0 scales, or g,
+ * keep small weights.
+ *  codes : rows x k bytes, row-major (one byte per element).
+ *  scales: rows x k/block bytes, row-major (MX_LAYOUT_ROWMAJOR order).
+ *
+ * mx_quantize_fp8 / mx_dequantize_fp8: as mx_quantize / mx_dequantize (same arguments,
+ * errors and value rules: dequantized value one fp32 rounding of e * s * g, bf16 the
+ * nearest-even bf16 of that; byte 0x7F/0xFF, never written by the quantizer, reads as NaN),
+ * row-major scales only.
+ *
+ * mx_gemm_fp8 -- Y = X . dequant(Wq)^T with bf16 X (m x k, row stride ld_x) and FP8 weights
+ * (n x k codes, n x k/block scales as written by mx_quantize_fp8), fp32 accumulation, Y of
+ * y_type (m x n, row stride ld_y).  Weights enter the bf16 matrix cores as e * s, exact for
+ * |e * s| >= 2^-133; g multiplies the fp32 sums.  Errors as mx_gemm (W4A16); needs no
+ * workspace.
+ *
+ * mx_use_fp8 -- the fallback rule (host): 1 when sigma < 1e-4, else 0.
+ */
+mx_status mx_quantize_fp8(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x, int block,
+                          mx_scale_fmt fmt, float tensor_scale, uint8_t* codes, uint8_t* scales, void* stream);
+mx_status mx_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, int block,
+                            mx_scale_fmt fmt, float tensor_scale, void* y, mx_dtype y_type, int64_t ld_y,
+                            void* stream);
+mx_status mx_gemm_fp8(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x, const uint8_t* w_codes,
+                      const uint8_t* w_scales, int block, mx_scale_fmt fmt, float tensor_scale, void* y,
+                      mx_dtype y_type, int64_t ld_y, void* stream);
+int mx_use_fp8(double sigma);
+
+/*
  * Block-size policy ([MXS] section 6 item 2: the block size follows the tensor's standard
  * deviation; section 5.1 item 1: a block size per layer kind).
  *

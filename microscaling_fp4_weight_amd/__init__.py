@@ -68,6 +68,14 @@ def lib() -> ctypes.CDLL:
     L.mx_adaptive_block_size.restype = i32
     L.mx_layer_block_size.argtypes = [i32]
     L.mx_layer_block_size.restype = i32
+    L.mx_quantize_fp8.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, vp, vp, vp]
+    L.mx_quantize_fp8.restype = i32
+    L.mx_dequantize_fp8.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, i32, i64, vp]
+    L.mx_dequantize_fp8.restype = i32
+    L.mx_gemm_fp8.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, vp, i32, i64, vp]
+    L.mx_gemm_fp8.restype = i32
+    L.mx_use_fp8.argtypes = [ctypes.c_double]
+    L.mx_use_fp8.restype = i32
     L.mx_gemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     L.mx_gemm_workspace_size.restype = sz
     L.mx_gemm.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp,
@@ -209,6 +217,53 @@ def mx_adaptive_block_size(sigma: float) -> int:
 
 def mx_layer_block_size(kind: str) -> int:
     return int(lib().mx_layer_block_size(LAYER_KIND[kind]))
+
+
+def mx_quantize_fp8(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0,
+                    codes: torch.Tensor | None = None, scales: torch.Tensor | None = None, stream=None):
+    """FP8 (E4M3 element) MX quantization of x (rows x k, bf16/fp32 on the GPU) -> (codes rows x k
+    uint8, scales rows x k/block uint8)."""
+    rows, k, ld = _rows_ld(x, "x")
+    if codes is None:
+        codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, k // block if block else 0), dtype=torch.uint8, device=x.device)
+    st = lib().mx_quantize_fp8(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt], tensor_scale,
+                               _ptr(codes), _ptr(scales), _stream(stream))
+    _check(st, "mx_quantize_fp8")
+    return codes, scales
+
+
+def mx_dequantize_fp8(codes: torch.Tensor, scales: torch.Tensor, block: int, fmt: str,
+                      tensor_scale: float = 1.0, out_dtype: torch.dtype = torch.float32,
+                      y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    rows, k = codes.shape
+    if y is None:
+        y = torch.empty((rows, k), dtype=out_dtype, device=codes.device)
+    _, _, ldy = _rows_ld(y, "y")
+    st = lib().mx_dequantize_fp8(_ptr(codes), _ptr(scales), rows, k, block, FMT[fmt], tensor_scale, _ptr(y),
+                                 _dtype_code(y.dtype), ldy, _stream(stream))
+    _check(st, "mx_dequantize_fp8")
+    return y
+
+
+def mx_gemm_fp8(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, block: int, fmt: str,
+                tensor_scale: float = 1.0, out_dtype: torch.dtype = torch.bfloat16,
+                y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X . dequant(W8)^T; x: m x k bf16; w_codes: n x k; w_scales: n x k/block."""
+    m, k, ldx = _rows_ld(x, "x")
+    n = w_codes.size(0)
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _, _, ldy = _rows_ld(y, "y")
+    st = lib().mx_gemm_fp8(_ptr(x), m, n, k, ldx, _ptr(w_codes), _ptr(w_scales), block, FMT[fmt], tensor_scale,
+                           _ptr(y), _dtype_code(y.dtype), ldy, _stream(stream))
+    _check(st, "mx_gemm_fp8")
+    return y
+
+
+def mx_use_fp8(sigma: float) -> bool:
+    return bool(lib().mx_use_fp8(sigma))
 
 
 def mx_gemm_workspace_size(m: int, n: int, k: int, block: int, mode: str) -> int:

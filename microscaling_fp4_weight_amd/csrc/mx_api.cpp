@@ -256,6 +256,108 @@ int mx_layer_block_size(mx_layer_kind kind)
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// FP8 weight fallback
+// ---------------------------------------------------------------------------------------
+mx_status mx_quantize_fp8(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x, int block,
+                          mx_scale_fmt fmt, float tensor_scale, uint8_t* codes, uint8_t* scales, void* stream)
+{
+    mx_status st = check_quantized(rows, k, block, fmt, tensor_scale, MX_LAYOUT_ROWMAJOR);
+    if (st != MX_OK) return st;
+    if (x_type != MX_F32 && x_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_x < k) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return MX_OK;
+    if (!x || !codes || !scales) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
+    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
+    const int64_t esize = x_type == MX_BF16 ? 2 : 4;
+    mxk::QuantArgs a{};
+    a.x = x;
+    a.bf16 = x_type == MX_BF16;
+    a.rows = rows;
+    a.k = k;
+    a.ldx = ld_x;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = (double)tensor_scale;
+    a.codes = codes;
+    a.scales = scales;
+    a.fast = (k % 8 == 0) && ((ld_x * esize) % 16 == 0) && rows * (k / 8) < (int64_t(1) << 31);
+    a.ts_ks = 0;
+    return from_hip(mxk::launch_quantize_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, int block,
+                            mx_scale_fmt fmt, float tensor_scale, void* y, mx_dtype y_type, int64_t ld_y,
+                            void* stream)
+{
+    mx_status st = check_quantized(rows, k, block, fmt, tensor_scale, MX_LAYOUT_ROWMAJOR);
+    if (st != MX_OK) return st;
+    if (y_type != MX_F32 && y_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_y < k) return MX_ERR_INVALID_ARG;
+    if (rows == 0 || k == 0) return MX_OK;
+    if (!codes || !scales || !y) return MX_ERR_INVALID_ARG;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(y)) return MX_ERR_ALIGNMENT;
+    if (k > kMaxK) return MX_ERR_UNSUPPORTED;
+    const int64_t esize = y_type == MX_BF16 ? 2 : 4;
+    mxk::DequantArgs a{};
+    a.codes = codes;
+    a.scales = scales;
+    a.rows = rows;
+    a.k = k;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = (double)tensor_scale;
+    a.y = y;
+    a.bf16 = y_type == MX_BF16;
+    a.ldy = ld_y;
+    a.fast = (k % 8 == 0) && ((ld_y * esize) % 16 == 0) && rows * (k / 8) < (int64_t(1) << 31);
+    a.ts_ks = 0;
+    return from_hip(mxk::launch_dequantize_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_gemm_fp8(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x, const uint8_t* w_codes,
+                      const uint8_t* w_scales, int block, mx_scale_fmt fmt, float tensor_scale, void* y,
+                      mx_dtype y_type, int64_t ld_y, void* stream)
+{
+    if (m < 0 || n < 0) return MX_ERR_INVALID_ARG;
+    mx_status st = check_quantized(n, k, block, fmt, tensor_scale, MX_LAYOUT_ROWMAJOR);
+    if (st != MX_OK) return st;
+    if (y_type != MX_F32 && y_type != MX_BF16) return MX_ERR_INVALID_ARG;
+    if (ld_x < k || ld_y < n) return MX_ERR_INVALID_ARG;
+    if (m == 0 || n == 0) return MX_OK;
+    if (!y) return MX_ERR_INVALID_ARG;
+    if (!aligned16(y)) return MX_ERR_ALIGNMENT;
+    if (k == 0)
+        return from_hip(mxk::launch_fill_zero(y, m, n, ld_y, y_type == MX_BF16, static_cast<hipStream_t>(stream)));
+    if (!x || !w_codes || !w_scales) return MX_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales)) return MX_ERR_ALIGNMENT;
+    if (k > kMaxGemmK) return MX_ERR_UNSUPPORTED;
+    mxk::W8Args a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.m = m;
+    a.n = n;
+    a.k = k;
+    a.ldx = ld_x;
+    a.wc = w_codes;
+    a.ws = w_scales;
+    a.block = block;
+    a.fmt = (int)fmt;
+    a.g = (double)tensor_scale;
+    a.y = y;
+    a.y_bf16 = y_type == MX_BF16;
+    a.ldy = ld_y;
+    const int64_t xspan = (63 * ld_x + k) * 2, yspan = (63 * ld_y + 16) * 4;
+    a.fast = (k % 32 == 0) && ((ld_x * 2) % 16 == 0) && xspan < (int64_t(1) << 31) &&
+             yspan < (int64_t(1) << 31) && 16 * k < (int64_t(1) << 31);
+    return from_hip(mxk::launch_gemm_w8(a, static_cast<hipStream_t>(stream)));
+}
+
+int mx_use_fp8(double sigma)
+{
+    return sigma < 1e-4 ? 1 : 0;
+}
+
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode)
 {
     if (m < 0 || n < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;

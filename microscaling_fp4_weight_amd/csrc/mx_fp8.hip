@@ -1,0 +1,507 @@
+// mx_fp8.hip -- the FP8 weight fallback: E4M3 elements in the MX block structure.
+//
+// hotelren.com/news/2192771, article "量化技术演进与微缩量化原理": section 5.3 item 1 (a layer
+// whose weights have a standard deviation below 1e-4 comes out of FP4 quantization as zeros;
+// the remedy named there is FP8) and section 6 item 1 (key layers kept in FP8).  The format
+// keeps everything of the FP4 path but the element: per block of `block` elements along k a
+// scale in one of the three scale formats, the value nearest to absmax / (448 g) (448 being
+// the largest E4M3 magnitude, where FP4 divides by 6), and one E4M3 byte per element, the
+// value nearest to |x| / (s g), clipped at 448, ties to the even code, sign kept; a zero scale
+// flushes the block to +-0.
+//
+// Element rounding is exact: a quotient estimate q = |x| * fl(1/(s g)) in fp64 picks a code,
+// which an exact comparison of |x| with the neighbouring decision points (midpoint * s * g,
+// at most 33 significant bits, exact in fp64) corrects by at most one step.
+//
+// The W8A16 product Y = X . dequant(W8)^T runs on bf16 matrix cores: e * s (at most 8
+// significant bits) is exact in bf16 for |e * s| >= 2^-133, g multiplies the fp32 sums.
+#include "mx_device.h"
+#include "mx_internal.h"
+
+namespace mxk {
+namespace f8 {
+
+constexpr int THREADS = 256;
+
+// E4M3 magnitude of code c in 0..127 as an exact double (127 reads as 480, the pattern's
+// value were it not NaN; callers treat 0x7F separately).
+__device__ __forceinline__ double mag(uint32_t c)
+{
+    const uint32_t e = c >> 3, m = c & 7u;
+    const double p = __builtin_bit_cast(double, (uint64_t)(1023 + (int)e - 10) << 52);  // 2^(e-10)
+    return e == 0 ? (double)c * 0x1p-9 : (double)(8u + m) * p;
+}
+
+// E4M3 magnitude code (0..126) nearest to a / S: ties to even, clipped at 448.  a >= 0;
+// S > 0 is exact; rS is fl(1/S).
+__device__ __forceinline__ uint32_t code_of(double a, double S, double rS)
+{
+    const double q = a * rS;
+    uint32_t c;
+    if (q >= 448.0) {
+        c = 126;
+    } else if (q < 0x1p-6) {
+        c = (uint32_t)__builtin_rint(q * 512.0);  // subnormal codes 0..7 (8 is 2^-6)
+    } else {
+        const int e = (int)((__builtin_bit_cast(uint64_t, q) >> 52) & 0x7FF) - 1023;  // -6 .. 8
+        const double t = q * __builtin_bit_cast(double, (uint64_t)(1023 + 3 - e) << 52);  // [8, 16)
+        const int cc = (e + 7) * 8 + (int)__builtin_rint(t) - 8;
+        c = cc > 126 ? 126u : (uint32_t)cc;
+    }
+    if (c < 126) {
+        const double up = (mag(c) + mag(c + 1)) * 0.5 * S;
+        if (a > up || (a == up && (c & 1u))) ++c;
+    }
+    if (c > 0) {
+        const double dn = (mag(c - 1) + mag(c)) * 0.5 * S;
+        if (a < dn || (a == dn && (c & 1u))) --c;
+    }
+    return c;
+}
+
+struct Blk {
+    double S, rS;  // s * g and its reciprocal (S == 0: flushed)
+};
+
+template <int FMT>
+__device__ __forceinline__ Blk block_params(uint32_t sbyte, double g)
+{
+    Blk p;
+    p.S = scale_value_f64<FMT>(sbyte) * g;
+    p.rS = p.S != 0.0 ? 1.0 / p.S : 0.0;
+    return p;
+}
+
+// E4M3 byte of an element with fp32 bit pattern xb
+__device__ __forceinline__ uint32_t elem_byte(uint32_t xb, const Blk& p)
+{
+    const uint32_t sign = (xb >> 24) & 0x80u;
+    if (p.S == 0.0) return sign;
+    return sign | code_of((double)u2f(xb & 0x7FFFFFFFu), p.S, p.rS);
+}
+
+// ---------------------------------------------------------------------------------------
+// quantize, fast path: one lane per 8 consecutive elements (16-byte bf16 or 2 x 16-byte fp32
+// loads, 8 code bytes stored); blocks of 4 are two per lane, blocks of 8 one per lane, larger
+// ones span BLOCK / 8 adjacent lanes that combine their absmax with lane shuffles.
+// ---------------------------------------------------------------------------------------
+template <int BLOCK, int FMT, bool BF16>
+__global__ __launch_bounds__(THREADS) void quantize_fp8_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes,
+                                                               FastDiv upr_div, uint32_t upr, uint32_t total,
+                                                               double g, uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales, int64_t k)
+{
+    constexpr int NB = BLOCK < 8 ? 8 / BLOCK : 1;
+    constexpr int EPB = 8 / NB;
+    constexpr int LANES = BLOCK > 8 ? BLOCK / 8 : 1;
+    const uint32_t u = blockIdx.x * THREADS + threadIdx.x;
+    const bool act = u < total;
+    const uint32_t row = act ? upr_div.div(u) : 0u;
+    const uint32_t c8 = act ? u - row * upr : 0u;
+
+    uint32_t xb[8];
+    if (act) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(x + (int64_t)row * ldx_bytes + (int64_t)c8 * (BF16 ? 16 : 32));
+        if constexpr (BF16) {
+            const u32x4 v = p[0];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xb[2 * j] = w[j] << 16;
+                xb[2 * j + 1] = w[j] & 0xFFFF0000u;
+            }
+        } else {
+            const u32x4 v0 = p[0], v1 = p[1];
+            const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xb[j] = w[j];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xb[j] = 0u;
+    }
+
+    uint32_t amax[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < EPB; ++e) {
+            const uint32_t a = xb[b * EPB + e] & 0x7FFFFFFFu;
+            m = a > m ? a : m;
+        }
+        amax[b] = m;
+    }
+    if constexpr (LANES > 1) {
+#pragma unroll
+        for (int off = 1; off < LANES; off <<= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)amax[0], off);
+            amax[0] = o > amax[0] ? o : amax[0];
+        }
+    }
+
+    uint32_t cb[8], sb[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        sb[b] = scale_code_g<FMT>(amax[b], 448.0 * g);
+        const Blk p = block_params<FMT>(sb[b], g);
+#pragma unroll
+        for (int e = 0; e < EPB; ++e) cb[b * EPB + e] = elem_byte(xb[b * EPB + e], p);
+    }
+    if (!act) return;
+    const u32x2 cv = {cb[0] | (cb[1] << 8) | (cb[2] << 16) | (cb[3] << 24),
+                      cb[4] | (cb[5] << 8) | (cb[6] << 16) | (cb[7] << 24)};
+    *reinterpret_cast<u32x2*>(codes + (int64_t)row * k + (int64_t)c8 * 8) = cv;
+    uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
+    if constexpr (NB == 2) {
+        *reinterpret_cast<uint16_t*>(sp + c8 * 2) = (uint16_t)(sb[0] | (sb[1] << 8));
+    } else {
+        if (LANES == 1 || (c8 % LANES) == 0) sp[c8 / LANES] = (uint8_t)sb[0];
+    }
+}
+
+// quantize, generic path: one thread per block (any k % block == 0, any alignment)
+template <int FMT, bool BF16>
+__global__ __launch_bounds__(THREADS) void quantize_fp8_generic_kernel(const uint8_t* __restrict__ x, int64_t ldx,
+                                                                       int64_t rows, int64_t k, int block, double g,
+                                                                       uint8_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales)
+{
+    const int64_t nb = k / block;
+    const int64_t id = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+    if (id >= rows * nb) return;
+    const int64_t r = id / nb, b = id - r * nb;
+    const int64_t base = r * ldx + b * block;
+    auto bits = [&](int64_t i) -> uint32_t {
+        if constexpr (BF16) return (uint32_t)reinterpret_cast<const uint16_t*>(x)[base + i] << 16;
+        else return reinterpret_cast<const uint32_t*>(x)[base + i];
+    };
+    uint32_t amax = 0;
+    for (int i = 0; i < block; ++i) {
+        const uint32_t a = bits(i) & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+    }
+    const uint32_t sb = scale_code_g<FMT>(amax, 448.0 * g);
+    scales[r * nb + b] = (uint8_t)sb;
+    const Blk p = block_params<FMT>(sb, g);
+    for (int i = 0; i < block; ++i) codes[r * k + b * block + i] = (uint8_t)elem_byte(bits(i), p);
+}
+
+// ---------------------------------------------------------------------------------------
+// dequantize: y = fl32(e * s * g) (exact product in fp64), bf16 = RNE of that
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float dq_value(uint32_t c, double sg)
+{
+    const uint32_t m7 = c & 0x7Fu;
+    const float f = (float)(mag(m7) * sg);
+    return m7 == 0x7Fu ? __builtin_nanf("") : ((c & 0x80u) ? -f : f);  // 0x7F, 0xFF: NaN
+}
+
+template <int BLOCK, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(THREADS) void dequantize_fp8_kernel(const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales,
+                                                                 FastDiv upr_div, uint32_t upr, uint32_t total,
+                                                                 int64_t k, double g, uint8_t* __restrict__ y,
+                                                                 int64_t ldy_bytes)
+{
+    const uint32_t u = blockIdx.x * THREADS + threadIdx.x;  // unit of 8 elements
+    if (u >= total) return;
+    const uint32_t row = upr_div.div(u), c8 = u - row * upr;
+    const u32x2 cv = *reinterpret_cast<const u32x2*>(codes + (int64_t)row * k + (int64_t)c8 * 8);
+    const uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
+    double sg[BLOCK < 8 ? 2 : 1];
+    if constexpr (BLOCK < 8) {
+        sg[0] = scale_value_f64<FMT>(sp[c8 * 2]) * g;
+        sg[1] = scale_value_f64<FMT>(sp[c8 * 2 + 1]) * g;
+    } else {
+        sg[0] = scale_value_f64<FMT>(sp[(c8 * 8) / BLOCK]) * g;
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t c = ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3))) & 0xFFu;
+        v[e] = dq_value(c, sg[BLOCK < 8 ? e / 4 : 0]);
+    }
+    if constexpr (OUT_BF16) {
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2 * j], (__bf16)v[2 * j + 1]});
+        *reinterpret_cast<u32x4*>(y + (int64_t)row * ldy_bytes + (int64_t)c8 * 16) = u32x4{o[0], o[1], o[2], o[3]};
+    } else {
+        u32x4* p = reinterpret_cast<u32x4*>(y + (int64_t)row * ldy_bytes + (int64_t)c8 * 32);
+        p[0] = u32x4{f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])};
+        p[1] = u32x4{f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])};
+    }
+}
+
+template <int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(THREADS) void dequantize_fp8_generic_kernel(const uint8_t* __restrict__ codes,
+                                                                         const uint8_t* __restrict__ scales,
+                                                                         int64_t rows, int64_t k, int block, double g,
+                                                                         uint8_t* __restrict__ y, int64_t ldy)
+{
+    const int64_t id = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+    if (id >= rows * k) return;
+    const int64_t r = id / k, c = id - r * k;
+    const double sg = scale_value_f64<FMT>(scales[r * (k / block) + c / block]) * g;
+    const float v = dq_value(codes[r * k + c], sg);
+    if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(y)[r * ldy + c] = (__bf16)v;
+    else reinterpret_cast<float*>(y)[r * ldy + c] = v;
+}
+
+// ---------------------------------------------------------------------------------------
+// W8A16 GEMM / GEMV on bf16 16x16x32 matrix cores.  A workgroup (4 waves) owns 16 weight rows
+// (output columns) and 16 MT activation rows; its waves take every fourth 128-k window.  In a
+// window a lane holds weight row lane % 16 and the 32 consecutive k 32 (lane / 16) .. +31
+// (two 16-byte code loads: the four lanes of a row read its 128 bytes), dequantizes them to
+// bf16 in registers and feeds four MFMAs with the activations of the same k: MFMA i takes
+// k 32 (lane / 16) + 8 i .. +7 from every lane, the same permutation of k for both operands,
+// which leaves each dot product unchanged.  The next window's codes and scales are loaded
+// before the current window is computed.  The four waves' partial sums meet in LDS.
+// Requires k % 32 == 0.
+// ---------------------------------------------------------------------------------------
+template <int BLOCK>
+__device__ __forceinline__ uint64_t lane_scales(rsrc_t r, uint32_t off)
+{
+    if constexpr (BLOCK >= 32) return bload8(r, off);
+    else if constexpr (BLOCK == 16) return bload16(r, off);
+    else if constexpr (BLOCK == 8) return bload32(r, off);
+    else return bload64(r, off);
+}
+
+// 32 codes (8 dwords) with their scale bytes -> 32 bf16 (16 dwords), e * s exact.
+template <int BLOCK, int FMT>
+__device__ __forceinline__ void dequant_w8(const uint32_t (&cw)[8], uint64_t sbytes, uint32_t (&out)[16])
+{
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {  // half-dword h: elements 2h, 2h+1
+        const int e = 2 * h;
+        const uint32_t byte = (uint32_t)(sbytes >> (8 * (BLOCK >= 32 ? 0 : e / BLOCK))) & 0xFFu;
+        float pow2 = 1.0f, mant = 1.0f;
+        if constexpr (FMT == FMT_E8M0) {
+            pow2 = e8m0_value(byte);
+        } else {
+            const DecG1 p = dec_params_g1<FMT>(byte);
+            pow2 = p.pow2;
+            mant = p.mant;
+        }
+        f32x2 d;
+        if (h & 1) d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[h >> 1], pow2, true);
+        else d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[h >> 1], pow2, false);
+        const float lo = FMT == FMT_E8M0 ? d.x : d.x * mant, hi = FMT == FMT_E8M0 ? d.y : d.y * mant;
+        out[h] = (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);  // exact: at most 8 significant bits
+    }
+}
+
+template <int BLOCK, int FMT, int MT, bool OUT_BF16>
+__global__ __launch_bounds__(THREADS) void gemm_w8_kernel(const W8Args a)
+{
+    __shared__ f32x4 red[4][MT][64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t r16 = lane & 15, q = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16, m0 = (int64_t)blockIdx.y * 16 * MT;
+    const uint32_t K = (uint32_t)a.k;
+    const uint32_t nrows = (uint32_t)(a.n - n0 < 16 ? a.n - n0 : 16);
+    const uint32_t mrows = (uint32_t)(a.m - m0 < 16 * MT ? a.m - m0 : 16 * MT);
+    const rsrc_t wc = make_rsrc(a.wc + n0 * a.k, nrows * K);
+    const rsrc_t ws = make_rsrc(a.ws + n0 * (a.k / BLOCK), nrows * (K / BLOCK));
+    const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, (uint32_t)(((int64_t)(mrows - 1) * a.ldx + a.k) * 2));
+    const uint32_t nwin = (K + 127) / 128;
+
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_w = [&](uint32_t win, uint32_t (&cw)[8], uint64_t& sb) {
+        const uint32_t kc = win * 128 + 32 * q;
+        const bool ok = kc < K && r16 < nrows;
+        const uint32_t off = ok ? r16 * K + kc : kOOB;
+        const u32x4 c0 = bload128(wc, off), c1 = bload128(wc, ok ? off + 16 : kOOB);
+        cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
+        cw[4] = c1.x; cw[5] = c1.y; cw[6] = c1.z; cw[7] = c1.w;
+        sb = lane_scales<BLOCK>(ws, ok ? r16 * (K / BLOCK) + kc / BLOCK : kOOB);
+    };
+
+    uint32_t cw[8];
+    uint64_t sb = 0;
+    uint32_t win = (uint32_t)wave;
+    if (win < nwin) load_w(win, cw, sb);
+    for (; win < nwin; win += 4) {
+        uint32_t cn[8];
+        uint64_t sn = 0;
+        if (win + 4 < nwin) load_w(win + 4, cn, sn);
+        const uint32_t kc = win * 128 + 32 * q;
+        u32x4 xa[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const uint32_t xrow = 16 * t + r16;
+            const bool ok = kc < K && xrow < mrows;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xa[t][i] = bload128(xr, ok ? (xrow * (uint32_t)a.ldx + kc + 8 * i) * 2 : kOOB);
+        }
+        uint32_t wb[16];
+        dequant_w8<BLOCK, FMT>(cw, sb, wb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 bv = {wb[4 * i], wb[4 * i + 1], wb[4 * i + 2], wb[4 * i + 3]};
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[t][i]),
+                                                                 __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cw[j] = cn[j];
+        sb = sn;
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+    __syncthreads();
+    // wave w adds the four partials of m-subtiles t = w, w + 4, ... and stores them:
+    // lane holds C[4 (lane / 16) + i][lane % 16], rows m, columns n
+    constexpr uint32_t ESZ = OUT_BF16 ? 2 : 4;
+    const rsrc_t yr = make_rsrc(static_cast<uint8_t*>(a.y) + (m0 * a.ldy + n0) * ESZ, 0x7FFFFFFFu);
+    for (int t = wave; t < MT; t += 4) {
+        const f32x4 s = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t mm = 16 * t + 4 * q + i;
+            const uint32_t off = (mm < mrows && r16 < nrows) ? (mm * (uint32_t)a.ldy + r16) * ESZ : kOOB;
+            const float v = s[i] * (float)a.g;
+            if constexpr (OUT_BF16) bstore16(yr, off, __builtin_bit_cast(uint16_t, (__bf16)v));
+            else bstore32(yr, off, f2u(v));
+        }
+    }
+}
+
+// any k % block == 0: one thread per output, fp32 accumulation
+template <int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(THREADS) void gemm_w8_generic_kernel(const W8Args a)
+{
+    const int64_t id = (int64_t)blockIdx.x * THREADS + threadIdx.x;
+    if (id >= a.m * a.n) return;
+    const int64_t m = id / a.n, n = id - m * a.n;
+    float acc = 0.0f;
+    for (int64_t kk = 0; kk < a.k; ++kk) {
+        const double s = scale_value_f64<FMT>(a.ws[n * (a.k / a.block) + kk / a.block]);
+        const float w = dq_value(a.wc[n * a.k + kk], s);
+        acc = __builtin_fmaf(u2f((uint32_t)a.x[m * a.ldx + kk] << 16), w, acc);
+    }
+    const float v = acc * (float)a.g;
+    if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(a.y)[m * a.ldy + n] = (__bf16)v;
+    else reinterpret_cast<float*>(a.y)[m * a.ldy + n] = v;
+}
+
+}  // namespace f8
+
+// ---------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------
+template <int FMT, bool BF16>
+static hipError_t launch_q8(const QuantArgs& a, hipStream_t st)
+{
+    const int esz = BF16 ? 2 : 4;
+    if (!a.fast) {
+        const int64_t nblk = a.rows * (a.k / a.block);
+        hipLaunchKernelGGL((f8::quantize_fp8_generic_kernel<FMT, BF16>), dim3((unsigned)((nblk + 255) / 256)),
+                           dim3(f8::THREADS), 0, st, static_cast<const uint8_t*>(a.x), a.ldx, a.rows, a.k, a.block,
+                           a.g, a.codes, a.scales);
+        return hipGetLastError();
+    }
+    const uint32_t upr = (uint32_t)(a.k / 8), total = (uint32_t)(a.rows * upr);
+    const FastDiv fd = FastDiv::make(upr);
+    const dim3 grid((total + f8::THREADS - 1) / f8::THREADS);
+#define MXQ8(B)                                                                                              \
+    case B:                                                                                                  \
+        hipLaunchKernelGGL((f8::quantize_fp8_kernel<B, FMT, BF16>), grid, dim3(f8::THREADS), 0, st,         \
+                           static_cast<const uint8_t*>(a.x), a.ldx * esz, fd, upr, total, a.g, a.codes,     \
+                           a.scales, a.k);                                                                   \
+        break;
+    switch (a.block) {
+        MXQ8(4) MXQ8(8) MXQ8(16) MXQ8(32) MXQ8(64) MXQ8(128) MXQ8(256)
+        default: return hipErrorInvalidValue;
+    }
+#undef MXQ8
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t st)
+{
+#define MXF(F) \
+    if (a.fmt == F) return a.bf16 ? launch_q8<F, true>(a, st) : launch_q8<F, false>(a, st);
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, bool OUT_BF16>
+static hipError_t launch_dq8(const DequantArgs& a, hipStream_t st)
+{
+    if (!a.fast) {
+        const int64_t n = a.rows * a.k;
+        hipLaunchKernelGGL((f8::dequantize_fp8_generic_kernel<FMT, OUT_BF16>), dim3((unsigned)((n + 255) / 256)),
+                           dim3(f8::THREADS), 0, st, a.codes, a.scales, a.rows, a.k, a.block, a.g,
+                           static_cast<uint8_t*>(a.y), a.ldy);
+        return hipGetLastError();
+    }
+    const uint32_t upr = (uint32_t)(a.k / 8), total = (uint32_t)(a.rows * upr);
+    const FastDiv fd = FastDiv::make(upr);
+    const dim3 grid((total + f8::THREADS - 1) / f8::THREADS);
+    const int64_t ldyb = a.ldy * (OUT_BF16 ? 2 : 4);
+#define MXD8(B)                                                                                              \
+    case B:                                                                                                  \
+        hipLaunchKernelGGL((f8::dequantize_fp8_kernel<B, FMT, OUT_BF16>), grid, dim3(f8::THREADS), 0, st,   \
+                           a.codes, a.scales, fd, upr, total, a.k, a.g, static_cast<uint8_t*>(a.y), ldyb);  \
+        break;
+    switch (a.block) {
+        MXD8(4) MXD8(8) MXD8(16) MXD8(32) MXD8(64) MXD8(128) MXD8(256)
+        default: return hipErrorInvalidValue;
+    }
+#undef MXD8
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_fp8(const DequantArgs& a, hipStream_t st)
+{
+#define MXF(F) \
+    if (a.fmt == F) return a.bf16 ? launch_dq8<F, true>(a, st) : launch_dq8<F, false>(a, st);
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
+}
+
+template <int FMT, bool OUT_BF16>
+static hipError_t launch_w8(const W8Args& a, hipStream_t st)
+{
+    if (!a.fast) {
+        const int64_t total = a.m * a.n;
+        hipLaunchKernelGGL((f8::gemm_w8_generic_kernel<FMT, OUT_BF16>), dim3((unsigned)((total + 255) / 256)),
+                           dim3(f8::THREADS), 0, st, a);
+        return hipGetLastError();
+    }
+    const bool small = a.m <= 16;
+    const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)((a.m + (small ? 16 : 64) - 1) / (small ? 16 : 64)));
+#define MXW8(B)                                                                                                  \
+    case B:                                                                                                      \
+        if (small) hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(f8::THREADS), 0, st, a); \
+        else hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 4, OUT_BF16>), grid, dim3(f8::THREADS), 0, st, a);       \
+        break;
+    switch (a.block) {
+        MXW8(4) MXW8(8) MXW8(16) MXW8(32) MXW8(64) MXW8(128) MXW8(256)
+        default: return hipErrorInvalidValue;
+    }
+#undef MXW8
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w8(const W8Args& a, hipStream_t st)
+{
+#define MXF(F) \
+    if (a.fmt == F) return a.y_bf16 ? launch_w8<F, true>(a, st) : launch_w8<F, false>(a, st);
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mxk

@@ -120,6 +120,25 @@ struct StatsArgs {
 constexpr int kStatsMaxGroups = 1024;  // workgroups of each statistics pass (fixed grid cap)
 int stats_groups(int64_t rows, int64_t k);
 
+// W8A16 GEMM with FP8 (E4M3) weights
+struct W8Args {
+    const uint16_t* x;        // bf16 activations, m x k
+    int64_t m, n, k, ldx;
+    const uint8_t* wc;        // n x k E4M3 bytes
+    const uint8_t* ws;        // n x k/block scale bytes
+    int block;
+    int fmt;
+    double g;
+    void* y;
+    bool y_bf16;
+    int64_t ldy;
+    bool fast;                // k % 32 == 0, 16-byte aligned rows, 32-bit offsets: matrix-core kernel
+};
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t st);     // codes: rows x k bytes
+hipError_t launch_dequantize_fp8(const DequantArgs& a, hipStream_t st);
+hipError_t launch_gemm_w8(const W8Args& a, hipStream_t st);
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t st);
 hipError_t launch_tensor_stats(const StatsArgs& a, hipStream_t st);
 hipError_t launch_quant_error(const ErrArgs& a, hipStream_t st);

@@ -30,10 +30,11 @@ def declared_functions():
 
 def test_exports_match_header(L):
     names = declared_functions()
-    assert names == ["mx_adaptive_block_size", "mx_dequantize", "mx_gemm", "mx_gemm_workspace_size",
-                     "mx_layer_block_size", "mx_quant_error", "mx_quant_error_workspace_size",
-                     "mx_quantize", "mx_scale_bytes", "mx_status_string", "mx_tensor_stats",
-                     "mx_tensor_stats_workspace_size"]
+    assert names == ["mx_adaptive_block_size", "mx_dequantize", "mx_dequantize_fp8", "mx_gemm",
+                     "mx_gemm_fp8", "mx_gemm_workspace_size", "mx_layer_block_size", "mx_quant_error",
+                     "mx_quant_error_workspace_size", "mx_quantize", "mx_quantize_fp8", "mx_scale_bytes",
+                     "mx_status_string", "mx_tensor_stats", "mx_tensor_stats_workspace_size",
+                     "mx_use_fp8"]
     for n in names:
         assert hasattr(L, n)
     so = os.path.join(ROOT, "microscaling_fp4_weight_amd", "libmx.so")
@@ -199,3 +200,31 @@ def test_tensor_stats_validation(L):
     assert ts(out=FAKE + 8) == ALIGN
     assert ts(rows=0, x=None, out=None, work=None, wbytes=0) == OK
     assert ts(rows=1 << 20, k=1 << 15, ldx=1 << 15, wbytes=1 << 20) == UNSUPPORTED
+
+
+def test_fp8_validation(L):
+    import oracle
+    for sigma in (0.0, 5e-5, 9.99e-5, 1e-4, 0.02, float("nan")):
+        assert L.mx_use_fp8(sigma) == int(oracle.use_fp8(sigma))
+    q = L.mx_quantize_fp8
+    assert q(FAKE, BF16, 4, 48, 48, 32, E8M0, 1.0, FAKE, FAKE, None) == INVALID   # k % block
+    assert q(FAKE, BF16, 4, 64, 63, 32, E8M0, 1.0, FAKE, FAKE, None) == INVALID   # ld < k
+    assert q(FAKE, 7, 4, 64, 64, 32, E8M0, 1.0, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, BF16, 4, 64, 64, 32, 3, 1.0, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, BF16, 4, 64, 64, 32, E8M0, 0.0, FAKE, FAKE, None) == INVALID
+    assert q(None, BF16, 4, 64, 64, 32, E8M0, 1.0, FAKE, FAKE, None) == INVALID
+    assert q(FAKE + 2, BF16, 4, 64, 64, 32, E8M0, 1.0, FAKE, FAKE, None) == ALIGN
+    assert q(None, BF16, 0, 64, 64, 32, E8M0, 1.0, None, None, None) == OK
+    d = L.mx_dequantize_fp8
+    assert d(FAKE, FAKE, 4, 64, 32, E8M0, 1.0, FAKE, 9, 64, None) == INVALID
+    assert d(FAKE, FAKE, 4, 64, 32, E8M0, 1.0, FAKE, F32, 63, None) == INVALID
+    assert d(FAKE, FAKE, 4, 64, 32, E8M0, 1.0, FAKE + 4, F32, 64, None) == ALIGN
+    assert d(None, None, 0, 64, 32, E8M0, 1.0, None, F32, 64, None) == OK
+    gm = L.mx_gemm_fp8
+    assert gm(FAKE, 4, 8, 48, 48, FAKE, FAKE, 32, E8M0, 1.0, FAKE, F32, 8, None) == INVALID  # k % block
+    assert gm(FAKE, 4, 8, 64, 63, FAKE, FAKE, 32, E8M0, 1.0, FAKE, F32, 8, None) == INVALID
+    assert gm(FAKE, 4, 8, 64, 64, FAKE, FAKE, 32, E8M0, 1.0, FAKE, F32, 7, None) == INVALID
+    assert gm(FAKE, 4, 8, 64, 64, FAKE, FAKE, 32, E8M0, 1.0, None, F32, 8, None) == INVALID
+    assert gm(FAKE, 4, 8, 64, 64, FAKE, FAKE + 8, 32, E8M0, 1.0, FAKE, F32, 8, None) == ALIGN
+    assert gm(FAKE, -1, 8, 64, 64, FAKE, FAKE, 32, E8M0, 1.0, FAKE, F32, 8, None) == INVALID
+    assert gm(None, 0, 8, 64, 64, None, None, 32, E8M0, 1.0, None, F32, 8, None) == OK

@@ -1,0 +1,185 @@
+"""GPU parity of the FP8 weight fallback (hotelren.com/news/2192771, article
+"量化技术演进与微缩量化原理", section 5.3 item 1 and section 6 item 1) through the C ABI against
+the oracle: E4M3 codes and scale bytes bit-exact, dequantized values bit-exact, the W8A16
+product within |dY| <= 2e-5 * sum|x w| (plus half a bf16 ulp of Y for bf16 output)."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_fp4_weight_amd as mx
+import oracle
+import synth
+from gpu_util import DEV, assert_gemm_close, bf16_dev, edge_tensor, f32_dev, to_host_bits
+
+pytestmark = pytest.mark.gpu
+FMTS = ["e4m3", "ue5m3", "e8m0"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    mx.lib()
+
+
+def dev(x):
+    return bf16_dev(x) if x.dtype == np.uint16 else f32_dev(x)
+
+
+def check_quant(x, block, fmt, g=1.0, ld=None):
+    rows, k = x.shape
+    if ld is None:
+        xd = dev(x)
+    else:
+        wide = np.zeros((rows, ld), dtype=x.dtype)
+        wide[:, :k] = x
+        xd = dev(wide)[:, :k]
+    c, s = mx.mx_quantize_fp8(xd, block, fmt, g)
+    rc, rs = oracle.quantize_fp8(x, block, fmt, g)
+    np.testing.assert_array_equal(to_host_bits(s), rs)
+    np.testing.assert_array_equal(to_host_bits(c), rc)
+    return c, s, rc, rs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [4, 8, 16, 32, 64, 128, 256])
+def test_quantize_fp8(dtype, fmt, block):
+    x = synth.normal((24, 1024), dtype, f"q8.{dtype}", 0.3, 0.01, 20.0)
+    check_quant(x, block, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("g", [0.37, 3.1e-3])
+def test_quantize_fp8_tensor_scale(fmt, g):
+    g = float(np.float32(g))
+    x = synth.normal((16, 512), "bf16", "q8.g", 0.05, 0.01, 20.0)
+    check_quant(x, 32, fmt, g)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [8, 32, 128])
+def test_quantize_fp8_edge_values(fmt, block):
+    # every scale byte, every bf16 magnitude under a fixed maximum, ties, zeros, subnormals
+    check_quant(edge_tensor(512), block, fmt)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape,block,ld", [((9, 36), 4, None), ((7, 100), 4, None), ((20, 512), 32, 516),
+                                            ((3, 96), 32, None)])
+def test_quantize_fp8_generic_path(dtype, shape, block, ld):
+    # k % 8 != 0 or rows not 16-byte aligned: one thread per block
+    x = synth.normal(shape, dtype, f"q8g.{dtype}.{shape}", 0.1, 0.02, 20.0)
+    check_quant(x, block, "ue5m3", 1.0, ld)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [4, 32, 256])
+@pytest.mark.parametrize("g", [1.0, 0.37])
+def test_dequantize_fp8(out, fmt, block, g):
+    g = float(np.float32(g))
+    x = np.concatenate([synth.normal((12, 512), "bf16", "d8", 0.02, 0.01, 20.0), edge_tensor(512)[:40]])
+    rc, rs = oracle.quantize_fp8(x, block, fmt, g)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    y = mx.mx_dequantize_fp8(torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV), block, fmt, g, out_dtype=dt)
+    ref = oracle.dequantize_fp8(rc, rs, block, fmt, g, out)
+    got = to_host_bits(y)
+    if out == "f32":
+        np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    else:
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_dequantize_fp8_every_code_and_scale():
+    # all 256 element bytes (0x7F / 0xFF read as NaN) under every finite scale byte of each format
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    for fmt in FMTS:
+        scales = np.arange(256, dtype=np.uint8).reshape(256, 1).repeat(8, axis=1)
+        ok = np.array([np.isfinite(oracle.scale_value(b, fmt)) for b in range(256)])
+        c, s = codes[ok], scales[ok]
+        for out in ("f32", "bf16"):
+            dt = torch.float32 if out == "f32" else torch.bfloat16
+            y = mx.mx_dequantize_fp8(torch.from_numpy(np.ascontiguousarray(c)).to(DEV),
+                                     torch.from_numpy(np.ascontiguousarray(s)).to(DEV), 32, fmt, 1.0, out_dtype=dt)
+            ref = oracle.dequantize_fp8(c, s, 32, fmt, 1.0, out)
+            got = to_host_bits(y)
+            if out == "f32":
+                np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+            else:
+                np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 17, 100])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_fp8(m, fmt):
+    k, n = 1024, 200
+    x = synth.normal((m, k), "bf16", f"g8.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", "g8.w", 0.02, 0.01, 20.0)
+    rc, rs = oracle.quantize_fp8(w, 32, fmt)
+    cd, sd = torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV)
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 32, fmt)
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, fmt, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 m={m} {fmt} {dt}")
+
+
+@pytest.mark.parametrize("block", [4, 8, 16, 64, 128, 256])
+def test_gemm_fp8_blocks_tail_and_scale(block):
+    # k = 1280 (a partial last 128-k window), ragged n, per-tensor g
+    m, n, k = 7, 77, 1280
+    g = float(np.float32(0.0291))
+    x = synth.normal((m, k), "bf16", "g8b.x", 1.0)
+    w = synth.normal((n, k), "bf16", f"g8b.w.{block}", 0.5, 0.01, 20.0)
+    rc, rs = oracle.quantize_fp8(w, block, "ue5m3", g)
+    y = mx.mx_gemm_fp8(bf16_dev(x), torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV), block, "ue5m3", g,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm_fp8(x, rc, rs, block, "ue5m3", g)
+    assert_gemm_close(to_host_bits(y), yref, aref, False, f"w8 block {block}")
+
+
+def test_gemm_fp8_generic_path():
+    # k % 32 != 0: one thread per output
+    m, n, k = 5, 33, 72
+    x = synth.normal((m, k), "bf16", "g8g.x", 1.0)
+    w = synth.normal((n, k), "bf16", "g8g.w", 0.02)
+    rc, rs = oracle.quantize_fp8(w, 8, "e8m0")
+    y = mx.mx_gemm_fp8(bf16_dev(x), torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV), 8, "e8m0",
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 8, "e8m0")
+    assert_gemm_close(to_host_bits(y), yref, aref, False, "w8 generic")
+
+
+def test_fallback_scenario_sigma_below_1e4():
+    # a sigma = 5e-5 layer: FP4 with E4M3 block scales flushes every block to zero, which the
+    # fallback rule catches.  FP8 elements divide the block maximum by 448, so their scale must
+    # reach lower still: E4M3 and UE5M3 scales flush this tensor too, E8M0 scales keep it
+    w = synth.normal((64, 4096), "bf16", "fb.w", 5e-5)
+    wd = bf16_dev(w)
+    sigma = float(mx.mx_tensor_stats(wd).cpu().numpy()[1])
+    assert mx.mx_use_fp8(sigma) and oracle.use_fp8(sigma)
+    c4, s4 = mx.mx_quantize(wd, 32, "e4m3")
+    assert torch.count_nonzero(s4).item() == 0  # every FP4 block flushed
+    _, s8u, _, _ = check_quant(w, 32, "ue5m3")
+    assert torch.count_nonzero(s8u).item() == 0
+    c8, s8, _, _ = check_quant(w, 32, "e8m0")
+    y8 = mx.mx_dequantize_fp8(c8, s8, 32, "e8m0", out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    wf = synth.bf16_to_f32(w).astype(np.float64)
+    assert np.mean((y8 - wf) ** 2) < 1e-2 * np.mean(wf ** 2)  # FP4 lost all of it (ratio 1)
+
+
+def test_gemm_fp8_decode_shape_sampled():
+    # decode GEMV shape: m 1, k 4096, n 14336, block 32, E8M0, sampled columns against the oracle
+    x = synth.c3_x(1)
+    w = synth.c3_weight(14336)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize_fp8(wd, 32, "e8m0")
+    cols = np.array([0, 1, 777, 8191, 14335])
+    rc, rs = oracle.quantize_fp8(w[cols], 32, "e8m0")
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, "e8m0", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 32, "e8m0")
+    assert_gemm_close(to_host_bits(y)[:, cols], yref, aref, False, "w8 decode")
