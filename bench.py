@@ -204,6 +204,7 @@ def main():
     torch.cuda.empty_cache()
 
     rows = None if args.no_rows else measure_rows(mx, L, torch, np, synth, dev, stream)
+    fp8 = None if args.no_rows else measure_fp8(mx, L, torch, np, synth, dev, stream)
 
     cpu = None if args.no_cpu else cpu_baseline(np, synth)
 
@@ -222,6 +223,7 @@ def main():
         "error_split": error_split,
         "block_policy": block_policy,
         "rows": rows,
+        "fp8_fallback": fp8,
     }
     print(json.dumps(out), flush=True)
 
@@ -302,6 +304,100 @@ def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
             "fake_quant.s0.02.B32.e4m3": {"us": round(ft * 1e3, 2), "bytes": 4 * n, "GB/s": round(fgbs, 1),
                                           "frac_hbm": round(fgbs * 1e9 / PEAK_HBM, 3)},
             "per_config": per}
+
+
+def measure_fp8(mx, L, torch, np, synth, dev, stream):
+    """The FP8 weight fallback: E4M3-element quantize / dequantize of the Llama-7B FFN weight
+    (block 32, E8M0), the W8A16 decode GEMV (distinct weights back to back, graph replay, as
+    the W4A16 rows) and the 70B-FFN prefill GEMM."""
+    res = {}
+    bf = torch.bfloat16
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
+
+    n = C2_ROWS * C2_K
+    ws = [dev_bf16(synth.c2_weight(0.02))]
+    ws.append(ws[0].clone())
+    ws.append(ws[0].clone())
+    outs = [mx.mx_quantize_fp8(w, 32, "e8m0") for w in ws]
+    yq = [torch.empty((C2_ROWS, C2_K), dtype=bf, device=dev) for _ in range(3)]
+    qb = 2 * n + n + n // 32
+    for kind, fn in (("quantize", lambda i: mx.mx_quantize_fp8(ws[i], 32, "e8m0", codes=outs[i][0], scales=outs[i][1])),
+                     ("dequantize", lambda i: mx.mx_dequantize_fp8(outs[i][0], outs[i][1], 32, "e8m0", y=yq[i]))):
+        for i in range(3):
+            fn(i)
+        evs = []
+        for r in range(9):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(r % 3)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)[4]
+        gbs = qb / (t * 1e-3) / 1e9
+        res[f"{kind}_fp8.B32.e8m0.n{C2_ROWS}.k{C2_K}"] = {"us": round(t * 1e3, 2), "GB/s": round(gbs, 1),
+                                                         "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3)}
+    del ws, outs, yq
+
+    for nn, copies in ((4096, 64), (14336, 20)):
+        w = dev_bf16(synth.c3_weight(nn))
+        c0, s0 = mx.mx_quantize_fp8(w, 32, "e8m0")
+        del w
+        cs = [(c0.clone(), s0.clone()) for _ in range(copies)]
+        for m in (1, 16):
+            x = dev_bf16(synth.c3_x(m))
+            y = torch.empty((m, nn), dtype=bf, device=dev)
+
+            def decode_step():
+                sp = torch.cuda.current_stream().cuda_stream
+                for c, sc in cs:
+                    st = L.mx_gemm_fp8(x.data_ptr(), m, nn, 4096, 4096, c.data_ptr(), sc.data_ptr(), 32,
+                                       mx.FMT["e8m0"], 1.0, y.data_ptr(), 1, nn, sp)
+                    if st:
+                        raise mx.MXError(st, "mx_gemm_fp8")
+
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                decode_step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                decode_step()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            tot = e0.elapsed_time(e1) / 5
+            byt = nn * 4096 + nn * 4096 // 32 + m * 4096 * 2 + m * nn * 2
+            gbs = byt * copies / (tot * 1e-3) / 1e9
+            res[f"gemv_w8.m{m}.n{nn}.k4096"] = {
+                "GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
+                "us_per_launch": round(tot * 1e3 / copies, 2),
+                "launches": f"{copies} distinct weights back to back (graph replay)"}
+            del graph
+        del cs, c0, s0
+
+    w = dev_bf16(synth.c4_weight())
+    c8, s8 = mx.mx_quantize_fp8(w, 32, "e8m0")
+    del w
+    x = dev_bf16(synth.c4_x())
+    M, N, K = 2048, 28672, 8192
+    y = torch.empty((M, N), dtype=bf, device=dev)
+    fn = lambda: mx.mx_gemm_fp8(x, c8, s8, 32, "e8m0", y=y)
+    time_launches(torch, stream, [fn], reps=1)
+    ts = time_launches(torch, stream, [fn], reps=3)
+    t = sorted(ts)[1]
+    tf = 2 * M * N * K / (t * 1e-3) / 1e12
+    res[f"gemm_w8.m{M}.n{N}.k{K}"] = {"TFLOP/s": round(tf, 1), "frac_peak_bf16": round(tf * 1e12 / PEAK_BF16, 4),
+                                      "ms": round(t, 3)}
+    log("fp8 fallback: " + ", ".join(f"{k} {v.get('GB/s', v.get('TFLOP/s'))}" for k, v in res.items()))
+    return res
 
 
 def measure_block_policy(mx, torch, inputs, error_split, dev, stream):
