@@ -158,9 +158,10 @@ mx_status mx_quant_error(const void* x, mx_dtype x_type, int64_t rows, int64_t k
  * to a / (448 g) (448, the largest E4M3 magnitude, in place of 6), and every element becomes
  * the E4M3 byte (OCP E4M3FN: sign, 4 exponent bits with bias 7 and subnormals, 3 mantissa
  * bits, largest magnitude 448) nearest to |x| / (s g), clipped at 448, ties to the even
- * code, with the sign bit of x; a zero scale codes the block as +-0.  Note that E4M3 block
- * scales (smallest 2^-9) flush blocks with a < 448 * 2^-10 * g; UE5M3 or E8M0 scales, or g,
- * keep small weights.
+ * code, with the sign bit of x; a zero scale codes the block as +-0.  Note that the scale
+ * falls below a / 448: E4M3 scales (smallest 2^-9) flush blocks with a <= 448 * 2^-10 * g and
+ * UE5M3 scales (smallest 2^-17) those with a <= 448 * 2^-18 * g; E8M0 scales, or a per-tensor
+ * g, keep small weights.
  *  codes : rows x k bytes, row-major (one byte per element).
  *  scales: rows x k/block bytes, row-major (MX_LAYOUT_ROWMAJOR order).
  *
