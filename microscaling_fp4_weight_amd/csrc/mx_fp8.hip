@@ -85,7 +85,30 @@ __device__ __forceinline__ uint32_t elem_byte(uint32_t xb, const Blk& p)
 // loads, 8 code bytes stored); blocks of 4 are two per lane, blocks of 8 one per lane, larger
 // ones span BLOCK / 8 adjacent lanes that combine their absmax with lane shuffles.
 // ---------------------------------------------------------------------------------------
-template <int BLOCK, int FMT, bool BF16>
+// bf16 input, g == 1: the hardware converter (divides by the power of two of its scale
+// argument, rounds to nearest even, keeps the sign; quotients past 464 it turns into NaN
+// rather than 448, so the input is first clamped to +-448 times that power of two) after the
+// exact pre-scale by 1/m of the FP4 path for E4M3 / UE5M3 scale mantissas m: for bf16 inputs the
+// pre-scaled value lies on the same side of every decision point as the exact quotient and
+// lands exactly on a tie when the quotient is one (the same argument as for the E2M1 grid,
+// whose decision points are a subset of finer ones; checked by the parity tests around
+// every decision point of every scale mantissa).
+typedef __attribute__((ext_vector_type(2))) short i16x2;
+
+template <int FMT, int SEL>
+__device__ __forceinline__ i16x2 enc_fp8_pair(i16x2 old, uint32_t wd, const EncG1& p, float lim)
+{
+    float lo = u2f(wd << 16), hi = u2f(wd & 0xFFFF0000u);
+    if constexpr (FMT != FMT_E8M0) {
+        lo = __builtin_fmaf(lo, p.chi, lo * p.clo);
+        hi = __builtin_fmaf(hi, p.chi, hi * p.clo);
+    }
+    lo = __builtin_amdgcn_fmed3f(lo, -lim, lim);
+    hi = __builtin_amdgcn_fmed3f(hi, -lim, lim);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, lo, hi, p.pow2, SEL != 0);
+}
+
+template <int BLOCK, int FMT, bool BF16, bool HW>
 __global__ __launch_bounds__(THREADS) void quantize_fp8_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes,
                                                                FastDiv upr_div, uint32_t upr, uint32_t total,
                                                                double g, uint8_t* __restrict__ codes,
@@ -140,17 +163,41 @@ __global__ __launch_bounds__(THREADS) void quantize_fp8_kernel(const uint8_t* __
         }
     }
 
-    uint32_t cb[8], sb[NB];
+    uint32_t sb[NB];
+    u32x2 cv;
+    if constexpr (HW) {  // bf16 input, g == 1
+        i16x2 h0 = {0, 0}, h1 = {0, 0};
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        sb[b] = scale_code_g<FMT>(amax[b], 448.0 * g);
-        const Blk p = block_params<FMT>(sb[b], g);
+        for (int b = 0; b < NB; ++b) {
+            sb[b] = scale_code_g<FMT>(amax[b], 448.0);
+            const EncG1 p = enc_params_g1<FMT>(sb[b]);
+            const float lim = 448.0f * p.pow2;  // 448 * 2^E (exact, also for 2^-127)
 #pragma unroll
-        for (int e = 0; e < EPB; ++e) cb[b * EPB + e] = elem_byte(xb[b * EPB + e], p);
+            for (int pr = 0; pr < EPB / 2; ++pr) {
+                const int j = b * (EPB / 2) + pr;  // element pair j = elements 2j, 2j+1
+                const uint32_t wd = (xb[2 * j] >> 16) | (xb[2 * j + 1] & 0xFFFF0000u);
+                switch (j) {
+                    case 0: h0 = enc_fp8_pair<FMT, 0>(h0, wd, p, lim); break;
+                    case 1: h0 = enc_fp8_pair<FMT, 1>(h0, wd, p, lim); break;
+                    case 2: h1 = enc_fp8_pair<FMT, 0>(h1, wd, p, lim); break;
+                    default: h1 = enc_fp8_pair<FMT, 1>(h1, wd, p, lim); break;
+                }
+            }
+        }
+        cv = u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+    } else {
+        uint32_t cb[8];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            sb[b] = scale_code_g<FMT>(amax[b], 448.0 * g);
+            const Blk p = block_params<FMT>(sb[b], g);
+#pragma unroll
+            for (int e = 0; e < EPB; ++e) cb[b * EPB + e] = elem_byte(xb[b * EPB + e], p);
+        }
+        cv = u32x2{cb[0] | (cb[1] << 8) | (cb[2] << 16) | (cb[3] << 24),
+                   cb[4] | (cb[5] << 8) | (cb[6] << 16) | (cb[7] << 24)};
     }
     if (!act) return;
-    const u32x2 cv = {cb[0] | (cb[1] << 8) | (cb[2] << 16) | (cb[3] << 24),
-                      cb[4] | (cb[5] << 8) | (cb[6] << 16) | (cb[7] << 24)};
     *reinterpret_cast<u32x2*>(codes + (int64_t)row * k + (int64_t)c8 * 8) = cv;
     uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
     if constexpr (NB == 2) {
@@ -414,9 +461,14 @@ static hipError_t launch_q8(const QuantArgs& a, hipStream_t st)
     const dim3 grid((total + f8::THREADS - 1) / f8::THREADS);
 #define MXQ8(B)                                                                                              \
     case B:                                                                                                  \
-        hipLaunchKernelGGL((f8::quantize_fp8_kernel<B, FMT, BF16>), grid, dim3(f8::THREADS), 0, st,         \
-                           static_cast<const uint8_t*>(a.x), a.ldx * esz, fd, upr, total, a.g, a.codes,     \
-                           a.scales, a.k);                                                                   \
+        if (BF16 && a.g == 1.0)                                                                              \
+            hipLaunchKernelGGL((f8::quantize_fp8_kernel<B, FMT, BF16, BF16>), grid, dim3(f8::THREADS), 0, st, \
+                               static_cast<const uint8_t*>(a.x), a.ldx * esz, fd, upr, total, a.g, a.codes, \
+                               a.scales, a.k);                                                               \
+        else                                                                                                 \
+            hipLaunchKernelGGL((f8::quantize_fp8_kernel<B, FMT, BF16, false>), grid, dim3(f8::THREADS), 0, st, \
+                               static_cast<const uint8_t*>(a.x), a.ldx * esz, fd, upr, total, a.g, a.codes, \
+                               a.scales, a.k);                                                               \
         break;
     switch (a.block) {
         MXQ8(4) MXQ8(8) MXQ8(16) MXQ8(32) MXQ8(64) MXQ8(128) MXQ8(256)

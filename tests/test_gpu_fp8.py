@@ -183,3 +183,42 @@ def test_gemm_fp8_decode_shape_sampled():
     torch.cuda.synchronize()
     yref, aref = oracle.gemm_fp8(x, rc, rs, 32, "e8m0")
     assert_gemm_close(to_host_bits(y)[:, cols], yref, aref, False, "w8 decode")
+
+
+def _decision_point_tensor(fmt, scale_bytes):
+    """bf16 blocks of 32 whose maximum is 448 s (the block scale is then exactly s) and whose
+    other elements are the bf16 values at and around s times every E4M3 decision point (the
+    midpoints between neighbouring values), both signs."""
+    table = np.array([oracle.e4m3_value(c) for c in range(0x7F)])
+    mids = (table[:-1] + table[1:]) / 2
+    blocks = []
+    for sb in scale_bytes:
+        s = oracle.scale_value(sb, fmt)
+        t = (mids * s).astype(np.float32)
+        bits = (t.view(np.uint32) >> 16).astype(np.int64)  # bf16 at or just below, then neighbours
+        cand = np.concatenate([bits - 1, bits, bits + 1, bits + 2])
+        vals = (cand.astype(np.uint32) << 16).view(np.float32)
+        vals = vals[(vals > 0) & (vals <= 448 * s)]
+        vals = np.where(np.arange(vals.size) % 2 == 0, vals, -vals).astype(np.float32)
+        pad = (-vals.size) % 31
+        vals = np.concatenate([vals, np.zeros(pad, dtype=np.float32)]).reshape(-1, 31)
+        top = np.full((vals.shape[0], 1), 448 * s, dtype=np.float32)
+        blocks.append(np.concatenate([top, vals], axis=1))
+    x = np.concatenate(blocks).reshape(-1)
+    pad = (-x.size) % 1024
+    x = np.concatenate([x, np.zeros(pad, dtype=np.float32)]).reshape(-1, 1024)
+    b = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(synth.bf16_to_f32(b), x)  # every value is a bf16 value
+    return b
+
+
+@pytest.mark.parametrize("fmt,scale_bytes", [
+    ("e4m3", [8 * e + m for e in range(1, 13) for m in range(8)]),
+    ("ue5m3", [8 * e + m for e in range(6, 20) for m in range(8)]),
+    ("e8m0", list(range(100, 140))),
+])
+def test_quantize_fp8_every_decision_point(fmt, scale_bytes):
+    # exact decisions of the bf16 / g == 1 fast path at every E4M3 midpoint for every scale
+    # mantissa (E4M3, UE5M3) and a range of powers of two (E8M0)
+    x = _decision_point_tensor(fmt, scale_bytes)
+    check_quant(x, 32, fmt)
