@@ -510,17 +510,19 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     for nn, copies in ((4096, 64), (14336, 20)):
         w = dev_bf16(synth.c3_weight(nn))
         c0, s0 = mx.mx_quantize(w, 32, "e8m0")
+        _, s0p = mx.mx_quantize(w, 32, "e8m0", layout="preshuffled")  # same codes
         del w
-        cs = [(c0.clone(), s0.clone()) for _ in range(copies)]
-        for m in (1, 4, 16):
+        cs = [(c0.clone(), s0.clone(), s0p.clone()) for _ in range(copies)]
+        for m, lay in ((1, 0), (1, 2), (4, 0), (16, 0)):
             x = dev_bf16(synth.c3_x(m))
             y = torch.empty((m, nn), dtype=bf, device=dev)
 
             def decode_step():
                 sp = torch.cuda.current_stream().cuda_stream
-                for c, s in cs:
-                    st = L.mx_gemm(x.data_ptr(), m, nn, 4096, 4096, c.data_ptr(), s.data_ptr(), 32,
-                                   mx.FMT["e8m0"], 1.0, 0, 0, y.data_ptr(), 1, nn, None, 0, sp)
+                for c, s, sps in cs:
+                    st = L.mx_gemm(x.data_ptr(), m, nn, 4096, 4096, c.data_ptr(),
+                                   (sps if lay == 2 else s).data_ptr(), 32, mx.FMT["e8m0"], 1.0, lay, 0,
+                                   y.data_ptr(), 1, nn, None, 0, sp)
                     if st:
                         raise mx.MXError(st, "mx_gemm")
 
@@ -543,13 +545,13 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
             tot = e0.elapsed_time(e1) / reps  # ms per decode step (copies launches)
             byt = gemv_bytes(m, nn, 4096, 32)
             gbs = byt * copies / (tot * 1e-3) / 1e9
-            rows[f"gemv_a16.m{m}.n{nn}.k4096"] = {
+            rows[f"gemv_a16.m{m}.n{nn}.k4096" + (".preshuffled_scales" if lay == 2 else "")] = {
                 "GB/s": round(gbs, 1), "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
                 "us_per_launch": round(tot * 1e3 / copies, 2),
                 "TFLOP/s": round(2 * m * nn * 4096 * copies / (tot * 1e-3) / 1e12, 2),
                 "launches": f"{copies} distinct weights back to back (graph replay)"}
             del graph
-        del cs, c0, s0
+        del cs, c0, s0, s0p
         log(f"decode GEMV n={nn} done")
 
     # 70B-FFN prefill: W4A16 and W4A4
@@ -594,8 +596,20 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     rows["quantize.ue5m3.g.n53248.k16384"] = {"GB/s": round(gbs, 1),
                                               "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3),
                                               "ms": round(t, 3)}
-    del w
+    c5p, s5p = mx.mx_quantize(w, 32, "ue5m3", g, layout="preshuffled")  # same codes as c5
+    del w, c5p
     torch.cuda.empty_cache()
+    x = dev_bf16(synth.c5_x(1))
+    y = torch.empty((1, N), dtype=bf, device=dev)
+    fn = lambda: mx.mx_gemm(x, c5, s5p, 32, "ue5m3", g, "a16", y=y, layout="preshuffled")
+    time_launches(torch, stream, [fn])
+    ts = time_launches(torch, stream, [fn], reps=3)
+    t = sorted(ts)[1]
+    gbs = gemv_bytes(1, N, K, 32) / (t * 1e-3) / 1e9
+    rows[f"gemm_a16.ue5m3.g.m1.n{N}.k{K}.preshuffled_scales"] = {
+        "TFLOP/s": round(2 * N * K / (t * 1e-3) / 1e12, 2), "ms": round(t, 3), "GB/s": round(gbs, 1),
+        "frac_hbm": round(gbs * 1e9 / PEAK_HBM, 3)}
+    del x, y, s5p
     for m in (1, 256, 4096):
         x = dev_bf16(synth.c5_x(m))
         y = torch.empty((m, N), dtype=bf, device=dev)

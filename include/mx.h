@@ -38,6 +38,16 @@
  *  grouped in tiles of 256 (T = r / 256, t = r % 256) and blocks in stages of 8 (256
  *  elements; S = b / 8, u = b % 8); with KS = ceil(k / 256) stages, the scale of (r, b) is
  *  byte  2048 (T KS + S) + 1024 (t / 128) + 32 (t % 32) + 8 ((t / 32) % 4) + u.
+ * Layout MX_LAYOUT_PRESHUFFLED (block 32; [MXS] section 3.2 item 2 and section 5.3 item 3:
+ *  scale factors grouped in aligned words, tensors rearranged for the kernel that reads
+ *  them): the same codes; the scales in the order the m = 1 GEMV reads them, so that one
+ *  8-byte word holds one 32-element block's scales of 8 consecutive rows.  Rows are grouped
+ *  by 8 (R = r / 8, t = r % 8) and blocks in chunks of 64 (2048 elements; C = b / 64,
+ *  u = b % 64); with KC = ceil(k / 2048) chunks, the scale of (r, b) is byte
+ *  512 (R KC + C) + 8 u + t.  Bytes of the last chunk past the row's last block are written
+ *  as 0; bytes of rows past the last row (rows % 8 != 0) are not written.  Size
+ *  ceil(rows / 8) * KC * 512 bytes (mx_scale_bytes).  Read by mx_dequantize and by mx_gemm
+ *  in W4A16 mode with m == 1.
  *  The buffer holds ceil(rows / 256) KS 2048 bytes (mx_scale_bytes).  Bytes of blocks
  *  past the end of k in a row's last stage are written as 0 by mx_quantize; bytes of rows
  *  past the end are never written nor used.
@@ -79,7 +89,7 @@ typedef enum {
 
 typedef enum { MX_SCALE_E4M3 = 0, MX_SCALE_UE5M3 = 1, MX_SCALE_E8M0 = 2 } mx_scale_fmt;
 typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
-typedef enum { MX_LAYOUT_ROWMAJOR = 0, MX_LAYOUT_TILED = 1 } mx_layout;
+typedef enum { MX_LAYOUT_ROWMAJOR = 0, MX_LAYOUT_TILED = 1, MX_LAYOUT_PRESHUFFLED = 2 } mx_layout;
 typedef enum { MX_A16 = 0, MX_A4 = 1 } mx_act_mode;
 
 /*
@@ -88,13 +98,15 @@ typedef enum { MX_A16 = 0, MX_A4 = 1 } mx_act_mode;
  *  block      : block size along k, one of 4, 8, 16, 32, 64, 128, 256; k % block == 0.
  *  fmt        : block-scale format.
  *  tensor_scale: per-tensor fp32 scale g ([MXS] section 3.1 item 3; 1.0 for none).
- *  layout     : MX_LAYOUT_ROWMAJOR or MX_LAYOUT_TILED (scale order, above).
+ *  layout     : MX_LAYOUT_ROWMAJOR, MX_LAYOUT_TILED or MX_LAYOUT_PRESHUFFLED (scale order,
+ *               above).
  *  codes      : output, rows x k/2 bytes (layout above).
  *  scales     : output, mx_scale_bytes(rows, k, block, layout) bytes.
  * Errors: MX_ERR_INVALID_ARG for a null pointer, rows/k/ld_x negative or ld_x < k, k odd,
  * a block size outside the list, k % block != 0, an unknown fmt/x_type/layout, or g not a
  * finite normal positive number; MX_ERR_UNSUPPORTED for MX_LAYOUT_TILED with block != 32
- * or k > 4,194,304; MX_ERR_ALIGNMENT for a misaligned pointer.
+ * or k > 4,194,304, or MX_LAYOUT_PRESHUFFLED with block != 32; MX_ERR_ALIGNMENT for a
+ * misaligned pointer.
  * Codes and scale bytes are bit-exact with the definition above.
  */
 mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, int64_t ld_x,
@@ -236,6 +248,8 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act
  *               bytes (mx_quantize output for an n x k weight).
  *  block, fmt, tensor_scale, layout: those of the weight.  MX_LAYOUT_TILED weights are
  *               accepted in MX_A4 mode with k % 128 == 0 (MX_ERR_UNSUPPORTED otherwise);
+ *               MX_LAYOUT_PRESHUFFLED weights in MX_A16 mode with m == 1 and ld_x a
+ *               multiple of 8 (MX_ERR_UNSUPPORTED otherwise);
  *               they make the W4A4 product faster.
  *  mode       : MX_A16 -- X is used as given (bf16 x dequantized weight);
  *               MX_A4  -- X is first MX-quantized along k with block 32, E8M0 scales and

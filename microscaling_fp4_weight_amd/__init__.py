@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_PKG, "libmx.so")
 FMT = {"e4m3": 0, "ue5m3": 1, "e8m0": 2}
 DTYPE = {"f32": 0, "bf16": 1}
 MODE = {"a16": 0, "a4": 1}
-LAYOUT = {"rowmajor": 0, "tiled": 1}
+LAYOUT = {"rowmajor": 0, "tiled": 1, "preshuffled": 2}
 STATUS = {0: "MX_OK", -1: "MX_ERR_INVALID_ARG", -2: "MX_ERR_UNSUPPORTED", -3: "MX_ERR_ALIGNMENT",
           -4: "MX_ERR_HIP"}
 
@@ -125,7 +125,7 @@ def mx_quantize(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0
                 scales: torch.Tensor | None = None, stream=None):
     """MX-quantize a 2-D bf16/fp32 GPU tensor (rows x k) along k.
     Returns (codes uint8 rows x k/2, scales uint8: rows x k/block for layout "rowmajor", a
-    flat buffer of mx_scale_bytes(...) bytes for layout "tiled")."""
+    flat buffer of mx_scale_bytes(...) bytes for layouts "tiled" and "preshuffled")."""
     rows, k, ld = _rows_ld(x, "x")
     if codes is None:
         codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)

@@ -44,11 +44,13 @@ mx_status check_quantized(int64_t rows, int64_t k, int block, mx_scale_fmt fmt, 
         return MX_ERR_INVALID_ARG;
     if (fmt != MX_SCALE_E4M3 && fmt != MX_SCALE_UE5M3 && fmt != MX_SCALE_E8M0)
         return MX_ERR_INVALID_ARG;
-    if (layout != MX_LAYOUT_ROWMAJOR && layout != MX_LAYOUT_TILED) return MX_ERR_INVALID_ARG;
+    if (layout != MX_LAYOUT_ROWMAJOR && layout != MX_LAYOUT_TILED && layout != MX_LAYOUT_PRESHUFFLED)
+        return MX_ERR_INVALID_ARG;
     if (!valid_g(g)) return MX_ERR_INVALID_ARG;
     // the tiled scale layout is defined for 32-element blocks, and rows are processed in
     // whole 256-row tiles per launch, which bounds k as for the matmul
     if (layout == MX_LAYOUT_TILED && (block != 32 || k > kMaxGemmK)) return MX_ERR_UNSUPPORTED;
+    if (layout == MX_LAYOUT_PRESHUFFLED && block != 32) return MX_ERR_UNSUPPORTED;
     return MX_OK;
 }
 
@@ -57,13 +59,16 @@ int64_t launch_rows(int64_t k, mx_layout layout)
 {
     int64_t step = chunk_rows(k);
     if (layout == MX_LAYOUT_TILED) step = step < mxk::kTileRows ? mxk::kTileRows : step / mxk::kTileRows * mxk::kTileRows;
+    if (layout == MX_LAYOUT_PRESHUFFLED) step = step < mxk::kPreRows ? mxk::kPreRows : step / mxk::kPreRows * mxk::kPreRows;
     return step;
 }
 
 // Offset of row r0's scales (r0 a multiple of 256 for tiled scales).
 int64_t scale_offset(int64_t r0, int64_t k, int block, mx_layout layout)
 {
-    return layout == MX_LAYOUT_TILED ? r0 / mxk::kTileRows * mxk::tiled_stages(k) * mxk::kTileBytes : r0 * (k / block);
+    if (layout == MX_LAYOUT_TILED) return r0 / mxk::kTileRows * mxk::tiled_stages(k) * mxk::kTileBytes;
+    if (layout == MX_LAYOUT_PRESHUFFLED) return r0 / mxk::kPreRows * mxk::pre_chunks(k) * mxk::kPreBytes;
+    return r0 * (k / block);
 }
 
 }  // namespace
@@ -75,6 +80,7 @@ size_t mx_scale_bytes(int64_t rows, int64_t k, int block, mx_layout layout)
     if (rows < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;
     if (layout == MX_LAYOUT_ROWMAJOR) return (size_t)rows * (size_t)(k / block);
     if (layout == MX_LAYOUT_TILED && block == 32 && k <= kMaxGemmK) return (size_t)mxk::tiled_scale_bytes(rows, k);
+    if (layout == MX_LAYOUT_PRESHUFFLED && block == 32) return (size_t)mxk::pre_scale_bytes(rows, k);
     return 0;
 }
 
@@ -103,7 +109,7 @@ mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, i
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
     const int esize = x_type == MX_BF16 ? 2 : 4;
     if (k > kMaxK) return MX_ERR_UNSUPPORTED;
-    mxk::QuantArgs a;
+    mxk::QuantArgs a{};
     a.x = x;
     a.bf16 = x_type == MX_BF16;
     a.rows = rows;
@@ -116,6 +122,7 @@ mx_status mx_quantize(const void* x, mx_dtype x_type, int64_t rows, int64_t k, i
     a.scales = scales;
     a.fast = (k % 32 == 0) && ((ld_x * esize) % 16 == 0);
     a.ts_ks = layout == MX_LAYOUT_TILED ? (uint32_t)mxk::tiled_stages(k) : 0u;
+    a.ps_cb = layout == MX_LAYOUT_PRESHUFFLED ? (uint32_t)mxk::pre_chunks(k) : 0u;
     const int64_t step = launch_rows(k, layout);
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         mxk::QuantArgs c = a;
@@ -141,7 +148,7 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
     if (!aligned16(y) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGNMENT;
     const int esize = y_type == MX_BF16 ? 2 : 4;
     if (k > kMaxK) return MX_ERR_UNSUPPORTED;
-    mxk::DequantArgs a;
+    mxk::DequantArgs a{};
     a.codes = codes;
     a.scales = scales;
     a.rows = rows;
@@ -154,6 +161,7 @@ mx_status mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t row
     a.ldy = ld_y;
     a.fast = (k % 32 == 0) && ((ld_y * esize) % 16 == 0);
     a.ts_ks = layout == MX_LAYOUT_TILED ? (uint32_t)mxk::tiled_stages(k) : 0u;
+    a.ps_cb = layout == MX_LAYOUT_PRESHUFFLED ? (uint32_t)mxk::pre_chunks(k) : 0u;
     const int64_t step = launch_rows(k, layout);
     for (int64_t r0 = 0; r0 < rows; r0 += step) {
         mxk::DequantArgs c = a;
@@ -284,6 +292,7 @@ mx_status mx_quantize_fp8(const void* x, mx_dtype x_type, int64_t rows, int64_t 
     a.scales = scales;
     a.fast = (k % 8 == 0) && ((ld_x * esize) % 16 == 0) && rows * (k / 8) < (int64_t(1) << 31);
     a.ts_ks = 0;
+    a.ps_cb = 0;
     return from_hip(mxk::launch_quantize_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -313,6 +322,7 @@ mx_status mx_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int64_t
     a.ldy = ld_y;
     a.fast = (k % 8 == 0) && ((ld_y * esize) % 16 == 0) && rows * (k / 8) < (int64_t(1) << 31);
     a.ts_ks = 0;
+    a.ps_cb = 0;
     return from_hip(mxk::launch_dequantize_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -393,7 +403,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     if (need && !aligned16(workspace)) return MX_ERR_ALIGNMENT;
     if (k > kMaxGemmK) return MX_ERR_UNSUPPORTED;
 
-    mxk::GemmArgs a;
+    mxk::GemmArgs a{};
     a.x = static_cast<const uint16_t*>(x);
     a.m = m;
     a.n = n;
@@ -408,11 +418,14 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     a.y_bf16 = y_type == MX_BF16;
     a.ldy = ld_y;
     a.ws_tiled = layout == MX_LAYOUT_TILED;
+    a.ws_pre = layout == MX_LAYOUT_PRESHUFFLED;
     a.xq_codes = nullptr;
     a.xq_scales = nullptr;
     // weight scales in the tiled layout are read by the W4A4 matrix-core kernel only
     const bool mfma_a4 = mode == MX_A4 && mxk::a4_uses_mfma(a);
     if (a.ws_tiled && !mfma_a4) return MX_ERR_UNSUPPORTED;
+    // preshuffled weight scales are read by the m = 1 GEMV only
+    if (a.ws_pre && (mode != MX_A16 || m != 1 || (ld_x * 2) % 16 != 0)) return MX_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     // rows of Y per launch: keeps per-launch unit counts (outputs, pre-pass pairs) < 2^29;
@@ -435,7 +448,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
         c.xq_codes = ws + r0 * (k / 2);
         const mx_layout xl = mfma_a4 ? MX_LAYOUT_TILED : MX_LAYOUT_ROWMAJOR;
         c.xq_scales = ws + round256((size_t)m * (size_t)(k / 2)) + scale_offset(r0, k, 32, xl);
-        mxk::QuantArgs q;
+        mxk::QuantArgs q{};
         q.x = c.x;
         q.bf16 = true;
         q.rows = c.m;
@@ -448,6 +461,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
         q.scales = c.xq_scales;
         q.fast = (ld_x * 2) % 16 == 0;  // k % 32 == 0 holds (block 32)
         q.ts_ks = mfma_a4 ? (uint32_t)mxk::tiled_stages(k) : 0u;
+        q.ps_cb = 0;
         if (mxk::launch_quantize(q, s) != hipSuccess) return MX_ERR_HIP;
         if (mxk::launch_gemm_a4(c, s) != hipSuccess) return MX_ERR_HIP;
     }

@@ -302,6 +302,13 @@ __device__ __forceinline__ uint64_t tiled_scale_off(uint32_t row, uint32_t kb, u
            (((r >> 5) & 3u) << 3) + (kb & 7u);
 }
 
+// Byte offset of the scale of (row, 32-element block kb) in the preshuffled layout with cb
+// 2048-k chunks per 8-row group (the layout is described with kPreBytes in mx_internal.h).
+__device__ __forceinline__ uint64_t pre_scale_off(uint32_t row, uint32_t kb, uint32_t cb)
+{
+    return ((uint64_t)(row >> 3) * cb + (kb >> 6)) * 512u + ((kb & 63u) << 3) + (row & 7u);
+}
+
 // ---------------------------------------------------------------------------------------
 // Buffer loads: a resource descriptor carries a byte range, and lanes whose offset is out of
 // range read zero without a branch (used for masked rows and k-tails).

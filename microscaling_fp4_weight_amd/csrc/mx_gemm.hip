@@ -313,7 +313,9 @@ constexpr int DOT_ROWS = 8;
 constexpr int DOT_WAVES = 4;
 constexpr int DOT_CHUNK = 2048;
 
-template <int BLOCK, int FMT, int MM, bool OUT_BF16>
+// PRE: weight scales in the preshuffled layout (block 32): the scale bytes of the lane's block
+// for all 8 rows of the workgroup are one 8-byte word, one load instead of eight.
+template <int BLOCK, int FMT, int MM, bool OUT_BF16, bool PRE = false>
 __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs a)
 {
     __shared__ float red[DOT_WAVES][DOT_ROWS * MM];
@@ -327,7 +329,9 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
     const int64_t c1 = c0 + per < KC ? c0 + per : KC;
 
     const rsrc_t wr = make_rsrc(a.wc + n0 * (a.k / 2), nrows * (K / 2));
-    const rsrc_t sr = make_rsrc(a.ws + n0 * (a.k / BLOCK), nrows * (K / BLOCK));
+    const uint32_t pcb = (uint32_t)((K / 32 + 63) / 64);  // preshuffled: 2048-k chunks per row group
+    const rsrc_t sr = PRE ? make_rsrc(a.ws + (n0 / 8) * pcb * 512, pcb * 512)
+                          : make_rsrc(a.ws + n0 * (a.k / BLOCK), nrows * (K / BLOCK));
     const rsrc_t xr = make_rsrc(a.x, (uint32_t)(a.m * a.ldx * 2));
 
     float acc[DOT_ROWS][MM];
@@ -341,10 +345,13 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
         const bool ok = kk < K;
         u32x4 cw[DOT_ROWS];
         uint64_t sb[DOT_ROWS];
+        uint64_t sv = 0;
+        if constexpr (PRE) sv = bload64(sr, ok ? (uint32_t)c * 512 + 8 * lane : kOOB);
 #pragma unroll
         for (int r = 0; r < DOT_ROWS; ++r) {
             cw[r] = bload128(wr, ok ? r * (K / 2) + kk / 2 : kOOB);
-            sb[r] = bload_lane_scales<BLOCK>(sr, ok ? r * (K / BLOCK) + kk / BLOCK : kOOB);
+            if constexpr (PRE) sb[r] = (sv >> (8 * r)) & 0xFFu;
+            else sb[r] = bload_lane_scales<BLOCK>(sr, ok ? r * (K / BLOCK) + kk / BLOCK : kOOB);
         }
         uint32_t xf[MM][16];
 #pragma unroll
@@ -553,7 +560,10 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
         const dim3 grid((unsigned)((a.n + DOT_ROWS - 1) / DOT_ROWS));
         switch (a.block) {
 #define MXD1(B) case B: \
-    hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
+    if (B == 32 && a.ws_pre) \
+        hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 1, OUT_BF16, true>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
+    else \
+        hipLaunchKernelGGL((gemv_dot_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(64 * DOT_WAVES), 0, st, a); \
     break;
             MXD1(4) MXD1(8) MXD1(16) MXD1(32) MXD1(64) MXD1(128) MXD1(256)
 #undef MXD1

@@ -41,6 +41,7 @@ struct QuantArgs {
     uint8_t* scales;
     bool fast;        // k % 32 == 0 and 16-byte aligned rows
     uint32_t ts_ks;   // 0: row-major scales; else tiled scales with this many 256-k stages
+    uint32_t ps_cb;   // 0: not preshuffled; else preshuffled scales with this many 2048-k chunks
 };
 
 struct DequantArgs {
@@ -55,6 +56,7 @@ struct DequantArgs {
     int64_t ldy;
     bool fast;
     uint32_t ts_ks;   // 0: row-major scales; else tiled scales with this many 256-k stages
+    uint32_t ps_cb;   // 0: not preshuffled; else preshuffled scales with this many 2048-k chunks
 };
 
 struct GemmArgs {
@@ -69,6 +71,7 @@ struct GemmArgs {
     bool y_bf16;
     int64_t ldy;
     bool ws_tiled;            // weight scales in the tiled layout (else row-major)
+    bool ws_pre;              // weight scales in the preshuffled layout (m == 1 GEMV only)
     // W4A4: quantized activations in the workspace (m x k/2 codes; scales tiled for the
     // matrix-core kernel, row-major for the direct one)
     uint8_t* xq_codes;
@@ -80,6 +83,17 @@ struct GemmArgs {
 // them the byte of row r (0..255 in the tile), block b (0..7 in the stage) sits at
 // 1024 (r / 128) + 32 (r % 32) + 8 ((r / 32) % 4) + b.
 constexpr int64_t kTileRows = 256, kTileK = 256, kTileBytes = 2048;
+
+// Preshuffled scale layout (block 32): rows in groups of 8, k in chunks of 2048 (64 blocks);
+// the 512 bytes of a (row group, chunk) pair are contiguous, group-major then chunk, and inside
+// them the byte of row r (0..7 in the group), block b (0..63 in the chunk) sits at 8 b + r, so
+// that one 8-byte word holds one block's scales of all 8 rows.
+constexpr int64_t kPreRows = 8, kPreBlocks = 64, kPreBytes = 512;
+inline int64_t pre_chunks(int64_t k) { return (k / 32 + kPreBlocks - 1) / kPreBlocks; }
+inline int64_t pre_scale_bytes(int64_t rows, int64_t k)
+{
+    return (rows + kPreRows - 1) / kPreRows * pre_chunks(k) * kPreBytes;
+}
 inline int64_t tiled_stages(int64_t k) { return (k + kTileK - 1) / kTileK; }
 inline int64_t tiled_scale_bytes(int64_t rows, int64_t k)
 {

@@ -29,7 +29,7 @@ template <int BLOCK, int FMT, bool BF16, bool G1>
 __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
     const uint8_t* __restrict__ x, int64_t ldx_bytes, FastDiv groups_per_row, uint32_t gpr,
     uint32_t total_groups, double g, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, int64_t k, uint32_t ts_ks)
+    uint8_t* __restrict__ scales, int64_t k, uint32_t ts_ks, uint32_t ps_cb)
 {
     constexpr int NW = BF16 ? 16 : 32;                    // 32-bit words holding 32 elements
     constexpr int NB = BLOCK <= 32 ? 32 / BLOCK : 1;      // blocks (or block parts) per lane
@@ -98,6 +98,12 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
             scales[tiled_scale_off(row, gc, ts_ks)] = (uint8_t)sbyte[0];
             // the blocks that pad the row's last stage read as scale byte 0
             for (uint32_t kb = gpr + gc; kb < 8 * ts_ks; kb += gpr) scales[tiled_scale_off(row, kb, ts_ks)] = 0;
+        }
+    } else if (BLOCK == 32 && ps_cb != 0) {  // preshuffled scale layout (block 32 only)
+        if (active) {
+            scales[pre_scale_off(row, gc, ps_cb)] = (uint8_t)sbyte[0];
+            // the blocks that pad the row's last chunk read as scale byte 0
+            for (uint32_t kb = gpr + gc; kb < 64 * ps_cb; kb += gpr) scales[pre_scale_off(row, kb, ps_cb)] = 0;
         }
     } else if (active) {
         uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
 template <int FMT, bool BF16, bool G1>
 __global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
     const uint8_t* __restrict__ x, int64_t ldx, int64_t rows, int64_t k, int block, double g,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t ts_ks)
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t ts_ks, uint32_t ps_cb)
 {
     const int64_t nb = k / block;
     const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -223,6 +229,9 @@ __global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
     if (ts_ks != 0) {  // tiled scale layout (block 32 only)
         scales[tiled_scale_off((uint32_t)r, (uint32_t)b, ts_ks)] = (uint8_t)sb;
         for (int64_t kb = nb + b; kb < 8 * (int64_t)ts_ks; kb += nb) scales[tiled_scale_off((uint32_t)r, (uint32_t)kb, ts_ks)] = 0;
+    } else if (ps_cb != 0) {  // preshuffled scale layout (block 32 only)
+        scales[pre_scale_off((uint32_t)r, (uint32_t)b, ps_cb)] = (uint8_t)sb;
+        for (int64_t kb = nb + b; kb < 64 * (int64_t)ps_cb; kb += nb) scales[pre_scale_off((uint32_t)r, (uint32_t)kb, ps_cb)] = 0;
     } else {
         scales[r * nb + b] = (uint8_t)sb;
     }
@@ -267,7 +276,7 @@ template <int BLOCK, int FMT, bool G1, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     FastDiv units_per_row, uint32_t upr, uint32_t total_units, int64_t k, double g,
-    uint8_t* __restrict__ y, int64_t ldy_bytes, uint32_t ts_ks)
+    uint8_t* __restrict__ y, int64_t ldy_bytes, uint32_t ts_ks, uint32_t ps_cb)
 {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t wbase = (blockIdx.x * kThreads + (threadIdx.x & ~63u)) * kDeqUnits;
@@ -291,6 +300,8 @@ __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
                 sb[h][1] = v >> 8;
             } else if (BLOCK == 32 && ts_ks != 0) {  // tiled scale layout
                 sb[h][0] = sb[h][1] = scales[tiled_scale_off(row[h], c8[h] / 4, ts_ks)];
+            } else if (BLOCK == 32 && ps_cb != 0) {  // preshuffled scale layout
+                sb[h][0] = sb[h][1] = scales[pre_scale_off(row[h], c8[h] / 4, ps_cb)];
             } else {
                 sb[h][0] = sb[h][1] = sp[(c8[h] * 8) / BLOCK];
             }
@@ -352,15 +363,16 @@ __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
 template <int FMT, bool G1, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void dequantize_generic_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t rows,
-    int64_t k, int block, double g, uint8_t* __restrict__ y, int64_t ldy, uint32_t ts_ks)
+    int64_t k, int block, double g, uint8_t* __restrict__ y, int64_t ldy, uint32_t ts_ks, uint32_t ps_cb)
 {
     const int64_t pairs = k / 2;
     const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (id >= rows * pairs) return;
     const int64_t r = id / pairs, j = id - r * pairs;
     const uint32_t cb = codes[r * pairs + j];
-    const uint32_t sb = ts_ks != 0 ? scales[tiled_scale_off((uint32_t)r, (uint32_t)(j / 16), ts_ks)]
-                                   : scales[r * (k / block) + (2 * j) / block];
+    const uint32_t sb = ts_ks != 0   ? scales[tiled_scale_off((uint32_t)r, (uint32_t)(j / 16), ts_ks)]
+                        : ps_cb != 0 ? scales[pre_scale_off((uint32_t)r, (uint32_t)(j / 16), ps_cb)]
+                                     : scales[r * (k / block) + (2 * j) / block];
     float pow2 = 1.0f, mant = 1.0f;
     double sg = 0.0;
     if constexpr (G1) {
@@ -396,7 +408,7 @@ static hipError_t launch_quantize_fmt(const QuantArgs& a, hipStream_t st)
         const int64_t ldb = a.ldx * (BF16 ? 2 : 4);
         switch (a.block) {
 #define MXQ(B) case B: hipLaunchKernelGGL((quantize_fast_kernel<B, FMT, BF16, G1>), grid, dim3(kThreads), 0, st, \
-                   (const uint8_t*)a.x, ldb, FastDiv::make(gpr), gpr, total, a.g, a.codes, a.scales, a.k, a.ts_ks); break;
+                   (const uint8_t*)a.x, ldb, FastDiv::make(gpr), gpr, total, a.g, a.codes, a.scales, a.k, a.ts_ks, a.ps_cb); break;
             MXQ(4) MXQ(8) MXQ(16) MXQ(32) MXQ(64) MXQ(128) MXQ(256)
 #undef MXQ
             default: return hipErrorInvalidValue;
@@ -405,7 +417,7 @@ static hipError_t launch_quantize_fmt(const QuantArgs& a, hipStream_t st)
         const int64_t n = a.rows * (a.k / a.block);
         const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
         hipLaunchKernelGGL((quantize_generic_kernel<FMT, BF16, G1>), grid, dim3(kThreads), 0, st,
-                           (const uint8_t*)a.x, a.ldx, a.rows, a.k, a.block, a.g, a.codes, a.scales, a.ts_ks);
+                           (const uint8_t*)a.x, a.ldx, a.rows, a.k, a.block, a.g, a.codes, a.scales, a.ts_ks, a.ps_cb);
     }
     return hipGetLastError();
 }
@@ -434,7 +446,7 @@ static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
         const int64_t ldb = a.ldy * (OUT_BF16 ? 2 : 4);
         switch (a.block) {
 #define MXD(B) case B: hipLaunchKernelGGL((dequantize_fast_kernel<B, FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st, \
-                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb, a.ts_ks); break;
+                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb, a.ts_ks, a.ps_cb); break;
             MXD(4) MXD(8) MXD(16) MXD(32) MXD(64) MXD(128) MXD(256)
 #undef MXD
             default: return hipErrorInvalidValue;
@@ -443,7 +455,7 @@ static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
         const int64_t n = a.rows * (a.k / 2);
         const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
         hipLaunchKernelGGL((dequantize_generic_kernel<FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st,
-                           a.codes, a.scales, a.rows, a.k, a.block, a.g, (uint8_t*)a.y, a.ldy, a.ts_ks);
+                           a.codes, a.scales, a.rows, a.k, a.block, a.g, (uint8_t*)a.y, a.ldy, a.ts_ks, a.ps_cb);
     }
     return hipGetLastError();
 }

@@ -134,3 +134,24 @@ def padding_positions(rows: int, k: int) -> np.ndarray:
         pads.append(2048 * ((r // 256) * ks + b // 8) + 1024 * (t // 128) + 32 * (t % 32)
                     + 8 * ((t // 32) % 4) + b % 8)
     return np.concatenate(pads) if pads else np.zeros(0, dtype=np.int64)
+
+
+def preshuffled_positions(rows: int, k: int) -> np.ndarray:
+    """Byte offsets of the preshuffled scale layout (block 32) for a rows x k/32 row-major scale
+    array: (r, b) -> 512 (R KC + C) + 8 u + t with R, t = divmod(r, 8), C, u = divmod(b, 64)."""
+    nb = k // 32
+    kc = (nb + 63) // 64
+    r = np.arange(rows)[:, None]
+    b = np.arange(nb)[None, :]
+    return 512 * ((r // 8) * kc + b // 64) + 8 * (b % 64) + r % 8
+
+
+def preshuffled_padding_positions(rows: int, k: int) -> np.ndarray:
+    """Bytes of the last chunk past each row's last block (written as zero)."""
+    nb = k // 32
+    kc = (nb + 63) // 64
+    pads = []
+    for b in range(nb, 64 * kc):
+        r = np.arange(rows)
+        pads.append(512 * ((r // 8) * kc + b // 64) + 8 * (b % 64) + r % 8)
+    return np.concatenate(pads) if pads else np.zeros(0, dtype=np.int64)

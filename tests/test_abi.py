@@ -62,7 +62,8 @@ FAKE = 1 << 20  # a 16-byte aligned non-null address; never dereferenced on thes
     ((FAKE, BF16, 4, 64, 32, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),     # ld < k
     ((FAKE, 7, 4, 64, 64, 32, E8M0, 1.0, 0, FAKE, FAKE), INVALID),        # dtype
     ((FAKE, BF16, 4, 64, 64, 32, 3, 1.0, 0, FAKE, FAKE), INVALID),        # fmt
-    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 2, FAKE, FAKE), INVALID),     # layout
+    ((FAKE, BF16, 4, 64, 64, 32, E8M0, 1.0, 3, FAKE, FAKE), INVALID),     # layout
+    ((FAKE, BF16, 4, 64, 64, 16, E8M0, 1.0, 2, FAKE, FAKE), UNSUPPORTED), # preshuffled needs block 32
     ((FAKE, BF16, 4, 64, 64, 16, E8M0, 1.0, 1, FAKE, FAKE), UNSUPPORTED), # tiled needs block 32
     ((FAKE, BF16, 4, 1 << 23, 1 << 23, 32, E8M0, 1.0, 1, FAKE, FAKE), UNSUPPORTED),  # tiled k bound
     ((FAKE, BF16, 4, 64, 64, 32, E8M0, 0.0, 0, FAKE, FAKE), INVALID),     # g = 0
@@ -103,7 +104,12 @@ def test_scale_bytes(L):
     assert sb(0, 64, 32, 1) == 0
     assert sb(4, 64, 16, 1) == 0          # tiled is defined for block 32 only
     assert sb(4, 48, 32, 0) == 0          # k % block
-    assert sb(4, 64, 32, 2) == 0          # unknown layout
+    # preshuffled: ceil(rows / 8) * ceil(k / 2048) * 512
+    assert sb(4, 64, 32, 2) == 512
+    assert sb(9, 4224, 32, 2) == 2 * 3 * 512
+    assert sb(8, 2048, 32, 2) == 512
+    assert sb(4, 64, 16, 2) == 0          # preshuffled is defined for block 32 only
+    assert sb(4, 64, 32, 3) == 0          # unknown layout
 
 
 def test_gemm_validation_and_workspace(L):
@@ -124,7 +130,12 @@ def test_gemm_validation_and_workspace(L):
     assert gemm(layout=1) == UNSUPPORTED                                    # W4A16
     assert gemm(layout=1, mode=A4, work=FAKE, wbytes=1 << 20) == UNSUPPORTED  # k = 64
     assert gemm(layout=1, mode=A4, block=16, k=128, ldx=128) == UNSUPPORTED
-    assert gemm(layout=2) == INVALID
+    assert gemm(layout=3) == INVALID
+    # preshuffled weight scales: the m = 1 W4A16 GEMV only
+    assert gemm(layout=2) == UNSUPPORTED                                    # m = 4
+    assert gemm(layout=2, m=1, mode=A4, work=FAKE, wbytes=1 << 20) == UNSUPPORTED
+    assert gemm(layout=2, m=1, ldx=68) == UNSUPPORTED                       # ld_x not a multiple of 8
+    assert gemm(layout=2, m=1, block=16) == UNSUPPORTED
 
     assert gemm(mode=A4, fmt=E4M3) == UNSUPPORTED      # W4A4 is E8M0-only
     assert gemm(mode=A4, block=64) == UNSUPPORTED      # and block 32 only
