@@ -311,7 +311,8 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a, uint
     // Epilogue.  Transposed 32x32 result layout: for tile (i, jn) a lane holds output row
     // m = i*32 + lane%32 and, for group q = e/4, columns n = jn*32 + 8q + 4*(lane/32) + e%4.
     // Rows of a wave's 128 x 64 block are staged through LDS (each wave in a region of its
-    // own, rows padded against bank conflicts) and written back as whole 16-byte chunks, 128
+    // own, 64 rows a pass, rows padded by 16 bytes against bank conflicts so that every
+    // read-back stays 16-byte aligned) and written back as whole 16-byte chunks, 128
     // or 256 contiguous bytes per output row.  Stores go through a buffer descriptor;
     // out-of-range chunks get an out-of-range offset and are dropped.
     constexpr uint32_t ESZ = OUT_BF16 ? 2 : 4;
@@ -322,10 +323,10 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a, uint
     // chunk stores need 16-byte aligned rows and chunks wholly in or out of range
     const bool vec = (ldy % CE) == 0 && (nlim % CE) == 0;
     if (vec) {
-        constexpr int PASSES = OUT_BF16 ? 1 : 2;             // 128 or 64 rows per pass
+        constexpr int PASSES = 2;                             // 64 rows per pass
         constexpr int IPP = MI / PASSES;                      // 32-row blocks per pass
         constexpr uint32_t RB = 32 * NJ * ESZ;                // bytes of a wave row (32 NJ columns)
-        constexpr uint32_t PITCH = RB + (OUT_BF16 ? 8 : 16);
+        constexpr uint32_t PITCH = RB + 16;                   // 16-byte aligned rows for the read-back
         constexpr uint32_t CPR = RB / 16;                     // chunks per row (8 or 16)
         constexpr uint32_t RPI = 64 / CPR;                    // rows per store instruction
         constexpr uint32_t PASS_ROWS = 32 * IPP;
