@@ -279,33 +279,41 @@ int ox_gemm(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
             double* y, double* aabs)
 {
     int64_t i, j, kk;
-    double* xh;
+    double *xh, *wh;
     uint8_t *xc = NULL, *xs = NULL;
     if (!x || !wcodes || !wscales || !mrows || !ncols || !y || !aabs || m < 0 || n < 0 ||
         k <= 0 || ldx < k || !valid_block(block) || k % block != 0 || fmt < 0 || fmt > 2 ||
         !(g > 0.0f) || isinf(g) || (mode != OX_A16 && mode != OX_A4))
         return -1;
     if (mode == OX_A4 && k % 32 != 0) return -1;
-    xh = (double*)malloc(sizeof(double) * (size_t)k);
+    for (i = 0; i < nm; ++i)
+        if (mrows[i] < 0 || mrows[i] >= m) return -1;
+    for (j = 0; j < nn; ++j)
+        if (ncols[j] < 0 || ncols[j] >= n) return -1;
+    /* the selected rows of X as values (A4: after their MX quantization), then one
+     * dequantized weight row per selected column */
+    xh = (double*)malloc(sizeof(double) * (size_t)(nm * k + k));
+    if (!xh) return -1;
+    wh = xh + nm * k;
     if (mode == OX_A4) {
         xc = (uint8_t*)malloc((size_t)k / 2);
         xs = (uint8_t*)malloc((size_t)k / 32);
     }
     for (i = 0; i < nm; ++i) {
-        int64_t mi = mrows[i];
-        if (mi < 0 || mi >= m) { free(xh); free(xc); free(xs); return -1; }
+        const uint16_t* xr = x + mrows[i] * ldx;
         if (mode == OX_A16) {
-            for (kk = 0; kk < k; ++kk) xh[kk] = bf16_value(x[mi * ldx + kk]);
+            for (kk = 0; kk < k; ++kk) xh[i * k + kk] = bf16_value(xr[kk]);
         } else { /* activations MX-quantized: block 32, E8M0, g = 1 */
-            ox_quantize(x + mi * ldx, OX_BF16, 1, k, k, 32, OX_E8M0, 1.0f, xc, xs);
-            for (kk = 0; kk < k; ++kk) xh[kk] = dq_exact(xc, xs, 0, kk, k, 32, OX_E8M0, 1.0);
+            ox_quantize(xr, OX_BF16, 1, k, k, 32, OX_E8M0, 1.0f, xc, xs);
+            for (kk = 0; kk < k; ++kk) xh[i * k + kk] = dq_exact(xc, xs, 0, kk, k, 32, OX_E8M0, 1.0);
         }
-        for (j = 0; j < nn; ++j) {
-            int64_t nj = ncols[j];
+    }
+    for (j = 0; j < nn; ++j) {
+        for (kk = 0; kk < k; ++kk) wh[kk] = dq_exact(wcodes, wscales, ncols[j], kk, k, block, fmt, (double)g);
+        for (i = 0; i < nm; ++i) {
             double acc = 0.0, accabs = 0.0;
-            if (nj < 0 || nj >= n) { free(xh); free(xc); free(xs); return -1; }
             for (kk = 0; kk < k; ++kk) {
-                double p = xh[kk] * dq_exact(wcodes, wscales, nj, kk, k, block, fmt, (double)g);
+                double p = xh[i * k + kk] * wh[kk];
                 acc += p;
                 accabs += fabs(p);
             }
@@ -480,19 +488,24 @@ int ox_gemm_fp8(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
                 double* y, double* aabs)
 {
     int64_t i, j, kk;
+    double* wh;
     if (!x || !wcodes || !wscales || !mrows || !ncols || !y || !aabs || m < 0 || n < 0 ||
         k <= 0 || ldx < k || !valid_block(block) || k % block != 0 || fmt < 0 || fmt > 2 ||
         !(g > 0.0f) || isinf(g))
         return -1;
-    for (i = 0; i < nm; ++i) {
-        int64_t mi = mrows[i];
-        if (mi < 0 || mi >= m) return -1;
-        for (j = 0; j < nn; ++j) {
-            int64_t nj = ncols[j];
+    for (i = 0; i < nm; ++i)
+        if (mrows[i] < 0 || mrows[i] >= m) return -1;
+    for (j = 0; j < nn; ++j)
+        if (ncols[j] < 0 || ncols[j] >= n) return -1;
+    wh = (double*)malloc(sizeof(double) * (size_t)k);  /* one dequantized weight row */
+    if (!wh) return -1;
+    for (j = 0; j < nn; ++j) {
+        for (kk = 0; kk < k; ++kk) wh[kk] = dq_exact_fp8(wcodes, wscales, ncols[j], kk, k, block, fmt, (double)g);
+        for (i = 0; i < nm; ++i) {
+            const uint16_t* xr = x + mrows[i] * ldx;
             double acc = 0.0, accabs = 0.0;
-            if (nj < 0 || nj >= n) return -1;
             for (kk = 0; kk < k; ++kk) {
-                double p = bf16_value(x[mi * ldx + kk]) * dq_exact_fp8(wcodes, wscales, nj, kk, k, block, fmt, (double)g);
+                double p = bf16_value(xr[kk]) * wh[kk];
                 acc += p;
                 accabs += fabs(p);
             }
@@ -500,6 +513,7 @@ int ox_gemm_fp8(const uint16_t* x, int64_t m, int64_t k, int64_t ldx,
             aabs[i * nn + j] = accabs;
         }
     }
+    free(wh);
     return 0;
 }
 
