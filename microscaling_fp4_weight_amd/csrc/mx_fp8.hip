@@ -15,8 +15,11 @@
 //
 // The W8A16 product Y = X . dequant(W8)^T runs on bf16 matrix cores: e * s (at most 8
 // significant bits) is exact in bf16 for |e * s| >= 2^-133, g multiplies the fp32 sums.
+#include <cmath>
+
 #include "mx_device.h"
 #include "mx_internal.h"
+#include "mx_wdeq.h"
 
 namespace mxk {
 namespace f8 {
@@ -317,30 +320,6 @@ __device__ __forceinline__ uint64_t lane_scales(rsrc_t r, uint32_t off)
     else return bload64(r, off);
 }
 
-// 32 codes (8 dwords) with their scale bytes -> 32 bf16 (16 dwords), e * s exact.
-template <int BLOCK, int FMT>
-__device__ __forceinline__ void dequant_w8(const uint32_t (&cw)[8], uint64_t sbytes, uint32_t (&out)[16])
-{
-#pragma unroll
-    for (int h = 0; h < 16; ++h) {  // half-dword h: elements 2h, 2h+1
-        const int e = 2 * h;
-        const uint32_t byte = (uint32_t)(sbytes >> (8 * (BLOCK >= 32 ? 0 : e / BLOCK))) & 0xFFu;
-        float pow2 = 1.0f, mant = 1.0f;
-        if constexpr (FMT == FMT_E8M0) {
-            pow2 = e8m0_value(byte);
-        } else {
-            const DecG1 p = dec_params_g1<FMT>(byte);
-            pow2 = p.pow2;
-            mant = p.mant;
-        }
-        f32x2 d;
-        if (h & 1) d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[h >> 1], pow2, true);
-        else d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cw[h >> 1], pow2, false);
-        const float lo = FMT == FMT_E8M0 ? d.x : d.x * mant, hi = FMT == FMT_E8M0 ? d.y : d.y * mant;
-        out[h] = (f2u(lo) >> 16) | (f2u(hi) & 0xFFFF0000u);  // exact: at most 8 significant bits
-    }
-}
-
 template <int BLOCK, int FMT, int MT, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) void gemm_w8_kernel(const W8Args a)
 {
@@ -523,6 +502,20 @@ hipError_t launch_dequantize_fp8(const DequantArgs& a, hipStream_t st)
     return hipErrorInvalidValue;
 }
 
+// Choice between the pipelined 128 x 256 tile kernel and the 16-row kernel above, from
+// measured costs on MI355X: a wave of up to 256 tiles takes about 11 ns per k with E8M0
+// scales (17.5 ns with E4M3 / UE5M3 scales, whose dequantization costs more), whatever the
+// tile count; the 16-row kernel runs at about 100 TFLOP/s.  Few tiles and small m favour the
+// latter (m 128, n 4096, k 4096: 41 against 45 us), many tiles the former (m 2048, n 28672,
+// k 8192: 1.0 against 7.9 ms).
+static bool w8_prefers_tiled(const W8Args& a)
+{
+    const double tiles = (double)((a.m + 127) / 128) * (double)((a.n + 255) / 256);
+    const double t_tiled = std::ceil(tiles / 256.0) * (double)a.k * (a.fmt == FMT_E8M0 ? 11e-9 : 17.5e-9);
+    const double t_rows = 2.0 * (double)a.m * (double)a.n * (double)a.k / 100e12;
+    return t_tiled < t_rows;
+}
+
 template <int FMT, bool OUT_BF16>
 static hipError_t launch_w8(const W8Args& a, hipStream_t st)
 {
@@ -531,6 +524,24 @@ static hipError_t launch_w8(const W8Args& a, hipStream_t st)
         hipLaunchKernelGGL((f8::gemm_w8_generic_kernel<FMT, OUT_BF16>), dim3((unsigned)((total + 255) / 256)),
                            dim3(f8::THREADS), 0, st, a);
         return hipGetLastError();
+    }
+    if (a.m > 16 && w8_prefers_tiled(a)) {
+        // the pipelined matrix-core kernel of the W4A16 product, with FP8 codes
+        GemmArgs g{};
+        g.x = a.x;
+        g.m = a.m;
+        g.n = a.n;
+        g.k = a.k;
+        g.ldx = a.ldx;
+        g.wc = a.wc;
+        g.ws = a.ws;
+        g.block = a.block;
+        g.fmt = a.fmt;
+        g.g = (float)a.g;
+        g.y = a.y;
+        g.y_bf16 = a.y_bf16;
+        g.ldy = a.ldy;
+        if (a16_uses_tiled(g)) return launch_gemm_w8_tiled(g, st);
     }
     const bool small = a.m <= 16;
     const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)((a.m + (small ? 16 : 64) - 1) / (small ? 16 : 64)));

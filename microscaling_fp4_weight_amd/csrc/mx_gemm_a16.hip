@@ -18,6 +18,11 @@
 // result tile is transposed (rows n, columns m); the epilogue stages it through LDS and
 // writes whole 16-byte chunks.  Workgroups are mapped so that the m-tiles sharing a weight
 // tile run on the same XCD.
+//
+// The same kernel serves FP8 (E4M3) weights in the same block structure (the W8A16 product
+// of the FP8 fallback): a weight row then brings 128 code bytes per stage, a stage is 64 KB
+// and the ring two stages deep (three would not fit in LDS), so the loads of a stage are
+// issued one stage before it is read.
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_wdeq.h"
@@ -26,34 +31,52 @@ namespace mxk {
 
 namespace a16 {
 
-constexpr int BM = 128, BN = 256, BK = 128, STAGES = 3;
+constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int WAVES = 8, THREADS = 64 * WAVES;
 constexpr int MI = 2, NJ = 2;                    // per wave: 2 (m) x 2 (n) tiles of 32 x 32
 constexpr int XROWB = BK * 2;                    // activation bytes per row per stage (256)
-constexpr int WROWB = BK / 2;                    // code bytes per weight row per stage (64)
 constexpr int X_BYTES = BM * XROWB;              // 32 KB
-constexpr int W_BYTES = BN * WROWB;              // 16 KB
-constexpr int STAGE_BYTES = X_BYTES + W_BYTES;   // 48 KB
 constexpr int SWIN_K = 512;                      // k per scale window
 constexpr int SWIN_BYTES = BN * (SWIN_K / 32);   // 4 KB
-constexpr int SWIN_OFF = STAGES * STAGE_BYTES;
-constexpr int LDS_BYTES = SWIN_OFF + 2 * SWIN_BYTES;  // 155648 (of 160 KB)
-constexpr int LOADS_PER_STAGE = 6;               // per wave: 4 activation + 2 code loads
 constexpr int LOADS_PER_WINDOW = 2;              // per wave
+
+// Stage geometry by weight width: FP4 (W8 false) or FP8 codes.
+template <bool W8>
+struct Geo {
+    static constexpr int WROWB = W8 ? BK : BK / 2;             // code bytes per weight row per stage
+    static constexpr int W_BYTES = BN * WROWB;                 // 16 or 32 KB
+    static constexpr int STAGE_BYTES = X_BYTES + W_BYTES;      // 48 or 64 KB
+    static constexpr int STAGES = W8 ? 2 : 3;
+    static constexpr int SWIN_OFF = STAGES * STAGE_BYTES;
+    static constexpr int LDS_BYTES = SWIN_OFF + 2 * SWIN_BYTES;  // 155648 or 139264 (of 160 KB)
+    static constexpr int WCH = WROWB / 16;                     // 16-byte chunks per weight row
+    static constexpr int WRPL = 64 / WCH;                      // weight rows per 1 KB load
+    static constexpr int WLOADS = BN / WRPL / WAVES;           // code loads per wave (2 or 4)
+    static constexpr int LOADS_PER_STAGE = 4 + WLOADS;         // per wave, with 4 activation loads
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS chunk permutations against bank conflicts: activation rows have 16 chunks of 16 bytes
-// (XOR with row % 16), weight rows 4 (XOR with (row / 4) % 4).
+// (XOR with row % 16); weight rows 4 (FP4: XOR with (row / 4) % 4) or 8 (FP8: XOR with
+// (row / 2) % 8), so that the rows sharing a 256-byte line permute their chunks differently.
 __device__ __forceinline__ uint32_t xswz(uint32_t row, uint32_t c) { return c ^ (row & 15u); }
-__device__ __forceinline__ uint32_t wswz(uint32_t row, uint32_t c) { return c ^ ((row >> 2) & 3u); }
+template <bool W8>
+__device__ __forceinline__ uint32_t wswz(uint32_t row, uint32_t c)
+{
+    if constexpr (W8) return c ^ ((row >> 1) & 7u);
+    else return c ^ ((row >> 2) & 3u);
+}
 
 // This wave's share of stage s's loads into the stage buffer at `st`.
 // Activations: 32 loads of 4 rows x 256 bytes (lane: row lane/16, LDS chunk lane%16).
-// Codes: 16 loads of 16 rows x 64 bytes (lane: row lane/4, LDS chunk lane%4).
+// Codes: 16 loads of 16 rows x 64 bytes (FP4; lane: row lane/4, LDS chunk lane%4) or 32 loads
+// of 8 rows x 128 bytes (FP8; lane: row lane/8, LDS chunk lane%8).
+template <bool W8>
 __device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uint32_t s, rsrc_t xr, rsrc_t wr,
                                             uint32_t ldx, uint32_t K)
 {
+    using G = Geo<W8>;
     const uint32_t k0 = s * BK;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -65,12 +88,12 @@ __device__ __forceinline__ void issue_stage(uint8_t* st, int wave, int lane, uin
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(st + grp * 1024), 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const uint32_t grp = (uint32_t)(wave * 2 + q);          // 16-row group, 0..15
-        const uint32_t row = grp * 16 + (lane >> 2);
-        const uint32_t c = wswz(row, lane & 3);
-        const uint32_t kk = k0 + 32 * c;
-        const uint32_t off = kk < K ? row * (K / 2) + kk / 2 : kOOB;
+    for (int q = 0; q < G::WLOADS; ++q) {
+        const uint32_t grp = (uint32_t)(wave * G::WLOADS + q);  // group of WRPL rows
+        const uint32_t row = grp * G::WRPL + lane / G::WCH;
+        const uint32_t c = wswz<W8>(row, lane % G::WCH);
+        const uint32_t kk = k0 + (W8 ? 16 : 32) * c;            // first k of chunk c
+        const uint32_t off = kk < K ? (W8 ? row * K + kk : row * (K / 2) + kk / 2) : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(st + X_BYTES + grp * 1024), 16, off, 0, 0, 0);
     }
 }
@@ -98,16 +121,20 @@ __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "m
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Fragments of one 64-k window w of a stage: per m-block i, 64 activation bytes (k = 64w + 32h
-// .. +31 of row m); per n-block jn, 16 code bytes (same k of weight row n) and the scale byte.
+// .. +31 of row m); per n-block jn, 16 (FP4) or 32 (FP8) code bytes (same k of weight row n)
+// and the scale byte.
+template <bool W8>
 struct Frags {
     u32x4 x[MI][4];
-    u32x4 w[NJ];
+    u32x4 w[NJ][W8 ? 2 : 1];
     uint32_t s[NJ];
 };
 
+template <bool W8>
 __device__ __forceinline__ void read_frags(const uint8_t* st, const uint8_t* swin, uint32_t sbyte, int w,
-                                           uint32_t xrow0, uint32_t wrow0, uint32_t h, Frags& f)
+                                           uint32_t xrow0, uint32_t wrow0, uint32_t h, Frags<W8>& f)
 {
+    using G = Geo<W8>;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const uint32_t row = xrow0 + 32 * i;
@@ -118,17 +145,32 @@ __device__ __forceinline__ void read_frags(const uint8_t* st, const uint8_t* swi
 #pragma unroll
     for (int jn = 0; jn < NJ; ++jn) {
         const uint32_t row = wrow0 + 32 * jn;
-        f.w[jn] = *reinterpret_cast<const u32x4*>(st + X_BYTES + row * WROWB + 16 * wswz(row, 2 * w + h));
+        if constexpr (W8) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+                f.w[jn][c] = *reinterpret_cast<const u32x4*>(st + X_BYTES + row * G::WROWB +
+                                                            16 * wswz<W8>(row, 4 * w + 2 * h + c));
+        } else {
+            f.w[jn][0] = *reinterpret_cast<const u32x4*>(st + X_BYTES + row * G::WROWB + 16 * wswz<W8>(row, 2 * w + h));
+        }
         f.s[jn] = swin[row * 16 + sbyte + 2 * w];
     }
 }
 
-template <int FMT>
-__device__ __forceinline__ void mfma_window(f32x16 (&acc)[MI][NJ], const Frags& f)
+template <int FMT, bool W8>
+__device__ __forceinline__ void mfma_window(f32x16 (&acc)[MI][NJ], const Frags<W8>& f)
 {
     uint32_t bw[NJ][16];
 #pragma unroll
-    for (int jn = 0; jn < NJ; ++jn) dequant32<32, FMT>(f.w[jn], f.s[jn], bw[jn]);
+    for (int jn = 0; jn < NJ; ++jn) {
+        if constexpr (W8) {
+            const uint32_t cw[8] = {f.w[jn][0].x, f.w[jn][0].y, f.w[jn][0].z, f.w[jn][0].w,
+                                    f.w[jn][1].x, f.w[jn][1].y, f.w[jn][1].z, f.w[jn][1].w};
+            dequant_w8<32, FMT>(cw, f.s[jn], bw[jn]);
+        } else {
+            dequant32<32, FMT>(f.w[jn][0], f.s[jn], bw[jn]);
+        }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t)          // k-step t takes k 32h + 8t .. +7 of the window
 #pragma unroll
@@ -143,9 +185,12 @@ __device__ __forceinline__ void mfma_window(f32x16 (&acc)[MI][NJ], const Frags& 
         }
 }
 
-template <int FMT, bool OUT_BF16>
+template <int FMT, bool OUT_BF16, bool W8>
 __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
 {
+    using G = Geo<W8>;
+    constexpr int STAGES = G::STAGES, STAGE_BYTES = G::STAGE_BYTES, SWIN_OFF = G::SWIN_OFF;
+    constexpr int LOADS_PER_STAGE = G::LOADS_PER_STAGE;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
@@ -167,7 +212,8 @@ __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
     const uint32_t mrows = (uint32_t)(a.m - m0 < BM ? a.m - m0 : BM);
     const uint32_t nrows = (uint32_t)(a.n - n0 < BN ? a.n - n0 : BN);
     const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, ((mrows - 1) * ldx + K) * 2);
-    const rsrc_t wr = make_rsrc(a.wc + n0 * (a.k / 2), nrows * (K / 2));
+    const uint32_t wrowb = W8 ? K : K / 2;                   // code bytes per weight row
+    const rsrc_t wr = make_rsrc(a.wc + n0 * (int64_t)wrowb, nrows * wrowb);
     const rsrc_t sr = make_rsrc(a.ws + n0 * (a.k / 32), nrows * (K / 32));
 
     f32x16 acc[MI][NJ];
@@ -183,16 +229,17 @@ __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
     // next stage has landed, one barrier publishes it and frees this stage's buffer, which
     // receives the stage three ahead; window 0 of the next stage is read while window 1's MFMAs
     // run.  Scale window j + 1 is requested at stage 4j.  Stages past the end of k load as
-    // zeros (out-of-range offsets), so every iteration has the same shape.
+    // zeros (out-of-range offsets), so every iteration has the same shape.  With the two-deep
+    // FP8 ring the stage awaited at the barrier is the last one issued: every load has to land.
     const int S = (int)((K + BK - 1) / BK);
     issue_window(lds + SWIN_OFF, wave, lane, 0, sr, K);
 #pragma unroll
-    for (int p = 0; p < STAGES; ++p) issue_stage(lds + p * STAGE_BYTES, wave, lane, (uint32_t)p, xr, wr, ldx, K);
+    for (int p = 0; p < STAGES; ++p) issue_stage<W8>(lds + p * STAGE_BYTES, wave, lane, (uint32_t)p, xr, wr, ldx, K);
 
     const uint32_t r32 = lane & 31, h = lane >> 5;
     const uint32_t xrow0 = wm * 64 + r32, wrow0 = wn * 64 + r32;
 
-    Frags f0, f1;
+    Frags<W8> f0, f1;
     wait_vmcnt<(STAGES - 1) * LOADS_PER_STAGE>();
     barrier_only();
     read_frags(lds, lds + SWIN_OFF, h, 0, xrow0, wrow0, h, f0);
@@ -206,12 +253,13 @@ __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
         mfma_window<FMT>(acc, f0);
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkm0();
-        if ((s & 3) == 1) wait_vmcnt<LOADS_PER_STAGE + LOADS_PER_WINDOW>();
+        if constexpr (STAGES == 2) wait_vmcnt<0>();
+        else if ((s & 3) == 1) wait_vmcnt<LOADS_PER_STAGE + LOADS_PER_WINDOW>();
         else wait_vmcnt<LOADS_PER_STAGE>();
         barrier_only();
         __builtin_amdgcn_sched_barrier(0);
         if ((s & 3) == 0) issue_window(lds + SWIN_OFF + (((s >> 2) + 1) & 1) * SWIN_BYTES, wave, lane, (uint32_t)(s >> 2) + 1, sr, K);
-        issue_stage(lds + cur, wave, lane, (uint32_t)(s + STAGES), xr, wr, ldx, K);
+        issue_stage<W8>(lds + cur, wave, lane, (uint32_t)(s + STAGES), xr, wr, ldx, K);
         const int s1 = s + 1;
         const uint8_t* swin1 = lds + SWIN_OFF + ((s1 >> 2) & 1) * SWIN_BYTES;
         read_frags(lds + nxt, swin1, 4 * (uint32_t)(s1 & 3) + h, 0, xrow0, wrow0, h, f0);
@@ -236,7 +284,7 @@ __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
         constexpr uint32_t PITCH = RB + 16;
         constexpr uint32_t CPR = RB / 16;                    // chunks per row (8 or 16)
         constexpr uint32_t RPI = 64 / CPR;                   // rows per store instruction
-        static_assert(WAVES * 64 * PITCH <= (uint32_t)LDS_BYTES, "epilogue staging exceeds LDS");
+        static_assert(WAVES * 64 * PITCH <= (uint32_t)G::LDS_BYTES, "epilogue staging exceeds LDS");
         uint8_t* stg = lds + wave * 64 * PITCH;
         barrier_only();  // every wave is done reading the stage buffers
 #pragma unroll
@@ -282,14 +330,15 @@ __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
     }
 }
 
-template <int FMT, bool OUT_BF16>
+template <int FMT, bool OUT_BF16, bool W8>
 static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st)
 {
+    constexpr int LDS = Geo<W8>::LDS_BYTES;
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)gemm_a16_kernel<FMT, OUT_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+        (const void*)gemm_a16_kernel<FMT, OUT_BF16, W8>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (attr != hipSuccess) return attr;
     const unsigned tiles = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + BN - 1) / BN));
-    hipLaunchKernelGGL((gemm_a16_kernel<FMT, OUT_BF16>), dim3(tiles), dim3(THREADS), LDS_BYTES, st, a);
+    hipLaunchKernelGGL((gemm_a16_kernel<FMT, OUT_BF16, W8>), dim3(tiles), dim3(THREADS), LDS, st, a);
     return hipGetLastError();
 }
 
@@ -308,7 +357,16 @@ bool a16_uses_tiled(const GemmArgs& a)
 hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st)
 {
     if (!a16_uses_tiled(a)) return hipErrorInvalidValue;
-#define MXF(F) if (a.fmt == F) return a.y_bf16 ? a16::launch_tiled<F, true>(a, st) : a16::launch_tiled<F, false>(a, st);
+#define MXF(F) if (a.fmt == F) return a.y_bf16 ? a16::launch_tiled<F, true, false>(a, st) : a16::launch_tiled<F, false, false>(a, st);
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_w8_tiled(const GemmArgs& a, hipStream_t st)
+{
+    if (!a16_uses_tiled(a)) return hipErrorInvalidValue;
+#define MXF(F) if (a.fmt == F) return a.y_bf16 ? a16::launch_tiled<F, true, true>(a, st) : a16::launch_tiled<F, false, true>(a, st);
     MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
 #undef MXF
     return hipErrorInvalidValue;

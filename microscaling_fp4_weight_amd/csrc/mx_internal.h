@@ -104,6 +104,8 @@ bool a4_uses_mfma(const GemmArgs& a);
 // whether the large-m W4A16 product runs on the pipelined kernel (else the simple one)
 bool a16_uses_tiled(const GemmArgs& a);
 hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st);
+// the same pipelined kernel with FP8 (E4M3) weight codes, n x k bytes (same conditions)
+hipError_t launch_gemm_w8_tiled(const GemmArgs& a, hipStream_t st);
 
 struct ErrArgs {
     const void* x;

@@ -139,6 +139,66 @@ def test_gemm_fp8_blocks_tail_and_scale(block):
     assert_gemm_close(to_host_bits(y), yref, aref, False, f"w8 block {block}")
 
 
+def _gemm_fp8_case(m, n, k, fmt, g, tag, ldx=None, ldy=None):
+    x = synth.normal((m, k), "bf16", f"g8t.x.{tag}", 1.0)
+    w = synth.normal((n, k), "bf16", f"g8t.w.{tag}", 0.02 / g, 0.01, 20.0)
+    rc, rs = oracle.quantize_fp8(w, 32, fmt, g)
+    cd, sd = torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV)
+    xd = bf16_dev(x)
+    if ldx is not None:
+        wide = torch.zeros((m, ldx), dtype=torch.bfloat16, device=DEV)
+        wide[:, :k] = xd
+        xd = wide[:, :k]
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 32, fmt, g)
+    for dt in (torch.float32, torch.bfloat16):
+        y = None
+        if ldy is not None:
+            y = torch.full((m, ldy), float("nan"), dtype=dt, device=DEV)[:, :n]
+        y = mx.mx_gemm_fp8(xd, cd, sd, 32, fmt, g, out_dtype=dt, y=y)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 {tag} {fmt} {dt}")
+        if ldy is not None:  # nothing written beyond the n columns of each row
+            assert torch.isnan(y.as_strided((m, ldy - n), (ldy, 1), n)).all()
+
+
+# Larger products run on the pipelined matrix-core kernel (tiles of 128 x 256, k in stages of
+# 128, scale windows of 512); the library picks it when its estimated time is below the 16-row
+# kernel's, which these shapes pass by a factor of 1.1 or more with every scale format.  Every
+# output is compared: several tiles with ragged tails in m and n (down to a single row and
+# column), n-tile counts that are and are not multiples of 8 (two mappings of tiles to XCDs).
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("mnk", [(300, 6000, 1536), (129, 7937, 512), (200, 5000, 512)])
+def test_gemm_fp8_tiled(mnk, fmt):
+    m, n, k = mnk
+    _gemm_fp8_case(m, n, k, fmt, 1.0, f"{m}.{n}.{k}")
+
+
+@pytest.mark.parametrize("fmt,ldy", [("ue5m3", 4003), ("e8m0", 4008)])
+def test_gemm_fp8_tiled_tensor_scale_and_strides(fmt, ldy):
+    # padded activation rows (ldx = k + 8); output rows of n + 3 (odd: chunk stores are off,
+    # element stores on) or n + 8 (chunk stores on); per-tensor g
+    g = float(np.float32(0.0291))
+    _gemm_fp8_case(300, 4000, 1024, fmt, g, f"ld{ldy}", ldx=1032, ldy=ldy)
+
+
+def test_gemm_fp8_prefill_shape_sampled():
+    # 70B FFN prefill shape: m 2048, k 8192, n 28672, block 32, E8M0; sampled rows and columns
+    w = synth.c4_weight()
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize_fp8(wd, 32, "e8m0")
+    del wd
+    cols = np.array([0, 1, 255, 256, 5000, 14335, 20000, 28671])
+    rows = np.array([0, 1, 127, 128, 700, 1500, 2047])
+    rc, rs = oracle.quantize_fp8(w[cols], 32, "e8m0")
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
+    x = synth.c4_x()
+    y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, "e8m0", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    yref, aref = oracle.gemm_fp8(x[rows], rc, rs, 32, "e8m0")
+    assert_gemm_close(to_host_bits(y[rows][:, cols]), yref, aref, False, "w8 prefill")
+
+
 def test_gemm_fp8_generic_path():
     # k % 32 != 0: one thread per output
     m, n, k = 5, 33, 72
