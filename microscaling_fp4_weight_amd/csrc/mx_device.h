@@ -293,6 +293,62 @@ __device__ __forceinline__ uint32_t enc_elem_g(uint32_t xbits32, const EncG& p)
     return c | ((xbits32 >> 28) & 8u);
 }
 
+// bf16 input: the same decisions on packed 16-bit magnitudes.  A bf16 pattern has a zero
+// low half, so |x| > u  <=>  X > (u >> 16) with X the 15-bit magnitude of x.  The thresholds
+// are non-decreasing, so the count of those below X comes from a three-step search: X > U3
+// gives code bit 2; then U1 or U5 gives bit 1; then U0, U2, U4 or U6 gives bit 0.  Two
+// elements are decided at once, one per 16-bit half: X > U is the sign of U - X (both below
+// 2^15), spread over its half by an arithmetic shift into a 0 / 0xFFFF mask that selects the
+// next threshold with a bitfield insert.
+struct EncG16 {
+    uint32_t p[7];  // U_i in both halves
+};
+
+__device__ __forceinline__ EncG16 enc_params_g16(const EncG& e)
+{
+    EncG16 q;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) q.p[i] = (e.u[i] >> 16) * 0x00010001u;
+    return q;
+}
+
+typedef __attribute__((ext_vector_type(2))) short i16x2;
+
+// 0xFFFF in each half where X > U
+__device__ __forceinline__ uint32_t gt_mask16(uint32_t pu, uint32_t x)
+{
+    const u16x2 d = __builtin_bit_cast(u16x2, pu) - __builtin_bit_cast(u16x2, x);
+    uint32_t m = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, d) >> 15);
+    // opaque to the optimizer: left alone it rewrites the mask selects below into per-half
+    // compares and selects, several times the instruction count
+    asm("" : "+v"(m));
+    return m;
+}
+
+__device__ __forceinline__ uint32_t sel32(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+
+// Codes of the two bf16 elements of word w: element 0 (low half) in bits 0..3, element 1 in
+// bits 16..19.
+__device__ __forceinline__ uint32_t enc_pair_g16(uint32_t w, const EncG16& q)
+{
+    const uint32_t x = w & 0x7FFF7FFFu;
+    const uint32_t m2 = gt_mask16(q.p[3], x);
+    const uint32_t m1 = gt_mask16(sel32(m2, q.p[5], q.p[1]), x);
+    const uint32_t t3 = sel32(m1, sel32(m2, q.p[6], q.p[2]), sel32(m2, q.p[4], q.p[0]));
+    const uint32_t m0 = gt_mask16(t3, x);
+    return (m2 & 0x00040004u) | (m1 & 0x00020002u) | (m0 & 0x00010001u) | ((w >> 12) & 0x00080008u);
+}
+
+// Four such results (elements 0..7 of a code word, two per result) -> the code word.
+__device__ __forceinline__ uint32_t pack_pairs_g16(uint32_t z0, uint32_t z1, uint32_t z2, uint32_t z3)
+{
+    uint32_t a = z0 | (z1 << 8);  // nibbles of elements 0, 2 at bits 0, 8; 1, 3 at 16, 24
+    uint32_t b = z2 | (z3 << 8);
+    a |= a >> 12;                 // elements 0..3 in the low 16 bits
+    b |= b >> 12;
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+
 // Byte offset of the scale of (row, 32-element block kb) in the tiled scale layout with ks
 // 256-k stages per row tile (the layout is described with kTileBytes in mx_internal.h).
 __device__ __forceinline__ uint64_t tiled_scale_off(uint32_t row, uint32_t kb, uint32_t ks)

@@ -182,6 +182,17 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
                 }
             }
         }
+    } else if constexpr (BF16) {
+        // packed 16-bit decisions, two elements per word; word j holds elements 2j, 2j+1
+        uint32_t z[16];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const EncG16 q = enc_params_g16(enc_params_g<FMT>(sbyte[b], g));
+#pragma unroll
+            for (int jj = 0; jj < WPB; ++jj) z[b * WPB + jj] = enc_pair_g16(w[b * WPB + jj], q);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = pack_pairs_g16(z[4 * q], z[4 * q + 1], z[4 * q + 2], z[4 * q + 3]);
     } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {

@@ -76,6 +76,75 @@ def test_quantize_tensor_scale(fmt, g):
         np.testing.assert_array_equal(c, rc)
 
 
+def _tensor_scale_decision_blocks(fmt: str, g: float, dtype: str) -> np.ndarray:
+    """Blocks of 32, rows of 1024: for every positive finite scale byte s of `fmt` under the
+    per-tensor scale g, a block maximum a = 6 s g and, around each decision point t s' g
+    (s' the scale the oracle gives that maximum; t = 0.25, 0.75, ..., 5), fp32 values at
+    0, +-1, ..., +-40 fp32 units (f32) or the four nearest bf16 values (bf16), both signs."""
+    amax = []
+    for byte in range(256):
+        sv = oracle.scale_value(byte, fmt)
+        if not np.isfinite(sv) or sv <= 0:
+            continue
+        if 6.0 * sv * g > 3.0e38:
+            continue
+        a = np.float32(6.0 * sv * g)
+        if dtype == "bf16" and np.isfinite(a):  # nearest bf16 (ties to even)
+            ab = np.array([a], dtype=np.float32).view(np.uint32).astype(np.uint64)
+            ab = (ab + 0x7FFF + ((ab >> 16) & 1)) >> 16 << 16
+            a = ab.astype(np.uint32).view(np.float32)[0]
+        if not np.isfinite(a) or a < 1e-38:
+            continue
+        amax.append(a)
+    amax = np.array(amax, dtype=np.float32)
+    probe = np.zeros((amax.size, 32), dtype=np.float32)
+    probe[:, 0] = amax
+    _, sb = oracle.quantize(probe, 32, fmt, g)
+    ts = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    offs = np.array([0, 1, -1, 2, -2, 3, -3, 5, -5, 8, -8, 12, -12, 15, -15, 16, -16, 17, -17, 20, -20,
+                     30, -30, 40, -40], dtype=np.int64)
+    blocks = []
+    for a, byte in zip(amax, sb[:, 0]):
+        sv = oracle.scale_value(int(byte), fmt)
+        pts = (ts * sv * g).astype(np.float32)
+        bits = pts.view(np.uint32).astype(np.int64)
+        if dtype == "f32":
+            cand = (bits[:, None] + offs[None, :]).ravel()
+        else:
+            hb = bits >> 16
+            cand = (np.concatenate([hb - 1, hb, hb + 1, hb + 2]) << 16)
+        cand = cand[(cand > 0) & (cand < 0x7F800000)].astype(np.uint32)
+        vals = cand.view(np.float32)
+        vals = vals[vals <= a]
+        vals = np.where(np.arange(vals.size) % 2 == 0, vals, -vals).astype(np.float32)
+        pad = (-vals.size) % 31
+        vals = np.concatenate([vals, np.zeros(pad, dtype=np.float32)]).reshape(-1, 31)
+        top = np.full((vals.shape[0], 1), a, dtype=np.float32)
+        blocks.append(np.concatenate([top, vals], axis=1))
+    x = np.concatenate(blocks).reshape(-1)
+    x = np.concatenate([x, np.zeros((-x.size) % 1024, dtype=np.float32)]).reshape(-1, 1024)
+    if dtype == "bf16":
+        b = (x.view(np.uint32) >> 16).astype(np.uint16)
+        assert np.array_equal(synth.bf16_to_f32(b), x)  # every value is a bf16 value
+        return b
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("g", [0.37, 1.0 / 3.0, 0.70710677, 3.3e-3, 1234.5, 2.0 ** -7, 4.0])
+def test_quantize_tensor_scale_decision_points(dtype, fmt, g):
+    # with g != 1 the kernel decides elements from x * fl32(1/M) (s g = M 2^F) and redoes, with
+    # the exact comparison, lanes whose quotient comes near a decision point; these blocks put
+    # elements at and around every decision point of every scale, so both ways are exercised
+    g = float(np.float32(g))
+    x = _tensor_scale_decision_blocks(fmt, g, dtype)
+    c, s = run_quant(x, 32, fmt, g)
+    rc, rs = oracle.quantize(x, 32, fmt, g)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantize_generic_path(fmt):
     # k = 48 (not a multiple of 32) and an odd row stride both take the generic kernel
