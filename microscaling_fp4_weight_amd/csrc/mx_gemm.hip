@@ -401,35 +401,46 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
 }
 
 // ---------------------------------------------------------------------------------------
-// W4A16 GEMV for m = 1 on short streams (the decode shapes): the grid sweeps the code bytes
+// W4A16 GEMV for m <= 2 on short streams (the decode shapes): the grid sweeps the code bytes
 // in address order.  The codes form a sequence of 1 KB chunks (2048 k of one row, row-major);
 // a unit is 8 consecutive chunks (8 KB).  Step i of the persistent grid of G workgroups covers
 // units i G .. i G + G - 1, so at any time the whole GPU reads one contiguous slab, which on
 // MI355X streams markedly better than many workgroups each reading its own rows (measured:
 // n 14336, k 4096: 9.0 against 11.2 us per launch).  Wave w of a workgroup takes chunks 2w,
-// 2w+1 of the unit, which lie in one row because k / 2048 is 2, 4 or 8, with the next step's
-// loads in flight.  X is staged once per workgroup in LDS (lane l's 16-byte piece j of chunk c
-// at slot (4c + j) 64 + l, so that a read instruction covers 1 KB contiguous).  Each wave's
-// partial sum goes to LDS; the rows of the workgroup's units are summed at the end in a fixed
-// order.
+// 2w+1 of the unit; k / 2048 being 2, 4 or 8, they lie in one row and are the same two chunks
+// of k, 2w mod (k / 2048) and the next, at every step, so the wave holds its X for them in
+// registers, loaded once.  The next step's codes and scales are in flight while a step is
+// computed.  Each wave's partial sums go to LDS; the rows of the workgroup's units are
+// summed at the end in a fixed order.
 // ---------------------------------------------------------------------------------------
 constexpr uint32_t SW_GRID = 1024;
 constexpr uint32_t SW_MAX_STEPS = 4;
 
-template <int FMT, bool OUT_BF16, bool PRE>
+// MM: rows of X (m == MM)
+template <int FMT, bool OUT_BF16, bool PRE, int MM>
 __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint32_t units)
 {
-    __shared__ u32x4 xs[2048];  // X: k <= 16384
-    __shared__ float part[SW_MAX_STEPS][4];
+    __shared__ float part[SW_MAX_STEPS][4][MM];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t K = (uint32_t)a.k, KC = K / 2048, G = gridDim.x;
+    const uint32_t c0 = (2 * (uint32_t)wave) & (KC - 1);  // the wave's first chunk of k
+
+    // X of the wave's chunk pair: lane l holds k = (c0 + h) 2048 + 32 l .. +31 of each row
+    uint32_t xq[MM][2][16];
     {
-        const rsrc_t xr = make_rsrc(a.x, K * 2);
-        for (uint32_t t = threadIdx.x; t < KC * 256; t += 256) {
-            const uint32_t c = t >> 8, l = (t >> 2) & 63, j = t & 3;
-            xs[(c * 4 + j) * 64 + l] = bload128(xr, (c * 2048 + 32 * l + 8 * j) * 2);
-        }
-        __syncthreads();
+        const rsrc_t xr = make_rsrc(a.x, (uint32_t)(((int64_t)(MM - 1) * a.ldx + a.k) * 2));
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 v = bload128(xr, (uint32_t)(m * a.ldx * 2) + ((c0 + h) * 2048 + 32 * lane + 8 * j) * 2);
+                    xq[m][h][4 * j] = v.x;
+                    xq[m][h][4 * j + 1] = v.y;
+                    xq[m][h][4 * j + 2] = v.z;
+                    xq[m][h][4 * j + 3] = v.w;
+                }
     }
     const rsrc_t wr = make_rsrc(a.wc, (uint32_t)(a.n * (a.k / 2)));
     const rsrc_t sr = PRE ? make_rsrc(a.ws, (uint32_t)(((a.n + 7) / 8) * KC * 512))
@@ -437,13 +448,13 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
     const uint32_t nsteps = (units - blockIdx.x + G - 1) / G;  // units blockIdx.x + i G < units
 
     auto load = [&](uint32_t i, u32x4 (&cw)[2], uint32_t (&sb)[2]) {
-        const uint32_t q = (blockIdx.x + i * G) * 8 + 2 * wave, row = q / KC, c = q - row * KC;
+        const uint32_t row = ((blockIdx.x + i * G) * 8 + 2 * wave) / KC;
         const bool ok = i < nsteps;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            cw[h] = bload128(wr, ok ? row * (K / 2) + (c + h) * 1024 + lane * 16 : kOOB);
-            const uint32_t so = PRE ? ((row >> 3) * KC + c + h) * 512 + lane * 8 + (row & 7)
-                                    : row * (K / 32) + (c + h) * 64 + lane;
+            cw[h] = bload128(wr, ok ? row * (K / 2) + (c0 + h) * 1024 + lane * 16 : kOOB);
+            const uint32_t so = PRE ? ((row >> 3) * KC + c0 + h) * 512 + lane * 8 + (row & 7)
+                                    : row * (K / 32) + (c0 + h) * 64 + lane;
             sb[h] = bload8(sr, ok ? so : kOOB);
         }
     };
@@ -452,27 +463,27 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
     load(0, cw, sb);
     for (uint32_t i = 0; i < nsteps; ++i) {
         load(i + 1, cn, sn);
-        const uint32_t q = (blockIdx.x + i * G) * 8 + 2 * wave, row = q / KC, c = q - row * KC;
-        float acc = 0.0f;
+        float acc[MM];
+#pragma unroll
+        for (int m = 0; m < MM; ++m) acc[m] = 0.0f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint32_t bw[16];
             dequant32<32, FMT>(cw[h], sb[h], bw);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // components through plain registers: a bit_cast of a vector element compiles
-                // to element 0 with this compiler
-                const u32x4 xv = xs[((c + h) * 4 + j) * 64 + lane];
-                const uint32_t xq[4] = {xv.x, xv.y, xv.z, xv.w};
+            for (int m = 0; m < MM; ++m)
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq[t]),
-                                                          __builtin_bit_cast(bf16x2, bw[4 * j + t]), acc, false);
-            }
+                for (int t = 0; t < 16; ++t)
+                    acc[m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq[m][h][t]),
+                                                             __builtin_bit_cast(bf16x2, bw[t]), acc[m], false);
         }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-        if (lane == 0) part[i][wave] = acc;
+        for (int m = 0; m < MM; ++m) {
+            float v = acc[m];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            if (lane == 0) part[i][wave][m] = v;
+        }
         cw[0] = cn[0];
         cw[1] = cn[1];
         sb[0] = sn[0];
@@ -481,25 +492,35 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
     __syncthreads();
     // a unit holds 8 / KC rows; row rr of it sums the partials of waves rr KC/2 .. +KC/2-1
     const uint32_t rpu = 8 / KC;
-    if (threadIdx.x < nsteps * rpu) {
-        const uint32_t i = threadIdx.x / rpu, rr = threadIdx.x - i * rpu;
+    if (threadIdx.x < nsteps * rpu * MM) {
+        const uint32_t m = threadIdx.x % MM, ir = threadIdx.x / MM, i = ir / rpu, rr = ir - i * rpu;
         float v = 0.0f;
-        for (uint32_t w = rr * (KC / 2); w < (rr + 1) * (KC / 2); ++w) v += part[i][w];
-        store_y<OUT_BF16>(a.y, a.ldy, 0, (int64_t)(blockIdx.x + i * G) * rpu + rr, v * a.g);
+        for (uint32_t w = rr * (KC / 2); w < (rr + 1) * (KC / 2); ++w) v += part[i][w][m];
+        store_y<OUT_BF16>(a.y, a.ldy, m, (int64_t)(blockIdx.x + i * G) * rpu + rr, v * a.g);
     }
 }
 
 // the sweep's shape conditions; returns the unit count (0: not applicable)
 static uint32_t sweep_units(const GemmArgs& a)
 {
-    if (a.m != 1 || a.block != 32) return 0;
+    if (a.m < 1 || a.m > 2 || a.block != 32) return 0;
     if (a.k != 4096 && a.k != 8192 && a.k != 16384) return 0;  // 2, 4 or 8 chunks per row
+    if (((a.m - 1) * a.ldx + a.k) * 2 >= (int64_t(1) << 31)) return 0;
     const int64_t chunks = a.n * (a.k / 2048);
     if (chunks % 8 != 0) return 0;
     const int64_t units = chunks / 8;
     const int64_t g = units < SW_GRID ? units : SW_GRID;
     if (units == 0 || (units + g - 1) / g > SW_MAX_STEPS) return 0;
     return (uint32_t)units;
+}
+
+template <int FMT, bool OUT_BF16, int MM>
+static hipError_t launch_sweep(const GemmArgs& a, uint32_t units, hipStream_t st)
+{
+    const dim3 grid(units < SW_GRID ? units : SW_GRID);
+    if (a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM>), grid, dim3(256), 0, st, a, units);
+    else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM>), grid, dim3(256), 0, st, a, units);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -639,6 +660,10 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
                            dim3(256), 0, st, a);
         return hipGetLastError();
     }
+    if (const uint32_t units = sweep_units(a)) {
+        if (a.m == 1) return launch_sweep<FMT, OUT_BF16, 1>(a, units, st);
+        return launch_sweep<FMT, OUT_BF16, 2>(a, units, st);
+    }
     if (a.m >= 2 && a.m <= 16) {
         const unsigned tiles = (unsigned)((a.n + 15) / 16);
         unsigned g = tiles < 256 ? tiles : 256;                       // one workgroup per CU
@@ -656,12 +681,6 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
 #undef MXL
             default: return hipErrorInvalidValue;
         }
-        return hipGetLastError();
-    }
-    if (const uint32_t units = sweep_units(a)) {
-        const dim3 grid(units < SW_GRID ? units : SW_GRID);
-        if (a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true>), grid, dim3(256), 0, st, a, units);
-        else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false>), grid, dim3(256), 0, st, a, units);
         return hipGetLastError();
     }
     if (a.m == 1) {

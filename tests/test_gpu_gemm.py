@@ -60,20 +60,24 @@ def test_gemv_a16(m, fmt, block):
         check(x, c, s, cd, sd, block, fmt, 1.0, "a16", out)
 
 
-# m = 1 with block 32 and k in {4096, 8192, 16384} on short streams takes the sweeping GEMV
+# m <= 2 with block 32 and k in {4096, 8192, 16384} on short streams takes the sweeping GEMV
 # (a grid of at most 1024 workgroups, up to 4 steps each, over 8 KB units of codes): one and
 # several steps, workgroups with different step counts (unit counts just past 1024), rows
-# per unit 4, 2 and 1.  The preshuffled layout must give bit-identical results.
+# per unit 4, 2 and 1, one and two rows of X.  For m = 1 the preshuffled layout must give
+# bit-identical results.
+@pytest.mark.parametrize("m", [1, 2])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(1000, 4096), (8000, 4096), (2050, 8192), (777, 16384), (4096, 16384)])
-def test_gemv_sweep(fmt, n, k):
+def test_gemv_sweep(fmt, n, k, m):
     g = float(np.float32(0.37)) if fmt != "e8m0" else 1.0
-    x = synth.normal((1, k), "bf16", f"sw.x.{k}", 1.0)
+    x = synth.normal((m, k), "bf16", f"sw.x.{k}.{m}", 1.0)
     w = synth.normal((n, k), "bf16", f"sw.w.{n}.{k}", 0.02, 0.01, 20.0)
     c, s, cd, sd = quantize_ref(w, 32, fmt, g)
     yr = {}
     for out in ("f32", "bf16"):
-        yr[out] = check(x, c, s, cd, sd, 32, fmt, g, "a16", out, what=f"sweep {fmt} {n}x{k} {out}")
+        yr[out] = check(x, c, s, cd, sd, 32, fmt, g, "a16", out, what=f"sweep m={m} {fmt} {n}x{k} {out}")
+    if m > 1:
+        return
     cp, sp = mx.mx_quantize(bf16_dev(w), 32, fmt, g, layout="preshuffled")
     for out, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
         yp = mx.mx_gemm(bf16_dev(x), cp, sp, 32, fmt, g, "a16", out_dtype=dt, layout="preshuffled")
