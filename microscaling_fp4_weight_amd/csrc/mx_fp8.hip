@@ -525,24 +525,24 @@ static hipError_t launch_w8(const W8Args& a, hipStream_t st)
                            dim3(f8::THREADS), 0, st, a);
         return hipGetLastError();
     }
-    if (a.m > 16 && w8_prefers_tiled(a)) {
-        // the pipelined matrix-core kernel of the W4A16 product, with FP8 codes
-        GemmArgs g{};
-        g.x = a.x;
-        g.m = a.m;
-        g.n = a.n;
-        g.k = a.k;
-        g.ldx = a.ldx;
-        g.wc = a.wc;
-        g.ws = a.ws;
-        g.block = a.block;
-        g.fmt = a.fmt;
-        g.g = (float)a.g;
-        g.y = a.y;
-        g.y_bf16 = a.y_bf16;
-        g.ldy = a.ldy;
-        if (a16_uses_tiled(g)) return launch_gemm_w8_tiled(g, st);
-    }
+    // the W4A16 kernels with FP8 codes: the sweeping GEMV (m <= 2, short streams) and the
+    // pipelined matrix-core kernel (large products)
+    GemmArgs g{};
+    g.x = a.x;
+    g.m = a.m;
+    g.n = a.n;
+    g.k = a.k;
+    g.ldx = a.ldx;
+    g.wc = a.wc;
+    g.ws = a.ws;
+    g.block = a.block;
+    g.fmt = a.fmt;
+    g.g = (float)a.g;
+    g.y = a.y;
+    g.y_bf16 = a.y_bf16;
+    g.ldy = a.ldy;
+    if (w8_uses_sweep(g)) return launch_gemv_sweep_w8(g, st);
+    if (a.m > 16 && w8_prefers_tiled(a) && a16_uses_tiled(g)) return launch_gemm_w8_tiled(g, st);
     const bool small = a.m <= 16;
     const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)((a.m + (small ? 16 : 64) - 1) / (small ? 16 : 64)));
 #define MXW8(B)                                                                                                  \

@@ -416,16 +416,20 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
 constexpr uint32_t SW_GRID = 1024;
 constexpr uint32_t SW_MAX_STEPS = 4;
 
-// MM: rows of X (m == MM)
-template <int FMT, bool OUT_BF16, bool PRE, int MM>
+// MM: rows of X (m == MM).  W8: FP8 (E4M3) codes, a byte per element: a chunk of 2048 k is
+// then 2 KB, read as two 1 KB halves, and lane l holds k = 16 l .. 16 l + 15 of each half (two
+// 32-blocks, so two scale bytes); with FP4 codes lane l holds k = 32 l .. 32 l + 31 of the chunk.
+template <int FMT, bool OUT_BF16, bool PRE, int MM, bool W8>
 __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint32_t units)
 {
+    constexpr int NH = W8 ? 2 : 1;  // code loads per chunk
     __shared__ float part[SW_MAX_STEPS][4][MM];
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint32_t K = (uint32_t)a.k, KC = K / 2048, G = gridDim.x;
     const uint32_t c0 = (2 * (uint32_t)wave) & (KC - 1);  // the wave's first chunk of k
+    const uint32_t rowb = W8 ? K : K / 2;                   // code bytes per row
 
-    // X of the wave's chunk pair: lane l holds k = (c0 + h) 2048 + 32 l .. +31 of each row
+    // X of the wave's chunk pair in the order of the lane's 32 k (piece j = 8 k)
     uint32_t xq[MM][2][16];
     {
         const rsrc_t xr = make_rsrc(a.x, (uint32_t)(((int64_t)(MM - 1) * a.ldx + a.k) * 2));
@@ -435,30 +439,40 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const u32x4 v = bload128(xr, (uint32_t)(m * a.ldx * 2) + ((c0 + h) * 2048 + 32 * lane + 8 * j) * 2);
+                    const uint32_t kx = W8 ? (c0 + h) * 2048 + (j >> 1) * 1024 + 16 * lane + 8 * (j & 1)
+                                           : (c0 + h) * 2048 + 32 * lane + 8 * j;
+                    const u32x4 v = bload128(xr, (uint32_t)(m * a.ldx * 2) + kx * 2);
                     xq[m][h][4 * j] = v.x;
                     xq[m][h][4 * j + 1] = v.y;
                     xq[m][h][4 * j + 2] = v.z;
                     xq[m][h][4 * j + 3] = v.w;
                 }
     }
-    const rsrc_t wr = make_rsrc(a.wc, (uint32_t)(a.n * (a.k / 2)));
+    const rsrc_t wr = make_rsrc(a.wc, (uint32_t)(a.n * rowb));
     const rsrc_t sr = PRE ? make_rsrc(a.ws, (uint32_t)(((a.n + 7) / 8) * KC * 512))
                           : make_rsrc(a.ws, (uint32_t)(a.n * (a.k / 32)));
     const uint32_t nsteps = (units - blockIdx.x + G - 1) / G;  // units blockIdx.x + i G < units
 
-    auto load = [&](uint32_t i, u32x4 (&cw)[2], uint32_t (&sb)[2]) {
+    auto load = [&](uint32_t i, u32x4 (&cw)[2][NH], uint32_t (&sb)[2]) {
         const uint32_t row = ((blockIdx.x + i * G) * 8 + 2 * wave) / KC;
         const bool ok = i < nsteps;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            cw[h] = bload128(wr, ok ? row * (K / 2) + (c0 + h) * 1024 + lane * 16 : kOOB);
-            const uint32_t so = PRE ? ((row >> 3) * KC + c0 + h) * 512 + lane * 8 + (row & 7)
-                                    : row * (K / 32) + (c0 + h) * 64 + lane;
-            sb[h] = bload8(sr, ok ? so : kOOB);
+            const uint32_t c = c0 + h;
+            if constexpr (W8) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) cw[h][e] = bload128(wr, ok ? row * rowb + c * 2048 + e * 1024 + lane * 16 : kOOB);
+                const uint32_t so = row * (K / 32) + c * 64 + (lane >> 1);
+                sb[h] = bload8(sr, ok ? so : kOOB) | (bload8(sr, ok ? so + 32 : kOOB) << 8);
+            } else {
+                cw[h][0] = bload128(wr, ok ? row * rowb + c * 1024 + lane * 16 : kOOB);
+                const uint32_t so = PRE ? ((row >> 3) * KC + c) * 512 + lane * 8 + (row & 7)
+                                        : row * (K / 32) + c * 64 + lane;
+                sb[h] = bload8(sr, ok ? so : kOOB);
+            }
         }
     };
-    u32x4 cw[2], cn[2];
+    u32x4 cw[2][NH], cn[2][NH];
     uint32_t sb[2], sn[2];
     load(0, cw, sb);
     for (uint32_t i = 0; i < nsteps; ++i) {
@@ -469,7 +483,13 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint32_t bw[16];
-            dequant32<32, FMT>(cw[h], sb[h], bw);
+            if constexpr (W8) {
+                const uint32_t c8[8] = {cw[h][0].x, cw[h][0].y, cw[h][0].z, cw[h][0].w,
+                                        cw[h][1].x, cw[h][1].y, cw[h][1].z, cw[h][1].w};
+                dequant_w8<16, FMT>(c8, sb[h], bw);  // elements 0..15: first byte, 16..31: second
+            } else {
+                dequant32<32, FMT>(cw[h][0], sb[h], bw);
+            }
 #pragma unroll
             for (int m = 0; m < MM; ++m)
 #pragma unroll
@@ -484,10 +504,12 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
             for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
             if (lane == 0) part[i][wave][m] = v;
         }
-        cw[0] = cn[0];
-        cw[1] = cn[1];
-        sb[0] = sn[0];
-        sb[1] = sn[1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int e = 0; e < NH; ++e) cw[h][e] = cn[h][e];
+            sb[h] = sn[h];
+        }
     }
     __syncthreads();
     // a unit holds 8 / KC rows; row rr of it sums the partials of waves rr KC/2 .. +KC/2-1
@@ -514,13 +536,29 @@ static uint32_t sweep_units(const GemmArgs& a)
     return (uint32_t)units;
 }
 
-template <int FMT, bool OUT_BF16, int MM>
+template <int FMT, bool OUT_BF16, int MM, bool W8>
 static hipError_t launch_sweep(const GemmArgs& a, uint32_t units, hipStream_t st)
 {
     const dim3 grid(units < SW_GRID ? units : SW_GRID);
-    if (a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM>), grid, dim3(256), 0, st, a, units);
-    else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM>), grid, dim3(256), 0, st, a, units);
+    if (!W8 && a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>), grid, dim3(256), 0, st, a, units);
+    else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>), grid, dim3(256), 0, st, a, units);
     return hipGetLastError();
+}
+
+bool w8_uses_sweep(const GemmArgs& a) { return !a.ws_pre && sweep_units(a) != 0; }
+
+hipError_t launch_gemv_sweep_w8(const GemmArgs& a, hipStream_t st)
+{
+    const uint32_t units = sweep_units(a);
+    if (units == 0 || a.ws_pre) return hipErrorInvalidValue;
+#define MXF(F)                                                                                             \
+    if (a.fmt == F) {                                                                                      \
+        if (a.m == 1) return a.y_bf16 ? launch_sweep<F, true, 1, true>(a, units, st) : launch_sweep<F, false, 1, true>(a, units, st); \
+        return a.y_bf16 ? launch_sweep<F, true, 2, true>(a, units, st) : launch_sweep<F, false, 2, true>(a, units, st);              \
+    }
+    MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
+#undef MXF
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -661,8 +699,8 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
         return hipGetLastError();
     }
     if (const uint32_t units = sweep_units(a)) {
-        if (a.m == 1) return launch_sweep<FMT, OUT_BF16, 1>(a, units, st);
-        return launch_sweep<FMT, OUT_BF16, 2>(a, units, st);
+        if (a.m == 1) return launch_sweep<FMT, OUT_BF16, 1, false>(a, units, st);
+        return launch_sweep<FMT, OUT_BF16, 2, false>(a, units, st);
     }
     if (a.m >= 2 && a.m <= 16) {
         const unsigned tiles = (unsigned)((a.n + 15) / 16);

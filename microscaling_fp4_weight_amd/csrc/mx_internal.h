@@ -106,6 +106,9 @@ bool a16_uses_tiled(const GemmArgs& a);
 hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st);
 // the same pipelined kernel with FP8 (E4M3) weight codes, n x k bytes (same conditions)
 hipError_t launch_gemm_w8_tiled(const GemmArgs& a, hipStream_t st);
+// whether the m <= 2 sweeping GEMV takes FP8 codes of this shape, and its launcher
+bool w8_uses_sweep(const GemmArgs& a);
+hipError_t launch_gemv_sweep_w8(const GemmArgs& a, hipStream_t st);
 
 struct ErrArgs {
     const void* x;

@@ -181,6 +181,25 @@ def test_gemm_fp8_tiled_tensor_scale_and_strides(fmt, ldy):
     _gemm_fp8_case(300, 4000, 1024, fmt, g, f"ld{ldy}", ldx=1032, ldy=ldy)
 
 
+# m <= 2, block 32, k in {4096, 8192, 16384}, short streams: the sweeping GEMV with FP8 codes
+# (2 KB chunks of 2048 k read as two 1 KB halves; a lane's 32 k span two blocks): one and
+# several steps, uneven step counts, 1 / 2 / 4 rows per unit, one and two rows of X.
+@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(1000, 4096), (8000, 4096), (2050, 8192), (777, 16384)])
+def test_gemv_fp8_sweep(n, k, fmt, m):
+    g = float(np.float32(0.37)) if fmt == "ue5m3" else 1.0
+    x = synth.normal((m, k), "bf16", f"sw8.x.{k}.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", f"sw8.w.{n}.{k}", 0.02 / g, 0.01, 20.0)
+    rc, rs = oracle.quantize_fp8(w, 32, fmt, g)
+    cd, sd = torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV)
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 32, fmt, g)
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, fmt, g, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 sweep m={m} {fmt} {n}x{k} {dt}")
+
+
 def test_gemm_fp8_prefill_shape_sampled():
     # 70B FFN prefill shape: m 2048, k 8192, n 28672, block 32, E8M0; sampled rows and columns
     w = synth.c4_weight()
