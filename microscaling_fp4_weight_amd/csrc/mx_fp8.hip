@@ -247,6 +247,31 @@ __device__ __forceinline__ float dq_value(uint32_t c, double sg)
     return m7 == 0x7Fu ? __builtin_nanf("") : ((c & 0x80u) ? -f : f);  // 0x7F, 0xFF: NaN
 }
 
+// |e| of E4M3 magnitude code m (0..0x7E) as fp32, exact
+__device__ __forceinline__ float e4m3_mag_f32(uint32_t m)
+{
+    const uint32_t ex = m >> 3, mn = m & 7u;
+    return ex ? u2f(((ex + 120u) << 23) | (mn << 20)) : (float)mn * 0x1p-9f;
+}
+
+// The same value in fp32: e * s has at most 8 significant bits and lies in [2^-136, 2^128)
+// when s <= 2^118, so it is exact in fp32 (subnormals included) and one fp32 multiply by g
+// rounds e * s * g once, as the fp64 form does.  Larger scales (E8M0 bytes above 245) take
+// the fp64 form.
+__device__ __forceinline__ float dq_value_f32(uint32_t c, float s, float g)
+{
+    const uint32_t m7 = c & 0x7Fu;
+    const float f = (e4m3_mag_f32(m7) * s) * g;
+    return m7 == 0x7Fu ? __builtin_nanf("") : ((c & 0x80u) ? -f : f);  // 0x7F, 0xFF: NaN
+}
+
+template <int FMT>
+__device__ __forceinline__ float scale_value_f32(uint32_t byte)
+{
+    if constexpr (FMT == FMT_E8M0) return e8m0_value(byte);
+    else return fp8_value<FMT>(byte);
+}
+
 template <int BLOCK, int FMT, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) void dequantize_fp8_kernel(const uint8_t* __restrict__ codes,
                                                                  const uint8_t* __restrict__ scales,
@@ -259,18 +284,34 @@ __global__ __launch_bounds__(THREADS) void dequantize_fp8_kernel(const uint8_t* 
     const uint32_t row = upr_div.div(u), c8 = u - row * upr;
     const u32x2 cv = *reinterpret_cast<const u32x2*>(codes + (int64_t)row * k + (int64_t)c8 * 8);
     const uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
-    double sg[BLOCK < 8 ? 2 : 1];
+    constexpr int NS = BLOCK < 8 ? 2 : 1;  // scale bytes of the unit
+    uint32_t sb[NS];
     if constexpr (BLOCK < 8) {
-        sg[0] = scale_value_f64<FMT>(sp[c8 * 2]) * g;
-        sg[1] = scale_value_f64<FMT>(sp[c8 * 2 + 1]) * g;
+        sb[0] = sp[c8 * 2];
+        sb[1] = sp[c8 * 2 + 1];
     } else {
-        sg[0] = scale_value_f64<FMT>(sp[(c8 * 8) / BLOCK]) * g;
+        sb[0] = sp[(c8 * 8) / BLOCK];
     }
-    float v[8];
+    bool wide = false;  // an E8M0 scale above 2^118
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t c = ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3))) & 0xFFu;
-        v[e] = dq_value(c, sg[BLOCK < 8 ? e / 4 : 0]);
+    for (int i = 0; i < NS; ++i) wide |= FMT == FMT_E8M0 && sb[i] > 245u;
+    float v[8];
+    if (!wide) {
+        const float gf = (float)g;
+        float sf[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) sf[i] = scale_value_f32<FMT>(sb[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t c = ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3))) & 0xFFu;
+            v[e] = dq_value_f32(c, sf[BLOCK < 8 ? e / 4 : 0], gf);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t c = ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3))) & 0xFFu;
+            v[e] = dq_value(c, scale_value_f64<FMT>(sb[BLOCK < 8 ? e / 4 : 0]) * g);
+        }
     }
     if constexpr (OUT_BF16) {
         uint32_t o[4];
