@@ -171,6 +171,14 @@ __device__ __forceinline__ uint32_t scale_code_g(uint32_t abits, double six_g)
     else return fp8_code_f64<FMT>(v);
 }
 
+// Decoded scale as fp32 (exact; E8M0 byte 0 is the fp32 denormal 2^-127).
+template <int FMT>
+__device__ __forceinline__ float scale_value_f32(uint32_t byte)
+{
+    if constexpr (FMT == FMT_E8M0) return e8m0_value(byte);
+    else return fp8_value<FMT>(byte);
+}
+
 // Decoded scale as fp64 (exact).
 template <int FMT>
 __device__ __forceinline__ double scale_value_f64(uint32_t byte)

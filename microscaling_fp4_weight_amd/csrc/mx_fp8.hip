@@ -265,13 +265,6 @@ __device__ __forceinline__ float dq_value_f32(uint32_t c, float s, float g)
     return m7 == 0x7Fu ? __builtin_nanf("") : ((c & 0x80u) ? -f : f);  // 0x7F, 0xFF: NaN
 }
 
-template <int FMT>
-__device__ __forceinline__ float scale_value_f32(uint32_t byte)
-{
-    if constexpr (FMT == FMT_E8M0) return e8m0_value(byte);
-    else return fp8_value<FMT>(byte);
-}
-
 template <int BLOCK, int FMT, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) void dequantize_fp8_kernel(const uint8_t* __restrict__ codes,
                                                                  const uint8_t* __restrict__ scales,

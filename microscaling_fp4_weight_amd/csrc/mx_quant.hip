@@ -260,6 +260,10 @@ __global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
 // ---------------------------------------------------------------------------------------
 // dequantize, fast path: one lane per 32 consecutive elements
 // ---------------------------------------------------------------------------------------
+// G1: the converter applies pow2 and mant finishes e * s (exact).  Otherwise pow2 is the scale
+// s itself and mant is g: e * s has at most 6 significant bits and lies in [2^-128, 2^128) for
+// s <= 2^125, so it is exact in fp32 (subnormals included) and one fp32 multiply rounds e*s*g
+// once; sg = s * g in fp64 (non-zero only for E8M0 scales above 2^125) selects the fp64 form.
 template <int FMT, bool G1, bool OUT_BF16>
 __device__ __forceinline__ void dec_byte_pair(uint32_t cw, int sel, float pow2, float mant,
                                              double sg, float& lo, float& hi)
@@ -275,7 +279,10 @@ __device__ __forceinline__ void dec_byte_pair(uint32_t cw, int sel, float pow2, 
     if constexpr (G1) {
         lo = (FMT == FMT_E8M0) ? f.x : f.x * mant;
         hi = (FMT == FMT_E8M0) ? f.y : f.y * mant;
-    } else {  // one rounding of the exact e * s * g
+    } else if (sg == 0.0) {  // one rounding of the exact e * s * g
+        lo = (f.x * pow2) * mant;
+        hi = (f.y * pow2) * mant;
+    } else {
         lo = (float)((double)f.x * sg);
         hi = (float)((double)f.y * sg);
     }
@@ -342,8 +349,11 @@ __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
                     const DecG1 p = dec_params_g1<FMT>(byte);
                     pow2 = p.pow2;
                     mant = p.mant;
-                } else {
+                } else if (FMT == FMT_E8M0 && byte > 252u) {
                     sg = scale_value_f64<FMT>(byte) * g;
+                } else {
+                    pow2 = scale_value_f32<FMT>(byte);
+                    mant = (float)g;
                 }
                 float lo, hi;
                 dec_byte_pair<FMT, G1, OUT_BF16>(cw[h], j, pow2, mant, sg, lo, hi);
@@ -390,8 +400,11 @@ __global__ __launch_bounds__(kThreads) void dequantize_generic_kernel(
         const DecG1 p = dec_params_g1<FMT>(sb);
         pow2 = p.pow2;
         mant = p.mant;
-    } else {
+    } else if (FMT == FMT_E8M0 && sb > 252u) {
         sg = scale_value_f64<FMT>(sb) * g;
+    } else {
+        pow2 = scale_value_f32<FMT>(sb);
+        mant = (float)g;
     }
     float lo, hi;
     dec_byte_pair<FMT, G1, OUT_BF16>(cb, 0, pow2, mant, sg, lo, hi);
