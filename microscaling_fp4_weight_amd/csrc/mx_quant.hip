@@ -290,7 +290,9 @@ __device__ __forceinline__ void dec_byte_pair(uint32_t cw, int sel, float pow2, 
 
 constexpr int kDeqUnits = 2;  // 8-element units per lane
 
-template <int BLOCK, int FMT, bool G1, bool OUT_BF16>
+// LAY: scale layout, fixed at compile time so that the row-major kernel carries no layout
+// branches between its loads (0 row-major, 1 tiled, 2 preshuffled; 1 and 2 with block 32 only)
+template <int BLOCK, int FMT, bool G1, bool OUT_BF16, int LAY>
 __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     FastDiv units_per_row, uint32_t upr, uint32_t total_units, int64_t k, double g,
@@ -316,9 +318,9 @@ __global__ __launch_bounds__(kThreads) void dequantize_fast_kernel(
                 const uint32_t v = *reinterpret_cast<const uint16_t*>(sp + c8[h] * 2);
                 sb[h][0] = v & 0xFF;
                 sb[h][1] = v >> 8;
-            } else if (BLOCK == 32 && ts_ks != 0) {  // tiled scale layout
+            } else if constexpr (LAY == 1) {  // tiled scale layout
                 sb[h][0] = sb[h][1] = scales[tiled_scale_off(row[h], c8[h] / 4, ts_ks)];
-            } else if (BLOCK == 32 && ps_cb != 0) {  // preshuffled scale layout
+            } else if constexpr (LAY == 2) {  // preshuffled scale layout
                 sb[h][0] = sb[h][1] = scales[pre_scale_off(row[h], c8[h] / 4, ps_cb)];
             } else {
                 sb[h][0] = sb[h][1] = sp[(c8[h] * 8) / BLOCK];
@@ -469,10 +471,17 @@ static hipError_t launch_dequantize_fmt(const DequantArgs& a, hipStream_t st)
         const dim3 grid((total + per_wg - 1) / per_wg);
         const int64_t ldb = a.ldy * (OUT_BF16 ? 2 : 4);
         switch (a.block) {
-#define MXD(B) case B: hipLaunchKernelGGL((dequantize_fast_kernel<B, FMT, G1, OUT_BF16>), grid, dim3(kThreads), 0, st, \
-                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb, a.ts_ks, a.ps_cb); break;
-            MXD(4) MXD(8) MXD(16) MXD(32) MXD(64) MXD(128) MXD(256)
+#define MXDL(B, L) hipLaunchKernelGGL((dequantize_fast_kernel<B, FMT, G1, OUT_BF16, L>), grid, dim3(kThreads), 0, st, \
+                   a.codes, a.scales, FastDiv::make(upr), upr, total, a.k, a.g, (uint8_t*)a.y, ldb, a.ts_ks, a.ps_cb)
+#define MXD(B) case B: MXDL(B, 0); break;
+            MXD(4) MXD(8) MXD(16) MXD(64) MXD(128) MXD(256)
+            case 32:
+                if (a.ts_ks != 0) MXDL(32, 1);
+                else if (a.ps_cb != 0) MXDL(32, 2);
+                else MXDL(32, 0);
+                break;
 #undef MXD
+#undef MXDL
             default: return hipErrorInvalidValue;
         }
     } else {
