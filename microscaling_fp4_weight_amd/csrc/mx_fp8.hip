@@ -561,22 +561,22 @@ static hipError_t launch_w8(const W8Args& a, hipStream_t st)
     }
     // the W4A16 kernels with FP8 codes: the sweeping GEMV (m <= 2, short streams) and the
     // pipelined matrix-core kernel (large products)
-    GemmArgs g{};
-    g.x = a.x;
-    g.m = a.m;
-    g.n = a.n;
-    g.k = a.k;
-    g.ldx = a.ldx;
-    g.wc = a.wc;
-    g.ws = a.ws;
-    g.block = a.block;
-    g.fmt = a.fmt;
-    g.g = (float)a.g;
-    g.y = a.y;
-    g.y_bf16 = a.y_bf16;
-    g.ldy = a.ldy;
-    if (w8_uses_sweep(g)) return launch_gemv_sweep_w8(g, st);
-    if (a.m > 16 && w8_prefers_tiled(a) && a16_uses_tiled(g)) return launch_gemm_w8_tiled(g, st);
+    GemmArgs ga{};
+    ga.x = a.x;
+    ga.m = a.m;
+    ga.n = a.n;
+    ga.k = a.k;
+    ga.ldx = a.ldx;
+    ga.wc = a.wc;
+    ga.ws = a.ws;
+    ga.block = a.block;
+    ga.fmt = a.fmt;
+    ga.g = (float)a.g;
+    ga.y = a.y;
+    ga.y_bf16 = a.y_bf16;
+    ga.ldy = a.ldy;
+    if (w8_uses_sweep(ga)) return launch_gemv_sweep_w8(ga, st);
+    if (a.m > 16 && w8_prefers_tiled(a) && a16_uses_tiled(ga)) return launch_gemm_w8_tiled(ga, st);
     const bool small = a.m <= 16;
     const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)((a.m + (small ? 16 : 64) - 1) / (small ? 16 : 64)));
 #define MXW8(B)                                                                                                  \
