@@ -409,9 +409,9 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
 // n 14336, k 4096: 9.0 against 11.2 us per launch).  Wave w of a workgroup takes chunks 2w,
 // 2w+1 of the unit; k / 2048 being 2, 4 or 8, they lie in one row and are the same two chunks
 // of k, 2w mod (k / 2048) and the next, at every step, so the wave holds its X for them in
-// registers, loaded once.  The next step's codes and scales are in flight while a step is
-// computed.  Each wave's partial sums go to LDS; the rows of the workgroup's units are
-// summed at the end in a fixed order.
+// registers, loaded once (through LDS, once per workgroup).  The next step's codes and scales
+// are in flight while a step is computed.  Each wave's partial sums go to LDS; the rows of
+// the workgroup's units are summed at the end in a fixed order.
 // ---------------------------------------------------------------------------------------
 constexpr uint32_t SW_GRID = 1024;
 constexpr uint32_t SW_MAX_STEPS = 4;
@@ -429,10 +429,20 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
     const uint32_t c0 = (2 * (uint32_t)wave) & (KC - 1);  // the wave's first chunk of k
     const uint32_t rowb = W8 ? K : K / 2;                   // code bytes per row
 
-    // X of the wave's chunk pair in the order of the lane's 32 k (piece j = 8 k)
+    // X of the wave's chunk pair in the order of the lane's 32 k (piece j = 8 k).  The m rows
+    // of X are staged once per workgroup through LDS (m k / 8 pieces of 16 bytes, m k 2 bytes
+    // of dynamic LDS): each wave needs all of it when k / 2048 is 2, and fetching it once per
+    // workgroup instead of once per wave cuts its L2 traffic fourfold (measured: n 4096, k 4096,
+    // m 1: 5.4 -> 4.6 us).
+    extern __shared__ u32x4 xs[];
     uint32_t xq[MM][2][16];
     {
         const rsrc_t xr = make_rsrc(a.x, (uint32_t)(((int64_t)(MM - 1) * a.ldx + a.k) * 2));
+        for (uint32_t t = threadIdx.x; t < MM * (K / 8); t += 256) {
+            const uint32_t m = t / (K / 8), p = t - m * (K / 8);
+            xs[t] = bload128(xr, (uint32_t)(m * a.ldx * 2) + p * 16);
+        }
+        __syncthreads();
 #pragma unroll
         for (int m = 0; m < MM; ++m)
 #pragma unroll
@@ -441,7 +451,7 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t kx = W8 ? (c0 + h) * 2048 + (j >> 1) * 1024 + 16 * lane + 8 * (j & 1)
                                            : (c0 + h) * 2048 + 32 * lane + 8 * j;
-                    const u32x4 v = bload128(xr, (uint32_t)(m * a.ldx * 2) + kx * 2);
+                    const u32x4 v = xs[m * (K / 8) + kx / 8];
                     xq[m][h][4 * j] = v.x;
                     xq[m][h][4 * j + 1] = v.y;
                     xq[m][h][4 * j + 2] = v.z;
@@ -540,8 +550,9 @@ template <int FMT, bool OUT_BF16, int MM, bool W8>
 static hipError_t launch_sweep(const GemmArgs& a, uint32_t units, hipStream_t st)
 {
     const dim3 grid(units < SW_GRID ? units : SW_GRID);
-    if (!W8 && a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>), grid, dim3(256), 0, st, a, units);
-    else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>), grid, dim3(256), 0, st, a, units);
+    const size_t lds = (size_t)MM * a.k * 2;  // X; at most 64 KB (m <= 2, k <= 16384)
+    if (!W8 && a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>), grid, dim3(256), lds, st, a, units);
+    else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>), grid, dim3(256), lds, st, a, units);
     return hipGetLastError();
 }
 
