@@ -210,6 +210,92 @@ __global__ __launch_bounds__(THREADS) void quantize_fp8_kernel(const uint8_t* __
     }
 }
 
+// bf16 input, g == 1, k % 32 == 0: a lane takes 32 elements (four 16-byte loads, two 16-byte
+// code stores), so that the block scale (an fp64 division) and the addressing are paid once per
+// 32 elements instead of per 8; blocks of up to 32 are lane-local, larger ones span BLOCK / 32
+// lanes (absmax by shuffles).  Elements go through the hardware converter as above.
+template <int BLOCK, int FMT>
+__global__ __launch_bounds__(THREADS) void quantize_fp8_hw32_kernel(const uint8_t* __restrict__ x, int64_t ldx_bytes,
+                                                                    FastDiv gpr_div, uint32_t gpr, uint32_t total,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    uint8_t* __restrict__ scales, int64_t k)
+{
+    constexpr int NB = BLOCK <= 32 ? 32 / BLOCK : 1;  // blocks (or block parts) per lane
+    constexpr int WPB = 16 / NB;                       // bf16 pairs (words) per lane-local part
+    constexpr int LANES = BLOCK > 32 ? BLOCK / 32 : 1;
+    const uint32_t u = blockIdx.x * THREADS + threadIdx.x;
+    const bool act = u < total;
+    const uint32_t row = act ? gpr_div.div(u) : 0u;
+    const uint32_t gc = act ? u - row * gpr : 0u;  // the lane holds elements 32 gc .. +31
+
+    uint32_t w[16];  // word j: elements 2j (low half), 2j + 1
+    if (act) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(x + (int64_t)row * ldx_bytes + (int64_t)gc * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 v = p[q];
+            w[4 * q] = v.x;
+            w[4 * q + 1] = v.y;
+            w[4 * q + 2] = v.z;
+            w[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j] = 0u;
+    }
+
+    uint32_t amax[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        u16x2 m = __builtin_bit_cast(u16x2, w[b * WPB] & 0x7FFF7FFFu);
+#pragma unroll
+        for (int j = 1; j < WPB; ++j)
+            m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[b * WPB + j] & 0x7FFF7FFFu));
+        amax[b] = (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+    }
+    if constexpr (LANES > 1) {
+#pragma unroll
+        for (int off = 1; off < LANES; off <<= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)amax[0], off);
+            amax[0] = o > amax[0] ? o : amax[0];
+        }
+    }
+
+    uint32_t sb[NB];
+    i16x2 h[8];  // code dword d: elements 4d .. 4d + 3
+#pragma unroll
+    for (int d = 0; d < 8; ++d) h[d] = i16x2{0, 0};
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        sb[b] = scale_code_g<FMT>(amax[b], 448.0);
+        const EncG1 p = enc_params_g1<FMT>(sb[b]);
+        const float lim = 448.0f * p.pow2;  // 448 * 2^E (exact, also for 2^-127)
+#pragma unroll
+        for (int jj = 0; jj < WPB; ++jj) {
+            const int j = b * WPB + jj;  // word j -> half j % 2 of code dword j / 2
+            if (j & 1) h[j >> 1] = enc_fp8_pair<FMT, 1>(h[j >> 1], w[j], p, lim);
+            else h[j >> 1] = enc_fp8_pair<FMT, 0>(h[j >> 1], w[j], p, lim);
+        }
+    }
+    if (!act) return;
+    u32x4* cp = reinterpret_cast<u32x4*>(codes + (int64_t)row * k + (int64_t)gc * 32);
+    cp[0] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                  __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
+    cp[1] = u32x4{__builtin_bit_cast(uint32_t, h[4]), __builtin_bit_cast(uint32_t, h[5]),
+                  __builtin_bit_cast(uint32_t, h[6]), __builtin_bit_cast(uint32_t, h[7])};
+    uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
+    if constexpr (NB == 1) {
+        if (LANES == 1 || (gc % LANES) == 0) sp[gc / LANES] = (uint8_t)sb[0];
+    } else if constexpr (NB == 2) {
+        *reinterpret_cast<uint16_t*>(sp + gc * 2) = (uint16_t)(sb[0] | (sb[1] << 8));
+    } else if constexpr (NB == 4) {
+        *reinterpret_cast<uint32_t*>(sp + gc * 4) = sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24);
+    } else {
+        *reinterpret_cast<u32x2*>(sp + gc * 8) = u32x2{sb[0] | (sb[1] << 8) | (sb[2] << 16) | (sb[3] << 24),
+                                                       sb[4] | (sb[5] << 8) | (sb[6] << 16) | (sb[7] << 24)};
+    }
+}
+
 // quantize, generic path: one thread per block (any k % block == 0, any alignment)
 template <int FMT, bool BF16>
 __global__ __launch_bounds__(THREADS) void quantize_fp8_generic_kernel(const uint8_t* __restrict__ x, int64_t ldx,
@@ -467,6 +553,22 @@ static hipError_t launch_q8(const QuantArgs& a, hipStream_t st)
         hipLaunchKernelGGL((f8::quantize_fp8_generic_kernel<FMT, BF16>), dim3((unsigned)((nblk + 255) / 256)),
                            dim3(f8::THREADS), 0, st, static_cast<const uint8_t*>(a.x), a.ldx, a.rows, a.k, a.block,
                            a.g, a.codes, a.scales);
+        return hipGetLastError();
+    }
+    if (BF16 && a.g == 1.0 && a.k % 32 == 0) {  // 32 elements per lane
+        const uint32_t gpr = (uint32_t)(a.k / 32), total = (uint32_t)(a.rows * gpr);
+        const FastDiv fd = FastDiv::make(gpr);
+        const dim3 grid((total + f8::THREADS - 1) / f8::THREADS);
+        switch (a.block) {
+#define MXH(B)                                                                                                         \
+    case B:                                                                                                            \
+        hipLaunchKernelGGL((f8::quantize_fp8_hw32_kernel<B, FMT>), grid, dim3(f8::THREADS), 0, st,                       \
+                           static_cast<const uint8_t*>(a.x), a.ldx * esz, fd, gpr, total, a.codes, a.scales, a.k); \
+        break;
+            MXH(4) MXH(8) MXH(16) MXH(32) MXH(64) MXH(128) MXH(256)
+#undef MXH
+            default: return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     }
     const uint32_t upr = (uint32_t)(a.k / 8), total = (uint32_t)(a.rows * upr);
