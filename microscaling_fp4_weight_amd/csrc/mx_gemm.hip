@@ -551,6 +551,13 @@ static hipError_t launch_sweep(const GemmArgs& a, uint32_t units, hipStream_t st
 {
     const dim3 grid(units < SW_GRID ? units : SW_GRID);
     const size_t lds = (size_t)MM * a.k * 2;  // X; at most 64 KB (m <= 2, k <= 16384)
+    // allow the full 64 KB of dynamic LDS next to the static partial sums
+    static const hipError_t attr_pre = hipFuncSetAttribute(
+        (const void*)gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
+    if (attr_pre != hipSuccess) return attr_pre;
+    if (attr != hipSuccess) return attr;
     if (!W8 && a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>), grid, dim3(256), lds, st, a, units);
     else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>), grid, dim3(256), lds, st, a, units);
     return hipGetLastError();
