@@ -16,8 +16,8 @@
 // from 16 code bytes), and the four MFMA k-steps take them in the same permuted order, which
 // leaves every dot product intact.  The MFMA's A operand is the weight fragment, so each
 // result tile is transposed (rows n, columns m); the epilogue stages it through LDS and
-// writes whole 16-byte chunks.  Workgroups are mapped so that the m-tiles sharing a weight
-// tile run on the same XCD.
+// writes whole 16-byte chunks.  Workgroups are mapped so that the tiles resident on one XCD
+// share a few activation and weight tiles through its L2.
 //
 // The same kernel serves FP8 (E4M3) weights in the same block structure (the W8A16 product
 // of the FP8 fallback): a weight row then brings 128 code bytes per stage, a stage is 64 KB
@@ -197,10 +197,19 @@ __global__ __launch_bounds__(THREADS) void gemm_a16_kernel(const GemmArgs a)
     const uint32_t K = (uint32_t)a.k, ldx = (uint32_t)a.ldx;
 
     // tile mapping: with the n-tile count a multiple of 8, XCD x (= block % 8) takes n-tiles
-    // x, x+8, ... and, for each, every m-tile in turn
+    // x, x+8, ...; with the m-tile count a multiple of 4 it runs them in groups of 4 m-tiles
+    // (all its n-tiles for m-tiles 0-3, then 4-7, ...), so that the ~32 workgroups resident on
+    // an XCD share 4 activation tiles (2 MB each at k 8192) and ~8 weight tiles through its L2
+    // (fetched from the fabric per 70B-FFN launch: 2.0 GB when each XCD ran all 16 m-tiles of
+    // two n-tiles at a time); else, for each n-tile, every m-tile in turn
     const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + BN - 1) / BN);
     uint32_t mt, nt;
-    if ((NT & 7) == 0) {
+    if ((NT & 7) == 0 && (MT & 3) == 0) {
+        const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3, NT8 = NT >> 3;
+        const uint32_t grp = local / (4 * NT8), r = local - grp * (4 * NT8);
+        mt = grp * 4 + (r & 3);
+        nt = (r >> 2) * 8 + x;
+    } else if ((NT & 7) == 0) {
         const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3;
         mt = local % MT;
         nt = (local / MT) * 8 + x;

@@ -97,10 +97,13 @@ def test_gemm_a16_ragged(fmt, block):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("mnk", [(200, 300, 1024), (17, 256, 512), (300, 520, 2048), (256, 512, 1536)])
+@pytest.mark.parametrize("mnk", [(200, 300, 1024), (17, 256, 512), (300, 520, 2048), (256, 512, 1536),
+                                 (500, 1948, 512), (1024, 2048, 512)])
 def test_gemm_a16_pipelined(fmt, mnk):
     """Block 32 and k a multiple of 512: the pipelined kernel (128 x 256 tiles, 3-stage LDS
-    ring, 512-k scale windows) -- ragged m and n, one to several scale windows."""
+    ring, 512-k scale windows) -- ragged m and n, one to several scale windows; the last two
+    shapes (m-tiles a multiple of 4, n-tiles of 8) take the XCD-grouped tile order, one and
+    two groups of m-tiles, the first with ragged m and n."""
     m, n, k = mnk
     x = synth.normal((m, k), "bf16", f"gp.x.{m}", 1.0)
     w = synth.normal((n, k), "bf16", f"gp.w.{n}", 0.02, 0.01, 20.0)
