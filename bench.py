@@ -3,6 +3,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
     python bench.py --pmc-run      # launches for rocprofv3 --pmc traffic counters (see below)
+    python bench.py --pmc-run rows # launches of the GEMV / GEMM rows for rocprofv3 --pmc
 
 One step = the whole block-size/scale sweep on the Llama-7B FFN-shaped weight
 (4096 x 11008 bf16 ~ N(0, sigma^2), 0.1% entries x20): for every sigma in {0.005, 0.02, 0.1},
@@ -24,6 +25,9 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 size (five times, the calibration for the HBM byte counters), for
 `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`; the resulting per-launch bytes are kept in
 profiles/traffic.json and reported as `roofline.traffic` while the kernel source is unchanged.
+`--pmc-run rows` launches the decode GEMV (m 1, n 14336), the 405B-FFN GEMV (m 1), the 70B-FFN
+prefill GEMM in W4A16 and W4A4 (tiled weight scales) three times each, and the same copy, for
+the HBM byte and matrix-core counters of those kernels.
 """
 from __future__ import annotations
 
@@ -68,8 +72,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the GEMV/GEMM rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--pmc-run", action="store_true",
-                    help="only the launches that the traffic counters are read on")
+    ap.add_argument("--pmc-run", nargs="?", const="quantize", choices=("quantize", "rows"),
+                    help="only the launches that the counters are read on: the dominant kernel "
+                         "(default) or the GEMV / GEMM rows")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
@@ -88,8 +93,11 @@ def main():
     L = mx.lib()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    if args.pmc_run:
+    if args.pmc_run == "quantize":
         pmc_run(mx, torch, np, synth, dev)
+        return
+    if args.pmc_run == "rows":
+        pmc_rows(mx, torch, np, synth, dev)
         return
 
     # ---------------------------------------------------------------- C2 sweep setup
@@ -459,6 +467,73 @@ def pmc_run(mx, torch, np, synth, dev):
     torch.cuda.synchronize()
     log(f"pmc run: 5 x quantize ({quant_bytes(C2_ROWS * C2_K, 32)} algorithmic bytes), "
         f"5 x copy ({COPY_BYTES} bytes read, {COPY_BYTES} written)")
+
+
+def pmc_rows(mx, torch, np, synth, dev):
+    """Three launches each of the decode GEMV (m 1, n 14336, k 4096, block 32 E8M0), the
+    405B-FFN GEMV (m 1, UE5M3 with a tensor scale), the 70B-FFN prefill GEMM in W4A16 and in
+    W4A4 with tiled weight scales (its activation pre-pass is a quantize launch of its own),
+    each after a 512 MB fill that evicts the Infinity Cache, then five copies of COPY_BYTES."""
+    bf = torch.bfloat16
+
+    def dev_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(bf).to(dev)
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def launch3(what, fn):
+        for _ in range(3):
+            flush.fill_(1)
+            fn()
+        torch.cuda.synchronize()
+        log(f"pmc rows: 3 x {what}")
+
+    w = dev_bf16(synth.c3_weight(14336))
+    c3, s3 = mx.mx_quantize(w, 32, "e8m0")
+    del w
+    x = dev_bf16(synth.c3_x(1))
+    y = torch.empty((1, 14336), dtype=bf, device=dev)
+    launch3(f"decode GEMV m 1 n 14336 k 4096 ({gemv_bytes(1, 14336, 4096, 32)} algorithmic bytes)",
+            lambda: mx.mx_gemm(x, c3, s3, 32, "e8m0", 1.0, "a16", y=y))
+    del c3, s3, x, y
+
+    wh = synth.c5_weight()
+    g = synth.c5_tensor_scale(wh)
+    w = dev_bf16(wh)
+    del wh
+    N, K = 53248, 16384
+    c5, s5 = mx.mx_quantize(w, 32, "ue5m3", g)
+    del w
+    torch.cuda.empty_cache()
+    x = dev_bf16(synth.c5_x(1))
+    y = torch.empty((1, N), dtype=bf, device=dev)
+    launch3(f"405B-FFN GEMV m 1 ({gemv_bytes(1, N, K, 32)} algorithmic bytes)",
+            lambda: mx.mx_gemm(x, c5, s5, 32, "ue5m3", g, "a16", y=y))
+    del c5, s5, x, y
+    torch.cuda.empty_cache()
+
+    w = dev_bf16(synth.c4_weight())
+    c4, s4 = mx.mx_quantize(w, 32, "e8m0")
+    _, s4t = mx.mx_quantize(w, 32, "e8m0", layout="tiled")
+    del w
+    x = dev_bf16(synth.c4_x())
+    M, N, K = 2048, 28672, 8192
+    y = torch.empty((M, N), dtype=bf, device=dev)
+    ws = torch.empty(mx.mx_gemm_workspace_size(M, N, K, 32, "a4"), dtype=torch.uint8, device=dev)
+    launch3(f"W4A16 GEMM {M} x {N} x {K} ({2 * M * N * K} flops)",
+            lambda: mx.mx_gemm(x, c4, s4, 32, "e8m0", 1.0, "a16", y=y))
+    launch3(f"W4A4 GEMM {M} x {N} x {K}, tiled weight scales ({2 * M * N * K} flops)",
+            lambda: mx.mx_gemm(x, c4, s4t, 32, "e8m0", 1.0, "a4", y=y, workspace=ws, layout="tiled"))
+    del c4, s4, s4t, x, y, ws
+    torch.cuda.empty_cache()
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        flush.fill_(1)
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"pmc rows: 5 x copy ({COPY_BYTES} bytes read, {COPY_BYTES} written)")
 
 
 def load_traffic(kernel: str):
