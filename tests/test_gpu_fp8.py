@@ -200,6 +200,25 @@ def test_gemv_fp8_sweep(n, k, fmt, m):
         assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 sweep m={m} {fmt} {n}x{k} {dt}")
 
 
+@pytest.mark.parametrize("fmt,g", [("e8m0", 1.0), ("e4m3", 1.0), ("ue5m3", 0.37)])
+def test_fp8_full_tensor_exact(fmt, g):
+    """FP8 fallback on the whole Llama-7B FFN weight (4096 x 11008 bf16, block 32): every code,
+    scale byte and dequantized bf16 element equal to the oracle's (g = 1 takes the 32-element
+    lane kernel, g != 1 the 8-element one)."""
+    g = float(np.float32(g))
+    w = synth.c2_weight(0.02)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize_fp8(wd, 32, fmt, g)
+    y = mx.mx_dequantize_fp8(cd, sd, 32, fmt, g, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    del wd
+    rc, rs = oracle.quantize_fp8(w, 32, fmt, g)
+    np.testing.assert_array_equal(to_host_bits(sd), rs, err_msg=f"scales {fmt}")
+    np.testing.assert_array_equal(to_host_bits(cd), rc, err_msg=f"codes {fmt}")
+    np.testing.assert_array_equal(to_host_bits(y), oracle.dequantize_fp8(rc, rs, 32, fmt, g, "bf16"),
+                                  err_msg=f"dequantized {fmt}")
+
+
 def test_gemm_fp8_prefill_shape_sampled():
     # 70B FFN prefill shape: m 2048, k 8192, n 28672, block 32, E8M0; sampled rows and columns
     w = synth.c4_weight()

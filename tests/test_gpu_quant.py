@@ -237,6 +237,28 @@ def test_c2_full_size_sampled(sigma):
     del wd
 
 
+C2_FULL_CASES = [(0.02, 32, "e8m0"), (0.02, 32, "e4m3"), (0.02, 32, "ue5m3"), (0.02, 4, "e4m3"),
+                 (0.02, 256, "ue5m3"), (0.005, 32, "e8m0"), (0.1, 32, "e8m0")]
+
+
+@pytest.mark.parametrize("sigma,block,fmt", C2_FULL_CASES)
+def test_c2_full_tensor_exact(sigma, block, fmt):
+    """The whole Llama-7B FFN weight (4096 x 11008 bf16, 45 M elements), in the launch the
+    benchmark times: every code byte, scale byte and dequantized bf16 element equal to the
+    oracle's -- the block-32 E8M0 quantize is the benchmark's dominant kernel."""
+    w = synth.c2_weight(sigma)
+    wd = bf16_dev(w)
+    c, s = mx.mx_quantize(wd, block, fmt)
+    y = mx.mx_dequantize(c, s, 11008, block, fmt, 1.0, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    del wd
+    rc, rs = oracle.quantize(w, block, fmt)
+    np.testing.assert_array_equal(to_host_bits(s), rs, err_msg=f"scales {fmt} B={block}")
+    np.testing.assert_array_equal(to_host_bits(c), rc, err_msg=f"codes {fmt} B={block}")
+    np.testing.assert_array_equal(to_host_bits(y), oracle.dequantize(rc, rs, 11008, block, fmt, 1.0, "bf16"),
+                                  err_msg=f"dequantized {fmt} B={block}")
+
+
 def test_c5_full_size_two_level_sampled():
     """405B FFN weight 53248 x 16384 bf16, UE5M3 block 32 times a per-tensor scale
     g = fl32(max|W| / (6 * 114688)); sampled rows bit-exact, including the narrow bands."""
