@@ -78,7 +78,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
-              "build has no multi-GPU path (see the sharding note in DESIGN.md).", file=sys.stderr)
+              "library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -109,15 +109,15 @@ def main():
         inputs.append(wd)
         inputs.append(wd.clone())  # two copies per sigma: six 90 MB inputs in rotation
     n = C2_ROWS * C2_K
-    configs = [(si, b, f) for b in BLOCKS for f in FMTS for si in range(len(SIGMAS))]
-    codes = [torch.empty((C2_ROWS, C2_K // 2), dtype=torch.uint8, device=dev) for _ in configs]
-    scales = [torch.empty((C2_ROWS, C2_K // b), dtype=torch.uint8, device=dev) for (_, b, _) in configs]
+    sweep_cfgs = [(si, b, f) for b in BLOCKS for f in FMTS for si in range(len(SIGMAS))]
+    codes = [torch.empty((C2_ROWS, C2_K // 2), dtype=torch.uint8, device=dev) for _ in sweep_cfgs]
+    scales = [torch.empty((C2_ROWS, C2_K // b), dtype=torch.uint8, device=dev) for (_, b, _) in sweep_cfgs]
     deq_out = [torch.empty((C2_ROWS, C2_K), dtype=torch.bfloat16, device=dev) for _ in range(6)]
-    log(f"C2 setup {time.time() - t0:.1f}s: {len(configs)} configs")
+    log(f"C2 setup {time.time() - t0:.1f}s: {len(sweep_cfgs)} configurations")
 
     qcalls, dcalls = [], []
     step_bytes = 0
-    for i, (si, b, f) in enumerate(configs):
+    for i, (si, b, f) in enumerate(sweep_cfgs):
         x = inputs[2 * si + (i // len(SIGMAS)) % 2]
         qcalls.append((x.data_ptr(), 1, C2_ROWS, C2_K, C2_K, b, mx.FMT[f], 1.0, 0,
                        codes[i].data_ptr(), scales[i].data_ptr(), sp))
@@ -126,7 +126,7 @@ def main():
         step_bytes += 2 * quant_bytes(n, b)
     # the dominant kernel's three launches (one per sigma) are consecutive in the step; one
     # event pair around them gives its average launch duration inside the timed region
-    dom = [i for i, c in enumerate(configs) if c[1] == 32 and c[2] == "e8m0"]
+    dom = [i for i, c in enumerate(sweep_cfgs) if c[1] == 32 and c[2] == "e8m0"]
     assert dom == list(range(dom[0], dom[0] + len(SIGMAS)))
     q, dq = L.mx_quantize, L.mx_dequantize
 
@@ -182,7 +182,7 @@ def main():
         for i, a, b_ in evs:
             acc.setdefault(i, []).append(a.elapsed_time(b_))
         for i, ts in acc.items():
-            si, b, f = configs[i]
+            si, b, f = sweep_cfgs[i]
             key = f"{kind}.B{b}.{f}"
             per_cfg.setdefault(key, []).append(min(ts))
     per_config = {}
@@ -204,7 +204,7 @@ def main():
                 "traffic": traffic, "bytes_per_launch": dom_bytes,
                 "avg_launch_us": round(dom_avg_ms * 1e3, 3)}
 
-    error_split = measure_error_split(mx, L, torch, inputs, configs, dev, stream)
+    error_split = measure_error_split(mx, L, torch, inputs, sweep_cfgs, dev, stream)
     block_policy = measure_block_policy(mx, torch, inputs, error_split, dev, stream)
 
     # free the sweep buffers before the GEMM rows
@@ -236,7 +236,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
+def measure_error_split(mx, L, torch, inputs, sweep_cfgs, dev, stream):
     """The sweep's error split computed on the device (mx_quant_error: quantize, dequantize and
     the fp64 MSE_elem / MSE_max / MSE_zero sums in one pass over the weight): per-config
     kernel time (median of 3, one event pair per launch), the whole 63-config sweep, and the
@@ -245,9 +245,9 @@ def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
     sp = stream.cuda_stream
     need = max(mx.mx_quant_error_workspace_size(C2_ROWS, C2_K, b) for b in BLOCKS)
     work = torch.empty(need, dtype=torch.uint8, device=dev)
-    outs = torch.zeros((len(configs), 8), dtype=torch.float64, device=dev)
+    outs = torch.zeros((len(sweep_cfgs), 8), dtype=torch.float64, device=dev)
     calls = []
-    for i, (si, b, f) in enumerate(configs):
+    for i, (si, b, f) in enumerate(sweep_cfgs):
         x = inputs[2 * si + (i // len(SIGMAS)) % 2]
         calls.append((x.data_ptr(), 1, C2_ROWS, C2_K, C2_K, b, mx.FMT[f], 1.0, None, 0,
                        outs[i].data_ptr(), work.data_ptr(), need, sp))
@@ -274,7 +274,7 @@ def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
             e1.record(stream)
             evs.append((i, e0, e1))
     # fake quantization: the error split plus x^ written (sigma 0.02, block 32, E4M3)
-    fi = configs.index((1, 32, "e4m3"))
+    fi = sweep_cfgs.index((1, 32, "e4m3"))
     xh = torch.empty((C2_ROWS, C2_K), dtype=torch.bfloat16, device=dev)
     fq = list(calls[fi])
     fq[8], fq[9] = xh.data_ptr(), C2_K
@@ -294,7 +294,7 @@ def measure_error_split(mx, L, torch, inputs, configs, dev, stream):
     vals = outs.cpu().numpy()
     per = {}
     for i, ts in acc.items():
-        si, b, f = configs[i]
+        si, b, f = sweep_cfgs[i]
         t = sorted(ts)[1]
         gbs = 2 * n / (t * 1e-3) / 1e9
         per[f"s{SIGMAS[si]}.B{b}.{f}"] = {
