@@ -219,6 +219,30 @@ def test_fp8_full_tensor_exact(fmt, g):
                                   err_msg=f"dequantized {fmt}")
 
 
+@pytest.mark.parametrize("fmt,g", [("e8m0", 1.0), ("ue5m3", 0.37)])
+def test_gemm_fp8_wide_tiles_sampled(fmt, g):
+    """W8A16 through the wide-tile kernel (m 1000 and n 28600, both ragged): sampled rows and
+    columns against the oracle, fp32 and bf16 out."""
+    g = float(np.float32(g))
+    m, n, k = 1000, 28600, 1024
+    x = synth.normal((m, k), "bf16", "gw8.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gw8.w", 0.02 / g, 0.01, 20.0)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize_fp8(wd, 32, fmt, g)
+    del wd
+    cols = np.array([0, 1, 255, 256, 9999, 28415, 28416, 28599])
+    rows = np.array([0, 1, 127, 128, 255, 256, 767, 768, 999])
+    rc, rs = oracle.quantize_fp8(w[cols], 32, fmt, g)
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
+    yref, aref = oracle.gemm_fp8(x[rows], rc, rs, 32, fmt, g)
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, fmt, g, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y[rows][:, cols].float()), yref, aref, dt == torch.bfloat16,
+                          f"w8 wide tiles {fmt} {dt}")
+
+
 def test_gemm_fp8_prefill_shape_sampled():
     # 70B FFN prefill shape: m 2048, k 8192, n 28672, block 32, E8M0; sampled rows and columns
     w = synth.c4_weight()

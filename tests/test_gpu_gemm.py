@@ -266,6 +266,32 @@ def _c4_setup():
     return cd, sd, rc, rs, rows, cols
 
 
+# The wide-tile W4A16 kernel (256 x 256 tiles, 128 x 64 per wave): always for E4M3 / UE5M3
+# scales with m > 128 (the pipelined tests above cover it at small shapes); for E8M0 only where
+# its tiles fill whole rounds of the GPU -- here m 1000 (4 tiles, the last ragged), n 28600
+# (112 tiles, the last ragged), which the small shapes never reach.  Sampled rows and columns.
+@pytest.mark.parametrize("fmt,g", [("e8m0", 1.0), ("ue5m3", 0.37), ("e4m3", 1.0)])
+def test_gemm_a16_wide_tiles_sampled(fmt, g):
+    g = float(np.float32(g))
+    m, n, k = 1000, 28600, 1024
+    x = synth.normal((m, k), "bf16", "gw.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gw.w", 0.02, 0.01, 20.0)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize(wd, 32, fmt, g)
+    del wd
+    cols = np.array([0, 1, 255, 256, 9999, 28415, 28416, 28599])
+    rows = np.array([0, 1, 127, 128, 255, 256, 767, 768, 999])
+    rc, rs = oracle.quantize(w[cols], 32, fmt, g)
+    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
+    np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, fmt, g, "a16", out_dtype=dt)
+        torch.cuda.synchronize()
+        yref, aref = oracle.gemm(x[rows], rc, rs, 32, fmt, g, "a16")
+        assert_gemm_close(to_host_bits(y[rows][:, cols].float()), yref, aref, dt == torch.bfloat16,
+                          f"wide tiles {fmt} {dt}")
+
+
 @pytest.mark.parametrize("mode", ["a16", "a4"])
 def test_c4_prefill(mode):
     """70B FFN prefill M=2048, K=8192, N=28672, block 32 E8M0: W4A16 and W4A4."""
