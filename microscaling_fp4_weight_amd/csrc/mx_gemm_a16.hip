@@ -366,7 +366,7 @@ bool a16_uses_tiled(const GemmArgs& a)
 hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st)
 {
     if (!a16_uses_tiled(a)) return hipErrorInvalidValue;
-    if (a16w_uses(a)) return launch_gemm_a16w(a, false, st);  // E4M3 / UE5M3 scales: wider wave tiles
+    if (a16w_uses(a, false)) return launch_gemm_a16w(a, false, st);  // wider wave tiles
 #define MXF(F) if (a.fmt == F) return a.y_bf16 ? a16::launch_tiled<F, true, false>(a, st) : a16::launch_tiled<F, false, false>(a, st);
     MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
 #undef MXF
@@ -376,7 +376,7 @@ hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st)
 hipError_t launch_gemm_w8_tiled(const GemmArgs& a, hipStream_t st)
 {
     if (!a16_uses_tiled(a)) return hipErrorInvalidValue;
-    if (a16w_uses(a)) return launch_gemm_a16w(a, true, st);
+    if (a16w_uses(a, true)) return launch_gemm_a16w(a, true, st);
 #define MXF(F) if (a.fmt == F) return a.y_bf16 ? a16::launch_tiled<F, true, true>(a, st) : a16::launch_tiled<F, false, true>(a, st);
     MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
 #undef MXF

@@ -161,13 +161,14 @@ def _gemm_fp8_case(m, n, k, fmt, g, tag, ldx=None, ldy=None):
             assert torch.isnan(y.as_strided((m, ldy - n), (ldy, 1), n)).all()
 
 
-# Larger products run on the pipelined matrix-core kernel (tiles of 128 x 256, k in stages of
-# 128, scale windows of 512); the library picks it when its estimated time is below the 16-row
-# kernel's, which these shapes pass by a factor of 1.1 or more with every scale format.  Every
-# output is compared: several tiles with ragged tails in m and n (down to a single row and
-# column), n-tile counts that are and are not multiples of 8 (two mappings of tiles to XCDs).
+# Larger products run on the pipelined matrix-core kernels (scale windows of 512 k): for m > 128
+# the wide one (256 x 256 tiles, k in stages of 64), else the one with 128 x 256 tiles and
+# 128-k stages (the last shape); the library picks them when the estimated time is below the
+# 16-row kernel's, which these shapes pass by a factor of 1.1 or more with every scale format.
+# Every output is compared: several tiles with ragged tails in m and n (down to a single row
+# and column), n-tile counts that are and are not multiples of 8 (two mappings of tiles to XCDs).
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("mnk", [(300, 6000, 1536), (129, 7937, 512), (200, 5000, 512)])
+@pytest.mark.parametrize("mnk", [(300, 6000, 1536), (129, 7937, 512), (200, 5000, 512), (128, 8000, 1536)])
 def test_gemm_fp8_tiled(mnk, fmt):
     m, n, k = mnk
     _gemm_fp8_case(m, n, k, fmt, 1.0, f"{m}.{n}.{k}")
