@@ -364,14 +364,28 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
 #pragma unroll
         for (int r = 0; r < DOT_ROWS; ++r) {
             uint32_t bw[16];
-            dequant32<BLOCK, FMT>(cw[r], sb[r], bw);
+            if constexpr (BLOCK >= 32 && FMT != FMT_E8M0) {
+                // one scale for the lane's 32 k: its mantissa multiplies their fp32 sum once
+                const float mant = dequant32_pow2<FMT>(cw[r], (uint32_t)sb[r] & 0xFFu, bw);
 #pragma unroll
-            for (int m = 0; m < MM; ++m)
+                for (int m = 0; m < MM; ++m) {
+                    float t = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    acc[r][m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xf[m][i]),
-                                                                __builtin_bit_cast(bf16x2, bw[i]),
-                                                                acc[r][m], false);
+                    for (int i = 0; i < 16; ++i)
+                        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xf[m][i]),
+                                                            __builtin_bit_cast(bf16x2, bw[i]), t, false);
+                    acc[r][m] = __builtin_fmaf(t, mant, acc[r][m]);
+                }
+            } else {
+                dequant32<BLOCK, FMT>(cw[r], sb[r], bw);
+#pragma unroll
+                for (int m = 0; m < MM; ++m)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc[r][m] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xf[m][i]),
+                                                                    __builtin_bit_cast(bf16x2, bw[i]),
+                                                                    acc[r][m], false);
+            }
         }
     }
     // reduce over the 64 lanes, then over the waves
@@ -497,6 +511,19 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
                 const uint32_t c8[8] = {cw[h][0].x, cw[h][0].y, cw[h][0].z, cw[h][0].w,
                                         cw[h][1].x, cw[h][1].y, cw[h][1].z, cw[h][1].w};
                 dequant_w8<16, FMT>(c8, sb[h], bw);  // elements 0..15: first byte, 16..31: second
+            } else if constexpr (FMT != FMT_E8M0) {
+                // one scale for the lane's 32 k: its mantissa multiplies their fp32 sum once
+                const float mant = dequant32_pow2<FMT>(cw[h][0], sb[h] & 0xFFu, bw);
+#pragma unroll
+                for (int m = 0; m < MM; ++m) {
+                    float u = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        u = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq[m][h][t]),
+                                                            __builtin_bit_cast(bf16x2, bw[t]), u, false);
+                    acc[m] = __builtin_fmaf(u, mant, acc[m]);
+                }
+                continue;
             } else {
                 dequant32<32, FMT>(cw[h][0], sb[h], bw);
             }

@@ -70,6 +70,24 @@ __device__ __forceinline__ void dequant32(const u32x4 cw, uint64_t sbytes, uint3
     }
 }
 
+// The same 32 codes as e * 2^p (p = the scale's power of two; exact in bf16), returning the
+// rest of the scale (its mantissa; 1 for E8M0).  A dot product over one scale block can then
+// take the mantissa once, on the block's fp32 sum, instead of once per element: one
+// conversion per pair instead of a conversion, two multiplies and a pack.
+template <int FMT>
+__device__ __forceinline__ float dequant32_pow2(const u32x4 cw, uint32_t byte, uint32_t (&d)[16])
+{
+    const WScale<FMT> s = wscale<FMT>(byte);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        d[4 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[w], s.pow2, 0));
+        d[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[w], s.pow2, 1));
+        d[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[w], s.pow2, 2));
+        d[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[w], s.pow2, 3));
+    }
+    return s.mant;
+}
+
 // ---------------------------------------------------------------------------------------
 // FP8 weight fragment: 32 E4M3 codes (8 dwords, 32 consecutive k of one row) with their scale
 // bytes -> 32 bf16 (16 dwords), e * s exact: an E4M3 value has at most 4 significant bits and
