@@ -443,35 +443,6 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
     const uint32_t c0 = (2 * (uint32_t)wave) & (KC - 1);  // the wave's first chunk of k
     const uint32_t rowb = W8 ? K : K / 2;                   // code bytes per row
 
-    // X of the wave's chunk pair in the order of the lane's 32 k (piece j = 8 k).  The m rows
-    // of X are staged once per workgroup through LDS (m k / 8 pieces of 16 bytes, m k 2 bytes
-    // of dynamic LDS): each wave needs all of it when k / 2048 is 2, and fetching it once per
-    // workgroup instead of once per wave cuts its L2 traffic fourfold (measured: n 4096, k 4096,
-    // m 1: 5.4 -> 4.6 us).
-    extern __shared__ u32x4 xs[];
-    uint32_t xq[MM][2][16];
-    {
-        const rsrc_t xr = make_rsrc(a.x, (uint32_t)(((int64_t)(MM - 1) * a.ldx + a.k) * 2));
-        for (uint32_t t = threadIdx.x; t < MM * (K / 8); t += 256) {
-            const uint32_t m = t / (K / 8), p = t - m * (K / 8);
-            xs[t] = bload128(xr, (uint32_t)(m * a.ldx * 2) + p * 16);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < MM; ++m)
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t kx = W8 ? (c0 + h) * 2048 + (j >> 1) * 1024 + 16 * lane + 8 * (j & 1)
-                                           : (c0 + h) * 2048 + 32 * lane + 8 * j;
-                    const u32x4 v = xs[m * (K / 8) + kx / 8];
-                    xq[m][h][4 * j] = v.x;
-                    xq[m][h][4 * j + 1] = v.y;
-                    xq[m][h][4 * j + 2] = v.z;
-                    xq[m][h][4 * j + 3] = v.w;
-                }
-    }
     const rsrc_t wr = make_rsrc(a.wc, (uint32_t)(a.n * rowb));
     const rsrc_t sr = PRE ? make_rsrc(a.ws, (uint32_t)(((a.n + 7) / 8) * KC * 512))
                           : make_rsrc(a.ws, (uint32_t)(a.n * (a.k / 32)));
@@ -498,7 +469,47 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
     };
     u32x4 cw[2][NH], cn[2][NH];
     uint32_t sb[2], sn[2];
-    load(0, cw, sb);
+    // X of the wave's chunk pair in the order of the lane's 32 k (piece j = 8 k).  The m rows
+    // of X are staged once per workgroup through LDS (m k / 8 pieces of 16 bytes, m k 2 bytes
+    // of dynamic LDS): each wave needs all of it when k / 2048 is 2, and fetching it once per
+    // workgroup instead of once per wave cuts its L2 traffic fourfold (measured: n 4096, k 4096,
+    // m 1: 5.4 -> 4.6 us).
+    extern __shared__ u32x4 xs[];
+    uint32_t xq[MM][2][16];
+    {
+        // X by LDS-DMA (lane i of a load writes 16 bytes at the wave's base + 16 i; the piece
+        // count, m k / 8, is a multiple of 512), then step 0's codes and scales, so that the
+        // weights' HBM latency overlaps the staging; wait for this wave's X loads only (the
+        // NLOAD weight loads issued after them may stay in flight), then the barrier.
+        typedef __attribute__((address_space(3))) void lds_void;
+        const rsrc_t xr = make_rsrc(a.x, (uint32_t)(((int64_t)(MM - 1) * a.ldx + a.k) * 2));
+        const uint32_t npieces = MM * (K / 8);
+        for (uint32_t t0 = (uint32_t)wave * 64; t0 < npieces; t0 += 256) {
+            const uint32_t t = t0 + lane, m = t / (K / 8), p = t - m * (K / 8);
+            const uint32_t off = t < npieces ? (uint32_t)(m * a.ldx * 2) + p * 16 : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(xs + t0), 16, off, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load(0, cw, sb);
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int NLOAD = 2 * (NH + (W8 ? 2 : 1));  // vector-memory instructions of load()
+        __builtin_amdgcn_s_waitcnt((NLOAD & 0xF) | ((NLOAD >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < MM; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t kx = W8 ? (c0 + h) * 2048 + (j >> 1) * 1024 + 16 * lane + 8 * (j & 1)
+                                           : (c0 + h) * 2048 + 32 * lane + 8 * j;
+                    const u32x4 v = xs[m * (K / 8) + kx / 8];
+                    xq[m][h][4 * j] = v.x;
+                    xq[m][h][4 * j + 1] = v.y;
+                    xq[m][h][4 * j + 2] = v.z;
+                    xq[m][h][4 * j + 3] = v.w;
+                }
+    }
     for (uint32_t i = 0; i < nsteps; ++i) {
         load(i + 1, cn, sn);
         float acc[MM];
