@@ -247,10 +247,10 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act
  *  w_codes    : weight codes, n x k/2 bytes; w_scales: mx_scale_bytes(n, k, block, layout)
  *               bytes (mx_quantize output for an n x k weight).
  *  block, fmt, tensor_scale, layout: those of the weight.  MX_LAYOUT_TILED weights are
- *               accepted in MX_A4 mode with k % 128 == 0 (MX_ERR_UNSUPPORTED otherwise);
- *               MX_LAYOUT_PRESHUFFLED weights in MX_A16 mode with m == 1 and ld_x a
- *               multiple of 8 (MX_ERR_UNSUPPORTED otherwise);
- *               they make the W4A4 product faster.
+ *               accepted in MX_A4 mode with k % 128 == 0 (MX_ERR_UNSUPPORTED otherwise)
+ *               and make the W4A4 product faster; MX_LAYOUT_PRESHUFFLED weights in
+ *               MX_A16 mode with m == 1 and ld_x a multiple of 8 (MX_ERR_UNSUPPORTED
+ *               otherwise), with results bit-identical to the row-major order.
  *  mode       : MX_A16 -- X is used as given (bf16 x dequantized weight);
  *               MX_A4  -- X is first MX-quantized along k with block 32, E8M0 scales and
  *               g = 1 (bit-identical to mx_quantize with those arguments) into `workspace`,
