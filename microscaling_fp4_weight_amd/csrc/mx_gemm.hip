@@ -518,7 +518,33 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint32_t bw[16];
-            if constexpr (W8) {
+            if constexpr (W8 && FMT != FMT_E8M0) {
+                // two 16-element blocks (pairs 0-7: first scale byte, 8-15: second): each pair
+                // as e * 2^p in bf16 (exact), each block's mantissa once on its fp32 sum
+                const uint32_t c8[8] = {cw[h][0].x, cw[h][0].y, cw[h][0].z, cw[h][0].w,
+                                        cw[h][1].x, cw[h][1].y, cw[h][1].z, cw[h][1].w};
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const DecG1 p = dec_params_g1<FMT>((sb[h] >> (8 * q)) & 0xFFu);
+#pragma unroll
+                    for (int hh = 0; hh < 8; ++hh) {
+                        const int pr = 8 * q + hh;
+                        const bf16x2 v = (pr & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[pr >> 1], p.pow2, true)
+                                                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c8[pr >> 1], p.pow2, false);
+                        bw[pr] = __builtin_bit_cast(uint32_t, v);
+                    }
+#pragma unroll
+                    for (int m = 0; m < MM; ++m) {
+                        float u = 0.0f;
+#pragma unroll
+                        for (int hh = 0; hh < 8; ++hh)
+                            u = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq[m][h][8 * q + hh]),
+                                                                __builtin_bit_cast(bf16x2, bw[8 * q + hh]), u, false);
+                        acc[m] = __builtin_fmaf(u, p.mant, acc[m]);
+                    }
+                }
+                continue;
+            } else if constexpr (W8) {
                 const uint32_t c8[8] = {cw[h][0].x, cw[h][0].y, cw[h][0].z, cw[h][0].w,
                                         cw[h][1].x, cw[h][1].y, cw[h][1].z, cw[h][1].w};
                 dequant_w8<16, FMT>(c8, sb[h], bw);  // elements 0..15: first byte, 16..31: second
