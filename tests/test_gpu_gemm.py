@@ -112,6 +112,28 @@ def test_gemm_a16_pipelined(fmt, mnk):
         check(x, c, s, cd, sd, 32, fmt, 1.0, "a16", out)
 
 
+@pytest.mark.parametrize("fmt", ["e8m0", "ue5m3"])
+@pytest.mark.parametrize("ldy", [600, 523])
+def test_gemm_a16_strided_output(fmt, ldy):
+    """Output rows with a stride beyond n, 16-byte aligned (chunk epilogue) or odd (element
+    epilogue), through the 128 x 256 kernel (E8M0 here) and the wide-tile one (UE5M3); the
+    columns past n must stay untouched."""
+    g = float(np.float32(0.37)) if fmt != "e8m0" else 1.0
+    m, n, k = 300, 520, 1024
+    x = synth.normal((m, k), "bf16", "gst.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gst.w", 0.02, 0.01, 20.0)
+    c, s = oracle.quantize(w, 32, fmt, g)
+    cd, sd = torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV)
+    yref, aref = oracle.gemm(x, c, s, 32, fmt, g, "a16")
+    for dt in (torch.float32, torch.bfloat16):
+        big = torch.full((m, ldy), float("nan"), dtype=dt, device=DEV)
+        y = big[:, :n]
+        mx.mx_gemm(bf16_dev(x), cd, sd, 32, fmt, g, "a16", y=y)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"strided y {fmt} {ldy} {dt}")
+        assert torch.isnan(big[:, n:].float()).all()
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_gemm_a16_pipelined_tensor_scale_and_stride(fmt):
     """Two-level scaling (g != 1) and an activation row stride larger than k."""
