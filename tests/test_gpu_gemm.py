@@ -205,6 +205,27 @@ def test_gemm_a4(mnk):
         check(x, c, s, cd, sd, 32, "e8m0", 1.0, "a4", out)
 
 
+@pytest.mark.parametrize("layout", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("ldy", [600, 523])
+def test_gemm_a4_strided_output(layout, ldy):
+    """W4A4 into output rows with a stride beyond n (16-byte aligned: chunk epilogue; odd:
+    element epilogue), row-major and tiled weight scales; the columns past n stay untouched."""
+    m, n, k = 300, 520, 1024
+    x = synth.normal((m, k), "bf16", "gsa.x", 1.0)
+    w = synth.normal((n, k), "bf16", "gsa.w", 0.015, 0.001, 20.0)
+    c, s = oracle.quantize(w, 32, "e8m0")
+    cd, sd = mx.mx_quantize(bf16_dev(w), 32, "e8m0", layout=layout)
+    np.testing.assert_array_equal(to_host_bits(cd), c)
+    yref, aref = oracle.gemm(x, c, s, 32, "e8m0", 1.0, "a4")
+    for dt in (torch.float32, torch.bfloat16):
+        big = torch.full((m, ldy), float("nan"), dtype=dt, device=DEV)
+        y = big[:, :n]
+        mx.mx_gemm(bf16_dev(x), cd, sd, 32, "e8m0", 1.0, "a4", y=y, layout=layout)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"a4 strided y {layout} {ldy} {dt}")
+        assert torch.isnan(big[:, n:].float()).all()
+
+
 @pytest.mark.parametrize("k", [512, 4224, 160])
 def test_gemm_a4_prepass_matches_quantize(k):
     """The activations quantized inside mx_gemm (workspace) are byte-identical to
