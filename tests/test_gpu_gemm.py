@@ -85,6 +85,28 @@ def test_gemv_sweep(fmt, n, k, m):
         np.testing.assert_array_equal(to_host_bits(yp), to_host_bits(yr[out]))
 
 
+# Zero-scale blocks through the GEMVs (an E4M3 / UE5M3 scale's mantissa multiplies each block's
+# sum there, so a zero scale must give a zero block): all-zero blocks and blocks small enough
+# to flush (a <= 3 s_min: 1e-4 under E4M3, 1e-6 under UE5M3), on the sweeping kernel (k 4096)
+# and the row kernel (k 768), one and two rows of X.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(96, 4096), (100, 768)])
+@pytest.mark.parametrize("m", [1, 2])
+def test_gemv_zero_and_flushed_blocks(fmt, n, k, m):
+    g = float(np.float32(0.37)) if fmt != "e8m0" else 1.0
+    x = synth.normal((m, k), "bf16", f"gz.x.{m}.{k}", 1.0)
+    w32 = synth.normal((n, k), "f32", f"gz.w.{n}.{k}", 0.02)
+    blocks = w32.reshape(n, k // 32, 32)
+    blocks[::3, ::5] = 0.0                                   # all-zero blocks
+    tiny = 1e-4 if fmt == "e4m3" else 1e-6
+    blocks[1::3, 1::4] *= tiny / 0.02 / 4                     # flushing blocks (|x| < tiny)
+    w = torch.from_numpy(blocks.reshape(n, k)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    c, s, cd, sd = quantize_ref(w, 32, fmt, g)
+    assert (s == 0).any()
+    for out in ("f32", "bf16"):
+        check(x, c, s, cd, sd, 32, fmt, g, "a16", out, what=f"zero blocks m={m} {fmt} {n}x{k} {out}")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("block", [4, 16, 32, 128])
 def test_gemm_a16_ragged(fmt, block):
