@@ -88,10 +88,11 @@ def test_gemv_sweep(fmt, n, k, m):
 # Zero-scale blocks through the GEMVs (an E4M3 / UE5M3 scale's mantissa multiplies each block's
 # sum there, so a zero scale must give a zero block): all-zero blocks and blocks small enough
 # to flush (a <= 3 s_min: 1e-4 under E4M3, 1e-6 under UE5M3), on the sweeping kernel (k 4096)
-# and the row kernel (k 768), one and two rows of X.
+# and the row kernel (k 768), one and two rows of X; m 300 takes the tile kernels (k 4096: the
+# wide-tile one for E4M3 / UE5M3, the 128 x 256 one for E8M0; k 768: the unpipelined one).
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(96, 4096), (100, 768)])
-@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("m", [1, 2, 300])
 def test_gemv_zero_and_flushed_blocks(fmt, n, k, m):
     g = float(np.float32(0.37)) if fmt != "e8m0" else 1.0
     x = synth.normal((m, k), "bf16", f"gz.x.{m}.{k}", 1.0)
