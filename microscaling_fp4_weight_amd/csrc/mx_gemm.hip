@@ -519,8 +519,9 @@ __global__ __launch_bounds__(256) void gemv_sweep_kernel(const GemmArgs a, uint3
         for (int h = 0; h < 2; ++h) {
             uint32_t bw[16];
             if constexpr (W8 && FMT != FMT_E8M0) {
-                // two 16-element blocks (pairs 0-7: first scale byte, 8-15: second): each pair
-                // as e * 2^p in bf16 (exact), each block's mantissa once on its fp32 sum
+                // the lane's two 16-element pieces, each inside its own 32-element block (pairs
+                // 0-7: first scale byte, 8-15: second): each pair as e * 2^p in bf16 (exact),
+                // each piece's scale mantissa once on its fp32 sum
                 const uint32_t c8[8] = {cw[h][0].x, cw[h][0].y, cw[h][0].z, cw[h][0].w,
                                         cw[h][1].x, cw[h][1].y, cw[h][1].z, cw[h][1].w};
 #pragma unroll

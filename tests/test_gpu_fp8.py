@@ -201,6 +201,33 @@ def test_gemv_fp8_sweep(n, k, fmt, m):
         assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 sweep m={m} {fmt} {n}x{k} {dt}")
 
 
+# Zero-scale blocks through the sweeping FP8-weight GEMV (with E4M3 / UE5M3 scales the mantissa
+# of each lane's 16 elements, which lie in one 32-element block, multiplies their sum, so a
+# zero scale must give a zero contribution):
+# all-zero blocks and blocks below the FP8 flush threshold (a <= 448 s_min / 2 g-scaled:
+# E4M3 0.44 g, UE5M3 1.7e-3 g), one and two rows of X.
+@pytest.mark.parametrize("fmt,g", [("e8m0", 1.0), ("e4m3", 1.0), ("ue5m3", 0.37)])
+@pytest.mark.parametrize("m", [1, 2])
+def test_gemv_fp8_zero_and_flushed_blocks(fmt, g, m):
+    g = float(np.float32(g))
+    n, k = 96, 4096
+    x = synth.normal((m, k), "bf16", f"gz8.x.{m}", 1.0)
+    w32 = synth.normal((n, k), "f32", "gz8.w", 1.0)        # blocks well above every threshold
+    blocks = w32.reshape(n, k // 32, 32)                  # the scale blocks
+    blocks[::3, ::5] = 0.0
+    tiny = {"e8m0": 0.0, "e4m3": 0.2, "ue5m3": 5e-4}[fmt]
+    blocks[1::3, 1::4] *= tiny / 4
+    w = torch.from_numpy(blocks.reshape(n, k)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rc, rs = oracle.quantize_fp8(w, 32, fmt, g)
+    assert (rs == 0).any()
+    cd, sd = torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV)
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 32, fmt, g)
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, fmt, g, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 zero blocks {fmt} m={m} {dt}")
+
+
 @pytest.mark.parametrize("fmt,g", [("e8m0", 1.0), ("e4m3", 1.0), ("ue5m3", 0.37)])
 def test_fp8_full_tensor_exact(fmt, g):
     """FP8 fallback on the whole Llama-7B FFN weight (4096 x 11008 bf16, block 32): every code,
