@@ -344,15 +344,24 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
         const uint32_t kk = (uint32_t)c * DOT_CHUNK + 32 * lane;
         const bool ok = kk < K;
         u32x4 cw[DOT_ROWS];
-        uint64_t sb[DOT_ROWS];
-        uint64_t sv = 0;
-        if constexpr (PRE) sv = bload64(sr, ok ? (uint32_t)c * 512 + 8 * lane : kOOB);
+        uint64_t sb[PRE ? 1 : DOT_ROWS];
+        // preshuffled: the 8 rows' scale bytes as two dwords, each row's byte taken where it
+        // is used (64-bit per-row copies made the compiler serialize the chunk's loads)
+        uint32_t sv_lo = 0, sv_hi = 0;
+        if constexpr (PRE) {
+            const uint64_t sv = bload64(sr, ok ? (uint32_t)c * 512 + 8 * lane : kOOB);
+            sv_lo = (uint32_t)sv;
+            sv_hi = (uint32_t)(sv >> 32);
+        }
 #pragma unroll
         for (int r = 0; r < DOT_ROWS; ++r) {
             cw[r] = bload128(wr, ok ? r * (K / 2) + kk / 2 : kOOB);
-            if constexpr (PRE) sb[r] = (sv >> (8 * r)) & 0xFFu;
-            else sb[r] = bload_lane_scales<BLOCK>(sr, ok ? r * (K / BLOCK) + kk / BLOCK : kOOB);
+            if constexpr (!PRE) sb[r] = bload_lane_scales<BLOCK>(sr, ok ? r * (K / BLOCK) + kk / BLOCK : kOOB);
         }
+        auto sbyte = [&](int r) -> uint32_t {
+            if constexpr (PRE) return ((r < 4 ? sv_lo : sv_hi) >> (8 * (r & 3))) & 0xFFu;
+            else return (uint32_t)sb[r] & 0xFFu;
+        };
         uint32_t xf[MM][16];
 #pragma unroll
         for (int m = 0; m < MM; ++m)
@@ -361,12 +370,15 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
                 const u32x4 v = bload128(xr, ok && m < a.m ? (uint32_t)(m * a.ldx * 2) + (kk + 8 * j) * 2 : kOOB);
                 xf[m][4 * j] = v.x; xf[m][4 * j + 1] = v.y; xf[m][4 * j + 2] = v.z; xf[m][4 * j + 3] = v.w;
             }
+        // all of the chunk's loads are issued before any of its arithmetic (otherwise the
+        // scheduler may start on the first rows and issue the activation loads one at a time)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < DOT_ROWS; ++r) {
             uint32_t bw[16];
             if constexpr (BLOCK >= 32 && FMT != FMT_E8M0) {
                 // one scale for the lane's 32 k: its mantissa multiplies their fp32 sum once
-                const float mant = dequant32_pow2<FMT>(cw[r], (uint32_t)sb[r] & 0xFFu, bw);
+                const float mant = dequant32_pow2<FMT>(cw[r], sbyte(r), bw);
 #pragma unroll
                 for (int m = 0; m < MM; ++m) {
                     float t = 0.0f;
@@ -377,7 +389,8 @@ __global__ __launch_bounds__(64 * DOT_WAVES) void gemv_dot_kernel(const GemmArgs
                     acc[r][m] = __builtin_fmaf(t, mant, acc[r][m]);
                 }
             } else {
-                dequant32<BLOCK, FMT>(cw[r], sb[r], bw);
+                if constexpr (PRE) dequant32<BLOCK, FMT>(cw[r], (uint64_t)sbyte(r), bw);
+                else dequant32<BLOCK, FMT>(cw[r], sb[r], bw);
 #pragma unroll
                 for (int m = 0; m < MM; ++m)
 #pragma unroll
