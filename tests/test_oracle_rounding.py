@@ -195,3 +195,44 @@ def test_scale_of_f64_reciprocal_product_is_exact(ox, fmt):
     exact = ox.scale_bytes(a.astype(np.float64), 1.0, fmt)
     via_q = ox.scale_bytes(6.0 * q.astype(np.float64), 1.0, fmt)
     np.testing.assert_array_equal(exact, via_q)
+
+
+def _f32_neighbours(v: float) -> np.ndarray:
+    """The fp32 values adjacent to the real v: the largest fp32 below, the smallest above, and v
+    itself when it is an fp32 value (v >= 0, v within the fp32 range)."""
+    f = np.float32(v)
+    lo = f if float(f) <= v else np.nextafter(f, np.float32(0))
+    hi = f if float(f) >= v else np.nextafter(f, np.float32(np.inf))
+    cand = [np.nextafter(lo, np.float32(0)), lo, hi, np.nextafter(hi, np.float32(np.inf))]
+    return np.array(cand, dtype=np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e8m0"])
+def test_scale_of_fl32_quotient_is_exact_for_every_fp32(ox, fmt):
+    """Proof, for every positive finite fp32 a, that rounding fl32(a/6) onto the scale format
+    gives the byte of the exact a/6.  Both maps a -> byte are non-decreasing step functions of
+    a (fl32 division and nearest rounding are monotone).  The exact one steps only where a/6
+    crosses a midpoint between neighbouring scale values; if the two maps agree on the fp32
+    values on either side of every such step and at both ends of the fp32 range, then on each
+    interval between steps the quotient map is squeezed between equal values, so they agree
+    everywhere.  Checked: both neighbours (and one more on each side) of 6 x every midpoint
+    inside the fp32 range, the smallest subnormal and the largest finite fp32."""
+    vals = np.array([ox.scale_value(b, fmt) for b in range(0x7F if fmt == "e4m3" else 0xFF)])
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    fmax = float(np.finfo(np.float32).max)
+    pts = [np.array([2.0 ** -149, fmax], dtype=np.float32)]
+    # the flush step of E4M3 / UE5M3 sits at half the smallest subnormal scale (included in mids
+    # as the midpoint between 0 and it); E8M0 has no zero, its lowest step is between 2^-127 and
+    # 2^-126
+    for m in mids:
+        if 2.0 ** -149 <= 6.0 * m <= fmax:
+            pts.append(_f32_neighbours(6.0 * m))
+    a = np.concatenate(pts)
+    a = a[(a > 0) & np.isfinite(a)]
+    q = (a / np.float32(6.0)).astype(np.float32)
+    exact = ox.scale_bytes(a.astype(np.float64), 1.0, fmt)
+    via_q = ox.scale_bytes(6.0 * q.astype(np.float64), 1.0, fmt)
+    np.testing.assert_array_equal(exact, via_q)
+    # and the exact map does step at each of those midpoints (the premise of the argument)
+    inside = [m for m in mids if 2.0 ** -149 <= 6.0 * m <= fmax]
+    assert len(inside) > 10
