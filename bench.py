@@ -17,9 +17,13 @@ The remaining rows of the hot path are measured in the same run (`rows`): decode
 distinct weight copies), 70B-FFN prefill GEMM (2048 x 8192 x 28672) in W4A16 and W4A4, and
 the 405B-FFN shapes with two-level UE5M3 scaling (offline weight quantize; GEMV M=1; GEMM
 M=256, 4096).  `roofline` is for the dominant kernel, the B=32 E8M0 quantize; `cpu_baseline`
-times the single-threaded CPU oracle on a bounded sample of the same sweep.
+times the single-threaded CPU oracle, pinned to one core, on a bounded sample of the same
+sweep and on samples of the GEMV / GEMM rows.
 
-Prints ONE JSON line on stdout; progress goes to stderr.
+Prints ONE short JSON line on stdout (the summary: value, roofline, cpu_baseline and the rows
+as time and fraction of roofline); progress and the full per-configuration record
+(`[bench] detail {...}`: per-config times, the device error split, the block-size policy, the
+FP8 fallback rows) go to stderr, and with `--detail PATH` also to a JSON file.
 
 `--pmc-run` only launches the dominant kernel (five times) and a plain device copy of known
 size (five times, the calibration for the HBM byte counters), for
@@ -72,6 +76,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-rows", action="store_true", help="skip the GEMV/GEMM rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--detail", default=None,
+                    help="also write the full per-configuration record to this JSON file")
     ap.add_argument("--pmc-run", nargs="?", const="quantize", choices=("quantize", "rows"),
                     help="only the launches that the counters are read on: the dominant kernel "
                          "(default) or the GEMV / GEMM rows")
@@ -214,7 +220,9 @@ def main():
     rows = None if args.no_rows else measure_rows(mx, L, torch, np, synth, dev, stream)
     fp8 = None if args.no_rows else measure_fp8(mx, L, torch, np, synth, dev, stream)
 
-    cpu = None if args.no_cpu else cpu_baseline(np, synth)
+    detail = {"per_config": per_config, "error_split": error_split, "block_policy": block_policy,
+              "rows": rows, "fp8_fallback": fp8}
+    cpu = None if args.no_cpu else cpu_baseline(np, synth, value, rows)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -223,17 +231,63 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama7b-ffn 4096x11008 bf16 block/scale sweep: 3 sigma x 7 blocks "
                                "x 3 scale formats, quantize + dequantize (126 launches/step)",
-                   "rows": C2_ROWS, "k": C2_K, "sigmas": list(SIGMAS), "blocks": list(BLOCKS),
-                   "formats": list(FMTS), "bytes_per_step": step_bytes},
+                   "bytes_per_step": step_bytes},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "per_config": per_config,
-        "error_split": error_split,
-        "block_policy": block_policy,
-        "rows": rows,
-        "fp8_fallback": fp8,
+        "rows": compact_rows(rows, fp8, error_split),
     }
-    print(json.dumps(out), flush=True)
+    line = json.dumps(out, separators=(",", ":"))
+    # the full per-configuration record goes to stderr (and to --detail if given); stdout
+    # carries one short line
+    dline = json.dumps(detail, separators=(",", ":"))
+    log("detail " + dline)
+    if args.detail:
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail)), exist_ok=True)
+        with open(args.detail, "w") as fh:
+            fh.write(json.dumps({"summary": out, **detail}, indent=1))
+    if len(line) > 4096:
+        log(f"warning: summary line is {len(line)} bytes")
+    print(line, flush=True)
+
+
+def compact_rows(rows, fp8, error_split):
+    """The GEMV / GEMM / 405B rows in short form: time per launch (us for the GEMVs, ms
+    otherwise) and the fraction of the roofline that bounds the row ("of": HBM for quantize and
+    the GEMVs, the bf16 or FP4 matrix-core peak for the GEMMs)."""
+    if rows is None:
+        return None
+    out = {}
+
+    def put(name, r, fkey, of):
+        if r is None:
+            return
+        if "us_per_launch" in r:
+            out[name] = {"us": r["us_per_launch"], "frac": r[fkey], "of": of}
+        elif "us" in r:
+            out[name] = {"us": r["us"], "frac": r[fkey], "of": of}
+        else:
+            out[name] = {"ms": r["ms"], "frac": r[fkey], "of": of}
+
+    for nn in (4096, 14336):
+        for m in (1, 4, 16):
+            key = f"gemv_a16.m{m}.n{nn}.k4096"
+            put(key, rows.get(key), "frac_hbm", "hbm")
+    for key, of in (("gemm_a16.m2048.n28672.k8192", "bf16"), ("gemm_a4.m2048.n28672.k8192", "fp4"),
+                    ("gemm_a4.m2048.n28672.k8192.tiled_scales", "fp4")):
+        put(key, rows.get(key), "frac_peak", of)
+    put("quantize.ue5m3.g.n53248.k16384", rows.get("quantize.ue5m3.g.n53248.k16384"), "frac_hbm", "hbm")
+    for key in ("gemm_a16.ue5m3.g.m1.n53248.k16384", "gemm_a16.ue5m3.g.m1.n53248.k16384.preshuffled_scales"):
+        put(key.replace("gemm_a16", "gemv_a16"), rows.get(key), "frac_hbm", "hbm")
+    for m in (256, 4096):
+        key = f"gemm_a16.ue5m3.g.m{m}.n53248.k16384"
+        put(key, rows.get(key), "frac_peak_bf16", "bf16")
+    if error_split is not None:
+        out["error_split.63cfg"] = {"ms": error_split["sweep_ms"],
+                                    "frac": round(error_split["sweep_GB/s"] * 1e9 / PEAK_HBM, 3), "of": "hbm"}
+    for key, r in (fp8 or {}).items():
+        put(key, r, "frac_peak_bf16" if key.startswith("gemm_w8") else "frac_hbm",
+            "bf16" if key.startswith("gemm_w8") else "hbm")
+    return out
 
 
 def measure_error_split(mx, L, torch, inputs, sweep_cfgs, dev, stream):
@@ -658,6 +712,7 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     # 405B-FFN: offline two-level quantize, GEMV M=1, GEMM M=256 / 4096
     wh = synth.c5_weight()
     g = synth.c5_tensor_scale(wh)
+    rows["c5_tensor_scale"] = g
     w = dev_bf16(wh)
     del wh
     N, K = 53248, 16384
@@ -707,27 +762,108 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     return rows
 
 
-def cpu_baseline(np, synth):
-    """The CPU oracle as it stands (single-threaded C, fp64) on a bounded sample of the
-    sweep: the first 192 of 4096 rows of each sigma's weight, every block size and format,
-    quantize + dequantize."""
+def host_info():
+    """Host cores and CPU model, as the process sees them."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_count": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "model": model}
+
+
+# GEMM rows the oracle is timed on: (row name, full m, n, k, sampled rows, sampled columns, mode)
+ORACLE_GEMM = (
+    ("gemv_a16.m1.n14336.k4096", 1, 14336, 4096, 1, 14336, "a16"),
+    ("gemv_a16.m16.n14336.k4096", 16, 14336, 4096, 16, 14336, "a16"),
+    ("gemm_a16.m2048.n28672.k8192", 2048, 28672, 8192, 16, 4096, "a16"),
+    ("gemm_a4.m2048.n28672.k8192", 2048, 28672, 8192, 16, 4096, "a4"),
+    ("gemm_a16.ue5m3.g.m4096.n53248.k16384", 4096, 53248, 16384, 16, 2048, "a16"),
+)
+
+
+def cpu_baseline(np, synth, gpu_value, rows):
+    """The CPU oracle as it stands (single-threaded C, fp64 where it computes in floating
+    point), on the host's first usable core, on bounded samples of the workloads:
+     * the step's workload (`value`): quantize + dequantize of the first 256 of 4096 rows of
+       each sigma's Llama-7B FFN weight, every block size and scale format (GB/s of the same
+       algorithmic bytes as the GPU step);
+     * the GEMM oracle (dequantize, then an fp64 product): the decode GEMV rows in full (one
+       and sixteen activation rows, 14336 x 4096 weight), and 16 activation rows against a
+       slice of weight rows for the 70B-FFN prefill (W4A16 and W4A4) and the 405B-FFN m = 4096
+       product; their full-size times are estimated from a 16-row and a 1-row run of the same
+       weight slice (per weight row: one dequantization plus one dot product per activation
+       row), scaled to all n rows.
+    Inputs are generated and the sampled weights quantized before the clock starts; only the
+    oracle calls are timed."""
     import oracle
-    sample_rows = 448
-    t0 = time.perf_counter()
-    byt = 0
-    for sigma in SIGMAS:
-        w = synth.c2_weight(sigma, row0=0, nrows=sample_rows)
-        for b in BLOCKS:
-            for f in FMTS:
-                c, s = oracle.quantize(w, b, f)
-                oracle.dequantize(c, s, C2_K, b, f, 1.0, "bf16")
-                byt += 2 * quant_bytes(sample_rows * C2_K, b)
-    dt = time.perf_counter() - t0
-    log(f"cpu oracle sample: {dt:.1f}s")
-    return {"value": round(byt / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"{sample_rows} of {C2_ROWS} rows of each sigma's 4096x11008 weight, all 63 "
-                      "(sigma, block, format) quantize + dequantize, single-threaded C oracle"}
+    host = host_info()
+    sample_rows = 192
+    c2 = {sigma: synth.c2_weight(sigma, row0=0, nrows=sample_rows) for sigma in SIGMAS}
+    gemm_inputs = []
+    for name, m, n, k, ms, ns, mode in ORACLE_GEMM:
+        if k == 4096:
+            x, w, fmt, g = synth.c3_x(m), synth.c3_weight(n, row0=0, nrows=ns), "e8m0", 1.0
+        elif k == 8192:
+            x, w, fmt, g = synth.c4_x(row0=0, nrows=ms), synth.c4_weight(row0=0, nrows=ns), "e8m0", 1.0
+        else:
+            g = (rows or {}).get("c5_tensor_scale")
+            if g is None:
+                g = synth.c5_tensor_scale(synth.c5_weight())
+            x, w, fmt = synth.c5_x(m, row0=0, nrows=ms), synth.c5_weight(row0=0, nrows=ns), "ue5m3"
+        wc, wsc = oracle.quantize(w, 32, fmt, g)
+        gemm_inputs.append((x[:ms], wc, wsc, fmt, g))
+        del w
+    cpu = sorted(os.sched_getaffinity(0))[0]
+    saved = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {cpu})
+    try:
+        t0 = time.perf_counter()
+        byt = 0
+        for sigma in SIGMAS:
+            w = c2[sigma]
+            for b in BLOCKS:
+                for f in FMTS:
+                    c, sc = oracle.quantize(w, b, f)
+                    oracle.dequantize(c, sc, C2_K, b, f, 1.0, "bf16")
+                    byt += 2 * quant_bytes(sample_rows * C2_K, b)
+        dt = time.perf_counter() - t0
+        gemm = {}
+        for (name, m, n, k, ms, ns, mode), (x, wc, wsc, fmt, g) in zip(ORACLE_GEMM, gemm_inputs):
+            t1 = time.perf_counter()
+            oracle.gemm(x, wc, wsc, 32, fmt, g, mode)
+            gt = time.perf_counter() - t1
+            if (ms, ns) == (m, n):
+                est = gt
+            else:
+                # the oracle dequantizes each weight row once and then runs one fp64 dot product
+                # per activation row: time = (n / ns) (d + m c); a one-row run gives d + c
+                t1 = time.perf_counter()
+                oracle.gemm(x[:1], wc, wsc, 32, fmt, g, mode)
+                g1 = time.perf_counter() - t1
+                c = max(gt - g1, 0.0) / (ms - 1)
+                est = (n / ns) * (g1 - c + m * c)
+            ent = {"s": round(gt, 3), "GFLOP/s": round(2 * ms * ns * k / gt / 1e9, 3),
+                   "full_s": round(est, 2), "sample": f"{ms}x{ns} of {m}x{n}"}
+            g_row = (rows or {}).get(name)
+            if g_row is not None:
+                gpu_s = g_row["us_per_launch"] * 1e-6 if "us_per_launch" in g_row else g_row["ms"] * 1e-3
+                ent["gpu_speedup"] = round(est / gpu_s, 1)
+            gemm[name] = ent
+    finally:
+        os.sched_setaffinity(0, saved)
+    value = byt / dt / 1e9
+    log(f"cpu oracle sample: {dt:.1f}s quantize+dequantize, "
+        + ", ".join(f"{k} {v['s']}s" for k, v in gemm.items()))
+    return {"value": round(value, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2), "gpu_speedup": round(gpu_value / value, 1),
+            "sample": f"first {sample_rows} of {C2_ROWS} rows of each sigma's 4096x11008 weight, all 63 "
+                      "(sigma, block, format) quantize + dequantize; single-threaded C oracle pinned to one core",
+            "host": host, "pinned_cpu": cpu, "gemm": gemm}
 
 
 if __name__ == "__main__":

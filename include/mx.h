@@ -24,6 +24,8 @@
  *  MX_SCALE_UE5M3: unsigned 5-bit exponent (bias 15, subnormals), 3-bit mantissa,
  *                  0xFF NaN, max 114688.
  *  MX_SCALE_E8M0:  2^(byte - 127), bytes 0..254; never zero.
+ *  The NaN bytes of the scale formats (E4M3 0x7F and 0xFF, UE5M3 0xFF, E8M0 0xFF) are never
+ *  written by mx_quantize; mx_dequantize and mx_gemm read them as unspecified values.
  *  tensor_scale g: fp32, finite, normal, > 0 (1.0 = single-level scaling).
  *
  * Layout MX_LAYOUT_ROWMAJOR:
@@ -38,6 +40,9 @@
  *  grouped in tiles of 256 (T = r / 256, t = r % 256) and blocks in stages of 8 (256
  *  elements; S = b / 8, u = b % 8); with KS = ceil(k / 256) stages, the scale of (r, b) is
  *  byte  2048 (T KS + S) + 1024 (t / 128) + 32 (t % 32) + 8 ((t / 32) % 4) + u.
+ *  The buffer holds ceil(rows / 256) KS 2048 bytes (mx_scale_bytes).  Bytes of blocks
+ *  past the end of k in a row's last stage are written as 0 by mx_quantize; bytes of rows
+ *  past the end are never written nor used.
  * Layout MX_LAYOUT_PRESHUFFLED (block 32; [MXS] section 3.2 item 2 and section 5.3 item 3:
  *  scale factors grouped in aligned words, tensors rearranged for the kernel that reads
  *  them): the same codes; the scales in the order the m = 1 GEMV reads them, so that one
@@ -48,10 +53,7 @@
  *  as 0; bytes of rows past the last row (rows % 8 != 0) are not written.  Size
  *  ceil(rows / 8) * KC * 512 bytes (mx_scale_bytes).  Read by mx_dequantize and by mx_gemm
  *  in W4A16 mode with m == 1.
- *  The buffer holds ceil(rows / 256) KS 2048 bytes (mx_scale_bytes).  Bytes of blocks
- *  past the end of k in a row's last stage are written as 0 by mx_quantize; bytes of rows
- *  past the end are never written nor used.
- *  Dense tensors (x, y) are row-major with a leading dimension (row stride) in ELEMENTS.
+ * Dense tensors (x, y) are row-major with a leading dimension (row stride) in ELEMENTS.
  *
  * Conventions common to every entry point
  *  - Every pointer is a DEVICE pointer owned by the caller.  The library never allocates,

@@ -120,6 +120,42 @@ def _rows_ld(t: torch.Tensor, name: str):
     return t.size(0), t.size(1), t.stride(0) if t.size(0) > 1 else t.size(1)
 
 
+# Argument checks made before anything reaches the library: the C ABI trusts its pointers
+# and sizes, so a tensor of the wrong dtype, shape or device would be read or written out of
+# bounds on the GPU.  Dtypes and sizes are checked first, the device last.
+
+def _need_dtype(t: torch.Tensor, name: str, dtypes):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be of dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+
+
+def _need_bytes(t: torch.Tensor, name: str, nbytes: int):
+    """A contiguous uint8 buffer of at least nbytes bytes."""
+    _need_dtype(t, name, (torch.uint8,))
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < nbytes:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {nbytes} needed")
+
+
+def _need_shape(t: torch.Tensor, name: str, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_gpu(**tensors):
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (device {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {dev}")
+
+
 def mx_quantize(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0,
                 layout: str = "rowmajor", codes: torch.Tensor | None = None,
                 scales: torch.Tensor | None = None, stream=None):
@@ -127,6 +163,7 @@ def mx_quantize(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0
     Returns (codes uint8 rows x k/2, scales uint8: rows x k/block for layout "rowmajor", a
     flat buffer of mx_scale_bytes(...) bytes for layouts "tiled" and "preshuffled")."""
     rows, k, ld = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16, torch.float32))
     if codes is None:
         codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -135,6 +172,9 @@ def mx_quantize(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 1.0
         else:
             scales = torch.empty(max(mx_scale_bytes(rows, k, block, layout), 1), dtype=torch.uint8,
                                  device=x.device)
+    _need_bytes(codes, "codes", rows * (k // 2))
+    _need_bytes(scales, "scales", mx_scale_bytes(rows, k, block, layout))
+    _need_gpu(x=x, codes=codes, scales=scales)
     st = lib().mx_quantize(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt],
                            tensor_scale, LAYOUT[layout], _ptr(codes), _ptr(scales), _stream(stream))
     _check(st, "mx_quantize")
@@ -145,10 +185,18 @@ def mx_dequantize(codes: torch.Tensor, scales: torch.Tensor, k: int, block: int,
                   tensor_scale: float = 1.0, out_dtype: torch.dtype = torch.bfloat16,
                   layout: str = "rowmajor", y: torch.Tensor | None = None, stream=None):
     """y = e(code) * s * g as a rows x k tensor of out_dtype (bf16 or fp32)."""
+    if codes.dim() != 2:
+        raise ValueError("codes must be a 2-D tensor (rows x k/2)")
     rows = codes.size(0)
+    _need_shape(codes, "codes", (rows, k // 2))
+    _need_bytes(codes, "codes", rows * (k // 2))
+    _need_bytes(scales, "scales", mx_scale_bytes(rows, k, block, layout))
     if y is None:
         y = torch.empty((rows, k), dtype=out_dtype, device=codes.device)
+    _need_dtype(y, "y", (torch.bfloat16, torch.float32))
+    _need_shape(y, "y", (rows, k))
     _, _, ld = _rows_ld(y, "y")
+    _need_gpu(codes=codes, scales=scales, y=y)
     st = lib().mx_dequantize(_ptr(codes), _ptr(scales), rows, k, block, FMT[fmt], tensor_scale,
                              LAYOUT[layout], _ptr(y), _dtype_code(y.dtype), ld, _stream(stream))
     _check(st, "mx_dequantize")
@@ -171,6 +219,7 @@ def mx_quant_error(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 
     blocks, flushed blocks, non-flushed blocks whose maximum is not coded +-6.  When x_hat
     (same shape and dtype as x) is given, the dequantized tensor is written into it."""
     rows, k, ld = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16, torch.float32))
     ldh = 0
     if x_hat is not None:
         if x_hat.dtype != x.dtype or tuple(x_hat.shape) != tuple(x.shape):
@@ -178,9 +227,14 @@ def mx_quant_error(x: torch.Tensor, block: int, fmt: str, tensor_scale: float = 
         _, _, ldh = _rows_ld(x_hat, "x_hat")
     if out is None:
         out = torch.zeros(8, dtype=torch.float64, device=x.device)  # 7 used; 16-byte aligned
+    _need_dtype(out, "out", (torch.float64,))
+    if not out.is_contiguous() or out.numel() < 7:
+        raise ValueError("out must be a contiguous float64 tensor of at least 7 elements")
     need = mx_quant_error_workspace_size(rows, k, block)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _need_bytes(workspace, "workspace", need)
+    _need_gpu(x=x, x_hat=x_hat, out=out, workspace=workspace)
     st = lib().mx_quant_error(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt], tensor_scale,
                               _ptr(x_hat), ldh, _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(stream))
@@ -197,11 +251,17 @@ def mx_tensor_stats(x: torch.Tensor, out: torch.Tensor | None = None,
     """Mean, sample standard deviation and max |x| of a rows x k bf16/fp32 GPU tensor, computed
     on the device; returns a float64 device tensor of 3 values."""
     rows, k, ld = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16, torch.float32))
     if out is None:
         out = torch.zeros(4, dtype=torch.float64, device=x.device)  # 3 used; 16-byte aligned
+    _need_dtype(out, "out", (torch.float64,))
+    if not out.is_contiguous() or out.numel() < 3:
+        raise ValueError("out must be a contiguous float64 tensor of at least 3 elements")
     need = mx_tensor_stats_workspace_size(rows, k)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _need_bytes(workspace, "workspace", need)
+    _need_gpu(x=x, out=out, workspace=workspace)
     st = lib().mx_tensor_stats(_ptr(x), _dtype_code(x.dtype), rows, k, ld, _ptr(out), _ptr(workspace),
                                workspace.numel(), _stream(stream))
     _check(st, "mx_tensor_stats")
@@ -224,10 +284,14 @@ def mx_quantize_fp8(x: torch.Tensor, block: int, fmt: str, tensor_scale: float =
     """FP8 (E4M3 element) MX quantization of x (rows x k, bf16/fp32 on the GPU) -> (codes rows x k
     uint8, scales rows x k/block uint8)."""
     rows, k, ld = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16, torch.float32))
     if codes is None:
         codes = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((rows, k // block if block else 0), dtype=torch.uint8, device=x.device)
+    _need_bytes(codes, "codes", rows * k)
+    _need_bytes(scales, "scales", mx_scale_bytes(rows, k, block))
+    _need_gpu(x=x, codes=codes, scales=scales)
     st = lib().mx_quantize_fp8(_ptr(x), _dtype_code(x.dtype), rows, k, ld, block, FMT[fmt], tensor_scale,
                                _ptr(codes), _ptr(scales), _stream(stream))
     _check(st, "mx_quantize_fp8")
@@ -237,10 +301,17 @@ def mx_quantize_fp8(x: torch.Tensor, block: int, fmt: str, tensor_scale: float =
 def mx_dequantize_fp8(codes: torch.Tensor, scales: torch.Tensor, block: int, fmt: str,
                       tensor_scale: float = 1.0, out_dtype: torch.dtype = torch.float32,
                       y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    if codes.dim() != 2:
+        raise ValueError("codes must be a 2-D tensor (rows x k)")
     rows, k = codes.shape
+    _need_bytes(codes, "codes", rows * k)
+    _need_bytes(scales, "scales", mx_scale_bytes(rows, k, block))
     if y is None:
         y = torch.empty((rows, k), dtype=out_dtype, device=codes.device)
+    _need_dtype(y, "y", (torch.bfloat16, torch.float32))
+    _need_shape(y, "y", (rows, k))
     _, _, ldy = _rows_ld(y, "y")
+    _need_gpu(codes=codes, scales=scales, y=y)
     st = lib().mx_dequantize_fp8(_ptr(codes), _ptr(scales), rows, k, block, FMT[fmt], tensor_scale, _ptr(y),
                                  _dtype_code(y.dtype), ldy, _stream(stream))
     _check(st, "mx_dequantize_fp8")
@@ -252,10 +323,18 @@ def mx_gemm_fp8(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, 
                 y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Y = X . dequant(W8)^T; x: m x k bf16; w_codes: n x k; w_scales: n x k/block."""
     m, k, ldx = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16,))
+    if w_codes.dim() != 2 or w_codes.size(1) != k:
+        raise ValueError(f"w_codes must be a 2-D tensor (n x {k})")
     n = w_codes.size(0)
+    _need_bytes(w_codes, "w_codes", n * k)
+    _need_bytes(w_scales, "w_scales", mx_scale_bytes(n, k, block))
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _need_dtype(y, "y", (torch.bfloat16, torch.float32))
+    _need_shape(y, "y", (m, n))
     _, _, ldy = _rows_ld(y, "y")
+    _need_gpu(x=x, w_codes=w_codes, w_scales=w_scales, y=y)
     st = lib().mx_gemm_fp8(_ptr(x), m, n, k, ldx, _ptr(w_codes), _ptr(w_scales), block, FMT[fmt], tensor_scale,
                            _ptr(y), _dtype_code(y.dtype), ldy, _stream(stream))
     _check(st, "mx_gemm_fp8")
@@ -276,14 +355,24 @@ def mx_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, bloc
             workspace: torch.Tensor | None = None, stream=None):
     """Y = X . dequant(Wq)^T.  x: m x k bf16; w_codes: n x k/2; w_scales: n x k/block."""
     m, k, ldx = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16,))
+    if w_codes.dim() != 2 or w_codes.size(1) != k // 2:
+        raise ValueError(f"w_codes must be a 2-D tensor (n x {k // 2})")
     n = w_codes.size(0)
+    _need_bytes(w_codes, "w_codes", n * (k // 2))
+    _need_bytes(w_scales, "w_scales", mx_scale_bytes(n, k, block, layout))
     if y is None:
         y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _need_dtype(y, "y", (torch.bfloat16, torch.float32))
+    _need_shape(y, "y", (m, n))
     _, _, ldy = _rows_ld(y, "y")
     need = mx_gemm_workspace_size(m, n, k, block, mode)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        _need_bytes(workspace, "workspace", need)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _need_gpu(x=x, w_codes=w_codes, w_scales=w_scales, y=y, workspace=workspace)
     st = lib().mx_gemm(_ptr(x), m, n, k, ldx, _ptr(w_codes), _ptr(w_scales), block, FMT[fmt],
                        tensor_scale, LAYOUT[layout], MODE[mode], _ptr(y), _dtype_code(y.dtype), ldy,
                        _ptr(workspace), wbytes, _stream(stream))

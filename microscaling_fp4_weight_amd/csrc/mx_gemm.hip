@@ -166,15 +166,17 @@ struct GlW {
 // Scale byte(s) of the lane's 32 k in 128-k step kt (kq = lane / 16).  For blocks of 32 and
 // more, the 512 k of a wave's range have at most 16 scale bytes per row, which one load per
 // lane brings at once (the four lanes of a row read the same bytes) instead of one scattered
-// byte per step; k past the end gets a neutral byte (its codes are zero).
-template <int BLOCK>
+// byte per step; k past the end gets the format's byte for 1.0 (its codes are zero, so any
+// finite scale gives zero products).
+template <int BLOCK, int FMT>
 __device__ __forceinline__ uint64_t gl_scale(const GlW<BLOCK>& w, int kt, int kq, bool ok)
 {
     if constexpr (BLOCK >= 32) {
+        constexpr uint32_t one = FMT == FMT_E8M0 ? 127u : FMT == FMT_E4M3 ? 0x38u : 0x78u;
         const int dw = (kt * TK / BLOCK) / 4;                     // dword holding the byte (constant once kt is)
         const uint32_t idx = (uint32_t)(kt * TK + 32 * kq) / BLOCK;
         const uint32_t v = dw == 0 ? w.srow.x : dw == 1 ? w.srow.y : dw == 2 ? w.srow.z : w.srow.w;
-        return ok ? (v >> (8 * (idx & 3))) & 0xFFu : 127u;
+        return ok ? (v >> (8 * (idx & 3))) & 0xFFu : one;
     } else {
         return w.sb[kt];
     }
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(64 * GL_WAVES) void gemv_lds_kernel(const GemmArgs 
 #pragma unroll
             for (int kt = 0; kt < GL_KTW; ++kt) {
                 uint32_t bw[16];
-                dequant32<BLOCK, FMT>(w.cw[kt], gl_scale<BLOCK>(w, kt, kq, kc + kw + kt * TK + 32 * kq < K), bw);
+                dequant32<BLOCK, FMT>(w.cw[kt], gl_scale<BLOCK, FMT>(w, kt, kq, kc + kw + kt * TK + 32 * kq < K), bw);
                 const uint8_t* xp = lds + xrow * GL_PITCH + (kw + kt * TK + 32 * kq) * 2;
                 uint32_t xf[16];
 #pragma unroll
@@ -787,8 +789,10 @@ hipError_t launch_fill_zero(void* y, int64_t m, int64_t n, int64_t ldy, bool bf1
 template <int FMT, bool OUT_BF16>
 static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
 {
+    // the GEMV kernels address X through one buffer resource with 32-bit byte offsets
+    const bool x_span_ok = ((a.m - 1) * a.ldx + a.k) * 2 < (int64_t(1) << 31);
     const bool fast = (a.k % 32 == 0) && ((a.ldx * 2) % 16 == 0) && ((uintptr_t)a.x % 16 == 0);
-    if (!fast) {
+    if (!fast || (a.m <= 16 && !x_span_ok)) {
         const int64_t total = a.m * a.n;
         hipLaunchKernelGGL((gemm_generic_kernel<FMT, false, OUT_BF16>), dim3((unsigned)((total + 255) / 256)),
                            dim3(256), 0, st, a);

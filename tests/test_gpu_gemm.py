@@ -396,3 +396,27 @@ def test_c5_two_level(m, c5_weights):
         yref, aref = oracle.gemm(x[rows], rc, rs, 32, "ue5m3", g, "a16")
         assert_gemm_close(to_host_bits(y.float())[rows][:, cols], yref, aref, out == "bf16",
                           f"C5 m={m} {out}")
+
+
+def test_gemv_rows_past_2gb_stride():
+    """Activation rows so far apart that they span more than 2^31 bytes (3.2 / 4.3 GB): the
+    GEMV kernels address X with 32-bit offsets, so such a call must take the 64-bit path and
+    still agree with the oracle (m = 4 and 16, both outputs)."""
+    n, k = 96, 512
+    w = synth.normal((n, k), "bf16", "span.w", 0.02)
+    c, s, cd, sd = quantize_ref(w, 32, "e8m0")
+    for m, ld in ((4, 1 << 29), (16, 1 << 27)):
+        assert ((m - 1) * ld + k) * 2 >= 1 << 31
+        x = synth.normal((m, k), "bf16", f"span.x.{m}", 1.0)
+        print(f"span test m={m} ld={ld}", flush=True)
+        buf = torch.zeros((m - 1) * ld + k, dtype=torch.bfloat16, device=DEV)
+        xs = buf.as_strided((m, k), (ld, 1))
+        xs.copy_(bf16_dev(x))
+        for out in ("f32", "bf16"):
+            dt = torch.float32 if out == "f32" else torch.bfloat16
+            y = mx.mx_gemm(xs, cd, sd, 32, "e8m0", 1.0, "a16", out_dtype=dt)
+            torch.cuda.synchronize()
+            yref, aref = oracle.gemm(x, c, s, 32, "e8m0", 1.0, "a16")
+            assert_gemm_close(to_host_bits(y.float()), yref, aref, out == "bf16", f"span m={m} {out}")
+        del buf, xs
+        torch.cuda.empty_cache()

@@ -188,7 +188,9 @@ def test_dequantize(out, fmt, block, g):
 
 
 def test_dequantize_all_scale_bytes():
-    # every code with every scale byte (including those whose products overflow)
+    # every code with every finite scale byte (including those whose products overflow); the
+    # formats' NaN bytes are left out because the library's contract (include/mx.h) leaves
+    # their decoded value unspecified: mx_quantize never writes them
     for fmt in FMTS:
         codes = np.tile(np.arange(256, dtype=np.uint8), 256).reshape(256, 256)  # 512 elems/row
         scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 512 // 32, axis=1)
