@@ -57,7 +57,8 @@
  *
  * Conventions common to every entry point
  *  - Every pointer is a DEVICE pointer owned by the caller.  The library never allocates,
- *    frees, or synchronizes; it keeps no global mutable state and is thread-safe.
+ *    frees, or synchronizes; apart from mx_gemm_static's static scratch buffer (see there)
+ *    it keeps no global mutable state and is thread-safe.
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
  *    Outputs are valid once the stream has reached the call.
  *  - Arguments are validated on the host before anything is launched.  On an error status
@@ -86,7 +87,8 @@ typedef enum {
     MX_ERR_INVALID_ARG = -1, /* null pointer, negative size, k % block, bad enum, bad g, ... */
     MX_ERR_UNSUPPORTED = -2, /* a valid combination this library does not implement        */
     MX_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned                           */
-    MX_ERR_HIP = -4          /* the HIP runtime reported an error at launch                */
+    MX_ERR_HIP = -4,         /* the HIP runtime reported an error at launch                */
+    MX_ERR_TOO_LARGE = -5    /* mx_gemm_static: the call needs more than its static scratch */
 } mx_status;
 
 typedef enum { MX_SCALE_E4M3 = 0, MX_SCALE_UE5M3 = 1, MX_SCALE_E8M0 = 2 } mx_scale_fmt;
@@ -272,6 +274,28 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
                   float tensor_scale, mx_layout layout, mx_act_mode mode, void* y,
                   mx_dtype y_type, int64_t ld_y, void* workspace, size_t workspace_bytes,
                   void* stream);
+
+/*
+ * mx_gemm_static -- mx_gemm without a workspace argument, for callers that cannot allocate
+ * device memory around the call: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  The W4A4 activation codes and scales go to a scratch
+ * buffer the library owns: a static device array of MX_GEMM_STATIC_SCRATCH_BYTES (32 MiB)
+ * that every GPU the library runs on holds until the process ends.  Nothing is allocated or
+ * freed by this call.
+ *  Arguments, results and errors as mx_gemm (the same kernels run), plus MX_ERR_TOO_LARGE when
+ *  mx_gemm_workspace_size(m, n, k, block, mode) exceeds MX_GEMM_STATIC_SCRATCH_BYTES (W4A4 with
+ *  m * k above about 6.3e7), checked on the host before anything is launched.  W4A16 calls use
+ *  no scratch.
+ *  All calls on one GPU share that GPU's buffer: two W4A4 calls that may run at the same time
+ *  on one GPU (different streams without ordering between them) race on it and give wrong
+ *  results.  Calls ordered on one stream are safe; each call writes all the scratch it reads.
+ *  The buffer's device address is looked up on the first call on each device.
+ */
+#define MX_GEMM_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+mx_status mx_gemm_static(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
+                         const uint8_t* w_codes, const uint8_t* w_scales, int block, mx_scale_fmt fmt,
+                         float tensor_scale, mx_layout layout, mx_act_mode mode, void* y,
+                         mx_dtype y_type, int64_t ld_y, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* mx_status_string(mx_status s);

@@ -29,7 +29,8 @@ DTYPE = {"f32": 0, "bf16": 1}
 MODE = {"a16": 0, "a4": 1}
 LAYOUT = {"rowmajor": 0, "tiled": 1, "preshuffled": 2}
 STATUS = {0: "MX_OK", -1: "MX_ERR_INVALID_ARG", -2: "MX_ERR_UNSUPPORTED", -3: "MX_ERR_ALIGNMENT",
-          -4: "MX_ERR_HIP"}
+          -4: "MX_ERR_HIP", -5: "MX_ERR_TOO_LARGE"}
+GEMM_STATIC_SCRATCH_BYTES = 32 << 20  # MX_GEMM_STATIC_SCRATCH_BYTES in include/mx.h
 
 _lib = None
 
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.mx_gemm.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp,
                           sz, vp]
     L.mx_gemm.restype = i32
+    L.mx_gemm_static.argtypes = [vp, i64, i64, i64, i64, vp, vp, i32, i32, f32, i32, i32, vp, i32, i64, vp]
+    L.mx_gemm_static.restype = i32
     L.mx_status_string.argtypes = [i32]
     L.mx_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -377,4 +380,30 @@ def mx_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, bloc
                        tensor_scale, LAYOUT[layout], MODE[mode], _ptr(y), _dtype_code(y.dtype), ldy,
                        _ptr(workspace), wbytes, _stream(stream))
     _check(st, "mx_gemm")
+    return y
+
+
+def mx_gemm_static(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, block: int, fmt: str,
+                   tensor_scale: float = 1.0, mode: str = "a16", out_dtype: torch.dtype = torch.bfloat16,
+                   layout: str = "rowmajor", y: torch.Tensor | None = None, stream=None):
+    """mx_gemm with the W4A4 workspace in the library's static device buffer (no allocation
+    by the call; y must be given to keep the call allocation-free).  Calls that may overlap on
+    one GPU race on that buffer."""
+    m, k, ldx = _rows_ld(x, "x")
+    _need_dtype(x, "x", (torch.bfloat16,))
+    if w_codes.dim() != 2 or w_codes.size(1) != k // 2:
+        raise ValueError(f"w_codes must be a 2-D tensor (n x {k // 2})")
+    n = w_codes.size(0)
+    _need_bytes(w_codes, "w_codes", n * (k // 2))
+    _need_bytes(w_scales, "w_scales", mx_scale_bytes(n, k, block, layout))
+    if y is None:
+        y = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _need_dtype(y, "y", (torch.bfloat16, torch.float32))
+    _need_shape(y, "y", (m, n))
+    _, _, ldy = _rows_ld(y, "y")
+    _need_gpu(x=x, w_codes=w_codes, w_scales=w_scales, y=y)
+    st = lib().mx_gemm_static(_ptr(x), m, n, k, ldx, _ptr(w_codes), _ptr(w_scales), block, FMT[fmt],
+                              tensor_scale, LAYOUT[layout], MODE[mode], _ptr(y), _dtype_code(y.dtype), ldy,
+                              _stream(stream))
+    _check(st, "mx_gemm_static")
     return y

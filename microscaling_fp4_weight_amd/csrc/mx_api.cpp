@@ -92,6 +92,7 @@ const char* mx_status_string(mx_status s)
         case MX_ERR_UNSUPPORTED: return "unsupported combination";
         case MX_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
         case MX_ERR_HIP: return "HIP runtime error";
+        case MX_ERR_TOO_LARGE: return "needs more than the library's static scratch buffer";
     }
     return "unknown status";
 }

@@ -31,7 +31,7 @@ def declared_functions():
 def test_exports_match_header(L):
     names = declared_functions()
     assert names == ["mx_adaptive_block_size", "mx_dequantize", "mx_dequantize_fp8", "mx_gemm",
-                     "mx_gemm_fp8", "mx_gemm_workspace_size", "mx_layer_block_size", "mx_quant_error",
+                     "mx_gemm_fp8", "mx_gemm_static", "mx_gemm_workspace_size", "mx_layer_block_size", "mx_quant_error",
                      "mx_quant_error_workspace_size", "mx_quantize", "mx_quantize_fp8", "mx_scale_bytes",
                      "mx_status_string", "mx_tensor_stats", "mx_tensor_stats_workspace_size",
                      "mx_use_fp8"]
@@ -44,7 +44,7 @@ def test_exports_match_header(L):
 
 
 def test_status_strings(L):
-    for s in (OK, INVALID, UNSUPPORTED, ALIGN, -4):
+    for s in (OK, INVALID, UNSUPPORTED, ALIGN, -4, -5):
         assert L.mx_status_string(s)
     assert L.mx_status_string(OK) == b"success"
 
