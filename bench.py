@@ -789,7 +789,7 @@ ORACLE_GEMM = (
 def cpu_baseline(np, synth, gpu_value, rows):
     """The CPU oracle as it stands (single-threaded C, fp64 where it computes in floating
     point), on the host's first usable core, on bounded samples of the workloads:
-     * the step's workload (`value`): quantize + dequantize of the first 256 of 4096 rows of
+     * the step's workload (`value`): quantize + dequantize of the first 384 of 4096 rows of
        each sigma's Llama-7B FFN weight, every block size and scale format (GB/s of the same
        algorithmic bytes as the GPU step);
      * the GEMM oracle (dequantize, then an fp64 product): the decode GEMV rows in full (one
@@ -802,7 +802,7 @@ def cpu_baseline(np, synth, gpu_value, rows):
     oracle calls are timed."""
     import oracle
     host = host_info()
-    sample_rows = 192
+    sample_rows = 384
     c2 = {sigma: synth.c2_weight(sigma, row0=0, nrows=sample_rows) for sigma in SIGMAS}
     gemm_inputs = []
     for name, m, n, k, ms, ns, mode in ORACLE_GEMM:
