@@ -13,6 +13,7 @@ import torch
 
 import microscaling_fp4_weight_amd as mx
 import oracle
+import oracle_pool
 import synth
 from gpu_util import DEV, assert_gemm_close, bf16_dev, f32_dev, padding_positions, tiled_positions, to_host_bits
 
@@ -301,35 +302,62 @@ def test_c1_tiny_round_trip_and_gemv():
 
 @pytest.mark.parametrize("n", [4096, 14336])
 def test_c3_decode_gemv(n):
-    """Decode GEMV K=4096, N in {4096, 14336}, M in {1, 4, 16}; block 32 E8M0; bf16 out."""
+    """Decode GEMV K=4096, N in {4096, 14336}, M in {1, 4, 16}; block 32 E8M0; bf16 out.  The
+    whole weight's codes and scales bit-exact, and every output of every M checked."""
     w = synth.c3_weight(n)
     wd = bf16_dev(w)
+    del w
     cd, sd = mx.mx_quantize(wd, 32, "e8m0")
-    cols = np.unique(np.concatenate([np.arange(0, n, 97), [n - 1]]))
-    c = to_host_bits(cd[cols])
-    s = to_host_bits(sd[cols])
-    rc, rs = oracle.quantize(w[cols], 32, "e8m0")
-    np.testing.assert_array_equal(c, rc)
-    np.testing.assert_array_equal(s, rs)
-    for m in (1, 4, 16):
+    gemms = [(m, list(range(m)), "a16") for m in (1, 4, 16)]
+    rc, rs, ys = oracle_pool.full_weight(f"c3.{n}", n, "e8m0", 1.0, gemms)
+    np.testing.assert_array_equal(to_host_bits(cd), rc)
+    np.testing.assert_array_equal(to_host_bits(sd), rs)
+    for (m, _, _), (yref, aref) in zip(gemms, ys):
         x = synth.c3_x(m)
-        y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "e8m0", 1.0, "a16", out_dtype=torch.bfloat16)
-        torch.cuda.synchronize()
-        yref, aref = oracle.gemm(x, rc, rs, 32, "e8m0", 1.0, "a16")
-        assert_gemm_close(to_host_bits(y.float())[:, cols], yref, aref, True, f"C3 n={n} m={m}")
+        for dt in (torch.bfloat16, torch.float32):
+            y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "e8m0", 1.0, "a16", out_dtype=dt)
+            torch.cuda.synchronize()
+            assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"C3 n={n} m={m} {dt}")
 
 
-def _c4_setup():
+# one activation row in each 256-row m-tile of the 70B-FFN prefill (first and last rows included)
+C4_ROWS = [0, 293, 586, 879, 1172, 1465, 1758, 2047]
+
+
+@pytest.fixture(scope="module")
+def c4_full():
+    """The 70B-FFN weight quantized on the GPU (row-major and tiled scales) and by the oracle
+    (all 28672 rows, over host processes), with the oracle's W4A16 and W4A4 products for the
+    C4_ROWS activation rows against every weight row."""
     w = synth.c4_weight()
     wd = bf16_dev(w)
+    del w
     cd, sd = mx.mx_quantize(wd, 32, "e8m0")
+    _, sdt = mx.mx_quantize(wd, 32, "e8m0", layout="tiled")
     del wd
-    cols = np.array([0, 1, 5000, 14335, 20000, 28671])
-    rows = np.array([0, 1, 700, 1500, 2047])
-    rc, rs = oracle.quantize(w[cols], 32, "e8m0")
-    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
-    np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
-    return cd, sd, rc, rs, rows, cols
+    torch.cuda.empty_cache()
+    rc, rs, ys = oracle_pool.full_weight("c4", 28672, "e8m0", 1.0,
+                                         [(2048, C4_ROWS, "a16"), (2048, C4_ROWS, "a4")])
+    np.testing.assert_array_equal(to_host_bits(cd), rc)
+    np.testing.assert_array_equal(to_host_bits(sd), rs)
+    return cd, sd, sdt, {"a16": ys[0], "a4": ys[1]}
+
+
+@pytest.mark.parametrize("mode,layout", [("a16", "rowmajor"), ("a4", "rowmajor"), ("a4", "tiled")])
+def test_c4_prefill(mode, layout, c4_full):
+    """70B FFN prefill M=2048, K=8192, N=28672, block 32 E8M0: W4A16 and W4A4 (row-major and
+    tiled weight scales); all 28672 columns of one row in each 256-row m-tile, so every output
+    tile (and the W4A4 half tiles of the last round) is reached; fp32 and bf16 out."""
+    cd, sd, sdt, ref = c4_full
+    yref, aref = ref[mode]
+    xd = bf16_dev(synth.c4_x())
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm(xd, cd, sdt if layout == "tiled" else sd, 32, "e8m0", 1.0, mode, out_dtype=dt,
+                       layout=layout)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y[C4_ROWS].float()), yref, aref, dt == torch.bfloat16,
+                          f"C4 {mode} {layout} {dt}")
+        del y
 
 
 # The wide-tile W4A16 kernel (256 x 256 tiles, 128 x 64 per wave): always for E4M3 / UE5M3
@@ -358,44 +386,43 @@ def test_gemm_a16_wide_tiles_sampled(fmt, g):
                           f"wide tiles {fmt} {dt}")
 
 
-@pytest.mark.parametrize("mode", ["a16", "a4"])
-def test_c4_prefill(mode):
-    """70B FFN prefill M=2048, K=8192, N=28672, block 32 E8M0: W4A16 and W4A4."""
-    cd, sd, rc, rs, rows, cols = _c4_setup()
-    x = synth.c4_x()
-    y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "e8m0", 1.0, mode, out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    yref, aref = oracle.gemm(x[rows], rc, rs, 32, "e8m0", 1.0, mode)
-    assert_gemm_close(to_host_bits(y[rows][:, cols]), yref, aref, False, f"C4 {mode}")
+# activation rows of the 405B-FFN products: one in each 256-row m-tile for m = 4096
+C5_ROWS = {1: [0], 256: [0, 85, 170, 255], 4096: [256 * i + (97 * i) % 256 for i in range(15)] + [4095]}
 
 
 @pytest.fixture(scope="module")
 def c5_weights():
+    """The 405B-FFN weight (53248 x 16384, UE5M3 block 32, per-tensor g) quantized on the GPU and,
+    all rows, by the oracle over host processes, with the oracle's products for C5_ROWS."""
     w = synth.c5_weight()
     g = synth.c5_tensor_scale(w)
     wd = bf16_dev(w)
+    del w
     cd, sd = mx.mx_quantize(wd, 32, "ue5m3", g)
     del wd
-    cols = np.array([0, 3328 * 3 + 5, 26000, 53247])
-    rc, rs = oracle.quantize(w[cols], 32, "ue5m3", g)
-    np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
-    return cd, sd, rc, rs, cols, g
+    torch.cuda.empty_cache()
+    gemms = [(m, C5_ROWS[m], "a16") for m in (1, 256, 4096)]
+    rc, rs, ys = oracle_pool.full_weight("c5", 53248, "ue5m3", g, gemms)
+    np.testing.assert_array_equal(to_host_bits(cd), rc)
+    np.testing.assert_array_equal(to_host_bits(sd), rs)
+    return cd, sd, g, {m: y for (m, _, _), y in zip(gemms, ys)}
 
 
 @pytest.mark.parametrize("m", [1, 256, 4096])
 def test_c5_two_level(m, c5_weights):
     """405B FFN K=16384, N=53248, UE5M3 block 32 with per-tensor g; W4A16, fp32 accumulate,
-    bf16 out (fp32 out also checked for M=1)."""
-    cd, sd, rc, rs, cols, g = c5_weights
-    x = synth.c5_x(m)
-    rows = np.unique(np.array([0, m // 2, m - 1]))
+    bf16 out (fp32 out also for M=1): every column of the sampled rows (all 53248 outputs for
+    M=1, one row per 256-row m-tile for M=4096)."""
+    cd, sd, g, ref = c5_weights
+    yref, aref = ref[m]
+    rows = C5_ROWS[m]
+    xd = bf16_dev(synth.c5_x(m))
     for out in (("f32", "bf16") if m == 1 else ("bf16",)):
         dt = torch.float32 if out == "f32" else torch.bfloat16
-        y = mx.mx_gemm(bf16_dev(x), cd, sd, 32, "ue5m3", g, "a16", out_dtype=dt)
+        y = mx.mx_gemm(xd, cd, sd, 32, "ue5m3", g, "a16", out_dtype=dt)
         torch.cuda.synchronize()
-        yref, aref = oracle.gemm(x[rows], rc, rs, 32, "ue5m3", g, "a16")
-        assert_gemm_close(to_host_bits(y.float())[rows][:, cols], yref, aref, out == "bf16",
-                          f"C5 m={m} {out}")
+        assert_gemm_close(to_host_bits(y[rows].float()), yref, aref, out == "bf16", f"C5 m={m} {out}")
+        del y
 
 
 def test_gemv_rows_past_2gb_stride():

@@ -4,9 +4,10 @@ Codes and scale bytes must be bit-exact; dequantized values bit-exact.  Cases: e
 size x scale format x input dtype on small tensors spanning several workgroups with a
 ragged tail; the edge-case tensor (every scale byte, every bf16 magnitude to 6, exact ties,
 zero / flush / saturating / subnormal blocks); shapes that take the generic path (k not a
-multiple of 32, odd row stride); empty tensors; a per-tensor scale; and the full-size
-Llama-7B FFN (4096 x 11008) and 405B FFN (53248 x 16384) weights in the launch
-configuration the benchmark times, on sampled rows.
+multiple of 32, odd row stride); empty tensors; a per-tensor scale; every E4M3 / UE5M3 scale
+mantissa with every bf16 magnitude under it; and the full-size Llama-7B FFN (4096 x 11008)
+and 405B FFN (53248 x 16384) weights in the launch configuration the benchmark times, whole
+tensors compared.
 """
 import numpy as np
 import pytest
@@ -14,6 +15,7 @@ import torch
 
 import microscaling_fp4_weight_amd as mx
 import oracle
+import oracle_pool
 import synth
 from gpu_util import DEV, bf16_dev, edge_tensor, f32_dev, to_host_bits
 
@@ -261,14 +263,70 @@ def test_c2_full_tensor_exact(sigma, block, fmt):
                                   err_msg=f"dequantized {fmt} B={block}")
 
 
-def test_c5_full_size_two_level_sampled():
+def test_c5_full_tensor_two_level():
     """405B FFN weight 53248 x 16384 bf16, UE5M3 block 32 times a per-tensor scale
-    g = fl32(max|W| / (6 * 114688)); sampled rows bit-exact, including the narrow bands."""
+    g = fl32(max|W| / (6 * 114688)): every code and scale byte of the whole tensor equal to the
+    oracle's (oracle over host processes); dequantized rows sampled, including the narrow bands."""
     w = synth.c5_weight()
     g = synth.c5_tensor_scale(w)
     wd = bf16_dev(w)
     c, s = mx.mx_quantize(wd, 32, "ue5m3", g)
+    del wd
+    torch.cuda.synchronize()
+    rc, rs, _ = oracle_pool.full_weight("c5", 53248, "ue5m3", g, [])
+    np.testing.assert_array_equal(to_host_bits(s), rs)
+    np.testing.assert_array_equal(to_host_bits(c), rc)
     rows = [0, 3327, 3328 * 3, 3328 * 3 + 17, 26000, 3328 * 15, 53247]
-    rc, rs = oracle.quantize(w[rows], 32, "ue5m3", g)
-    np.testing.assert_array_equal(to_host_bits(s[rows]), rs)
-    np.testing.assert_array_equal(to_host_bits(c[rows]), rc)
+    y = mx.mx_dequantize(c[rows].contiguous(), s[rows].contiguous(), 16384, 32, "ue5m3", g,
+                         out_dtype=torch.bfloat16)
+    np.testing.assert_array_equal(to_host_bits(y), oracle.dequantize(rc[rows], rs[rows], 16384, 32, "ue5m3", g, "bf16"))
+
+
+def _mantissa_blocks(fmt: str, dtype: str) -> np.ndarray:
+    """Blocks of 32 whose maximum is 6 s (so the block scale is exactly s) for every scale
+    mantissa at three normal exponents and every subnormal scale of the format, holding every
+    bf16 magnitude up to 6 s with both signs, and (fp32 input) the fp32 values within 64 ulps
+    of every decision point t s of the element rounding."""
+    exps = {"e4m3": (-6, 0, 5), "ue5m3": (-14, 0, 10)}[fmt]
+    smin_exp = {"e4m3": -9, "ue5m3": -17}[fmt]
+    scales = [(1 + mi / 8) * 2.0 ** e for mi in range(8) for e in exps]
+    scales += [mi * 2.0 ** smin_exp for mi in range(1, 8)]
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    out = []
+    for sc in scales:
+        top = np.float32(6.0 * sc)
+        assert float(top) == 6.0 * sc and (np.array([top]).view(np.uint32)[0] & 0xFFFF) == 0  # bf16-exact
+        hi = int(np.array([top]).view(np.uint32)[0] >> 16)
+        mags = (np.arange(1, hi + 1, dtype=np.uint32) << 16).view(np.float32)
+        vals = [mags, -mags, np.array([0.0, -0.0], dtype=np.float32)]
+        if dtype == "f32":
+            for t in ties:
+                b = np.array([np.float32(t * sc)]).view(np.uint32).astype(np.int64)[0]
+                near = np.arange(b - 64, b + 65, dtype=np.int64).astype(np.uint32).view(np.float32)
+                vals += [near, -near]
+        v = np.concatenate(vals)
+        v = v[np.abs(v) <= top]
+        nb = -(-len(v) // 31)
+        v = np.pad(v, (0, nb * 31 - len(v)))
+        blk = np.empty((nb, 32), dtype=np.float32)
+        blk[:, 1:] = v.reshape(nb, 31)
+        blk[:, 0] = np.where(np.arange(nb) % 2 == 0, top, -top)  # the maximum, alternating sign
+        out.append(blk.reshape(-1))
+    x = np.concatenate(out)
+    pad = (-len(x)) % 512
+    x = np.concatenate([x, np.zeros(pad, dtype=np.float32)]).reshape(-1, 512)
+    if dtype == "bf16":
+        return (x.view(np.uint32) >> 16).astype(np.uint16)  # exact: every value is bf16
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3"])
+def test_quantize_every_scale_mantissa(fmt, dtype):
+    """The element encode divides by a block scale with a mantissa (E4M3 / UE5M3): every code
+    decided exactly for all eight mantissas (and the subnormal scales), g = 1, block 32."""
+    x = _mantissa_blocks(fmt, dtype)
+    c, s = run_quant(x, 32, fmt)
+    rc, rs = oracle.quantize(x, 32, fmt)
+    np.testing.assert_array_equal(s, rs)
+    np.testing.assert_array_equal(c, rc)
