@@ -798,6 +798,9 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
                            dim3(256), 0, st, a);
         return hipGetLastError();
     }
+    // m = 2 takes the 16-row-unit kernel where it applies (k 4096; 5.5 against 6.4 us at n
+    // 4096, even at n 14336), the sweeping kernel otherwise (k 8192 / 16384)
+    if (a.m >= 2 && gemv16_applies(a)) return launch_gemv16(a, st);
     if (const uint32_t units = sweep_units(a)) {
         if (a.m == 1) return launch_sweep<FMT, OUT_BF16, 1, false>(a, units, st);
         return launch_sweep<FMT, OUT_BF16, 2, false>(a, units, st);

@@ -113,6 +113,10 @@ hipError_t launch_gemm_a16w(const GemmArgs& a, bool w8, hipStream_t st);
 // whether the m <= 2 sweeping GEMV takes FP8 codes of this shape, and its launcher
 bool w8_uses_sweep(const GemmArgs& a);
 hipError_t launch_gemv_sweep_w8(const GemmArgs& a, hipStream_t st);
+// the 2 <= m <= 16 GEMV with the activations in registers and 16-row weight units streamed in
+// address order (k = 4096, blocks of 32 and more, row-major scales)
+bool gemv16_applies(const GemmArgs& a);
+hipError_t launch_gemv16(const GemmArgs& a, hipStream_t st);
 
 struct ErrArgs {
     const void* x;

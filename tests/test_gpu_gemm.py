@@ -86,6 +86,32 @@ def test_gemv_sweep(fmt, n, k, m):
         np.testing.assert_array_equal(to_host_bits(yp), to_host_bits(yr[out]))
 
 
+# The 2 <= m <= 16 decode GEMV with k = 4096 (16-row weight units streamed by LDS-DMA, X in
+# registers): every block size it takes and every format, m at the edges and in between, n with
+# a ragged last unit, a grid with one unit per workgroup (n 100) and one with several (n 16 *
+# 2100 + 9: 2101 units over 526 workgroups), g != 1 for E4M3 / UE5M3; fp32 and bf16 out.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("block", [32, 64, 128, 256])
+@pytest.mark.parametrize("m,n", [(3, 100), (16, 100), (5, 33609), (16, 33609)])
+def test_gemv16(fmt, block, m, n):
+    k = 4096
+    g = float(np.float32(0.37)) if fmt != "e8m0" else 1.0
+    x = synth.normal((m, k), "bf16", f"g16.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", f"g16.w.{n}", 0.02, 0.01, 20.0)
+    c, s, cd, sd = quantize_ref(w, block, fmt, g)
+    cols = None if n <= 100 else np.unique(np.concatenate([np.arange(0, n, 37), np.arange(n - 40, n)]))
+    c_sel, s_sel = (c, s) if cols is None else (c[cols], s[cols])
+    xd = bf16_dev(x)
+    for out, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        y = mx.mx_gemm(xd, cd, sd, block, fmt, g, "a16", out_dtype=dt)
+        torch.cuda.synchronize()
+        yref, aref = oracle.gemm(x, c_sel, s_sel, block, fmt, g, "a16")
+        got = to_host_bits(y.float())
+        if cols is not None:
+            got = got[:, cols]
+        assert_gemm_close(got, yref, aref, out == "bf16", f"gemv16 m={m} n={n} {fmt} B={block} {out}")
+
+
 # Zero-scale blocks through the GEMVs (an E4M3 / UE5M3 scale's mantissa multiplies each block's
 # sum there, so a zero scale must give a zero block): all-zero blocks and blocks small enough
 # to flush (a <= 3 s_min: 1e-4 under E4M3, 1e-6 under UE5M3), on the sweeping kernel (k 4096)
