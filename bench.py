@@ -29,7 +29,7 @@ FP8 fallback rows) go to stderr, and with `--detail PATH` also to a JSON file.
 size (five times, the calibration for the HBM byte counters), for
 `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`; the resulting per-launch bytes are kept in
 profiles/traffic.json and reported as `roofline.traffic` while the kernel source is unchanged.
-`--pmc-run rows` launches the decode GEMV (m 1, n 14336), the 405B-FFN GEMV (m 1), the 70B-FFN
+`--pmc-run rows` launches the decode GEMV (m 1, 4, 16; n 14336), the 405B-FFN GEMV (m 1), the 70B-FFN
 prefill GEMM in W4A16 and W4A4 (tiled weight scales) three times each, and the same copy, for
 the HBM byte and matrix-core counters of those kernels.
 """
@@ -524,7 +524,7 @@ def pmc_run(mx, torch, np, synth, dev):
 
 
 def pmc_rows(mx, torch, np, synth, dev):
-    """Three launches each of the decode GEMV (m 1, n 14336, k 4096, block 32 E8M0), the
+    """Three launches each of the decode GEMV (m 1, 4 and 16, n 14336, k 4096, block 32 E8M0), the
     405B-FFN GEMV (m 1, UE5M3 with a tensor scale), the 70B-FFN prefill GEMM in W4A16 and in
     W4A4 with tiled weight scales (its activation pre-pass is a quantize launch of its own),
     each after a 512 MB fill that evicts the Infinity Cache, then five copies of COPY_BYTES."""
@@ -549,7 +549,12 @@ def pmc_rows(mx, torch, np, synth, dev):
     y = torch.empty((1, 14336), dtype=bf, device=dev)
     launch3(f"decode GEMV m 1 n 14336 k 4096 ({gemv_bytes(1, 14336, 4096, 32)} algorithmic bytes)",
             lambda: mx.mx_gemm(x, c3, s3, 32, "e8m0", 1.0, "a16", y=y))
-    del c3, s3, x, y
+    for m in (4, 16):
+        xm = dev_bf16(synth.c3_x(m))
+        ym = torch.empty((m, 14336), dtype=bf, device=dev)
+        launch3(f"decode GEMV m {m} n 14336 k 4096 ({gemv_bytes(m, 14336, 4096, 32)} algorithmic bytes)",
+                lambda: mx.mx_gemm(xm, c3, s3, 32, "e8m0", 1.0, "a16", y=ym))
+    del c3, s3, x, y, xm, ym
 
     wh = synth.c5_weight()
     g = synth.c5_tensor_scale(wh)
