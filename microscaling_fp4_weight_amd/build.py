@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmx.so")
-SOURCES = ["mx_quant.hip", "mx_error.hip", "mx_stats.hip", "mx_fp8.hip", "mx_gemm.hip", "mx_gemv16.hip", "mx_gemm_a4.hip", "mx_gemm_a16.hip", "mx_gemm_a16w.hip", "mx_static.hip", "mx_api.cpp"]
+SOURCES = ["mx_quant.hip", "mx_error.hip", "mx_stats.hip", "mx_fp8.hip", "mx_gemm.hip", "mx_gemv16.hip", "mx_gemm_a4.hip", "mx_gemm_a16.hip", "mx_gemm_a16w.hip", "mx_gemm_a16p.hip", "mx_static.hip", "mx_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -367,6 +367,7 @@ hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st)
 {
     if (!a16_uses_tiled(a)) return hipErrorInvalidValue;
     if (a16w_uses(a, false)) return launch_gemm_a16w(a, false, st);  // wider wave tiles
+    if (a16p_uses(a)) return launch_gemm_a16p(a, st);                 // two workgroups per CU
 #define MXF(F) if (a.fmt == F) return a.y_bf16 ? a16::launch_tiled<F, true, false>(a, st) : a16::launch_tiled<F, false, false>(a, st);
     MXF(FMT_E4M3) MXF(FMT_UE5M3) MXF(FMT_E8M0)
 #undef MXF

@@ -1,5 +1,5 @@
 // mx_gemm_a16w.hip -- the large-m W4A16 / W8A16 GEMM with wide wave tiles (all E4M3 and UE5M3
-// weight scales and FP8 weights; E8M0 FP4 weights when its tiles fill the GPU in whole rounds): the
+// weight scales, and FP8 weights): the
 // same product as mx_gemm_a16.hip, Y = X . dequant(Wq)^T with bf16 activations and fp32
 // accumulation (gtnt.cn/news/16247 "为什么我们需要4-bit浮点量化", section 3.1: dequantize, then
 // matmul; hotelren.com/news/2192771, article "量化技术演进与微缩量化原理", section 3.2 item 3:
@@ -377,19 +377,13 @@ bool a16w_uses(const GemmArgs& a, bool w8)
     if (!(a.m > 128 && a.block == 32 && a.k % a16w::SWIN_K == 0 && (a.ldx * 2) % 16 == 0 &&
           ((uintptr_t)a.x % 16) == 0 && xspan < 0x7FFFFFFF && yspan < 0x7FFFFFFF))
         return false;
-    if (a.fmt != FMT_E8M0) return true;  // E4M3 / UE5M3: the narrow kernel is bound by dequantization
+    if (a.fmt != FMT_E8M0) return true;  // E4M3 / UE5M3: the narrow kernels are bound by dequantization
     // FP8 weights with E8M0 scales: the narrow kernel's ring is only two stages deep (64 KB
     // stages); the wide one was faster even with a last round half full (70B-FFN prefill:
-    // 855 against 883 us)
-    if (w8) return true;
-    // FP4 weights with E8M0 scales: both kernels are bound by the matrix rate, the wide one slightly faster per
-    // output (measured: 4% at m 4096, n 53248, k 16384) -- take it when its 256 x 256 tiles
-    // need at most half the rounds of one tile per CU that the 128 x 256 tiles need (at
-    // 2048 x 28672 x 8192 they need 3.5 against 7 and the narrow kernel is 5% faster)
-    constexpr int64_t CUS = 256;
-    const int64_t nt = (a.n + a16w::BN - 1) / a16w::BN;
-    const int64_t tw = ((a.m + a16w::BM - 1) / a16w::BM) * nt, tn = ((a.m + 127) / 128) * nt;
-    return 2 * ((tw + CUS - 1) / CUS) <= (tn + CUS - 1) / CUS;
+    // 855 against 883 us).  FP4 weights with E8M0 scales take the two-workgroup kernel or the
+    // 8-wave one: in cycles both beat this one (2048 x 16384 x 8192: 692 k / 780 k cycles per
+    // XCD, modelled from the measured rounds, against 814 k measured)
+    return w8;
 }
 
 hipError_t launch_gemm_a16w(const GemmArgs& a, bool w8, hipStream_t st)

@@ -107,9 +107,13 @@ hipError_t launch_gemm_a16_tiled(const GemmArgs& a, hipStream_t st);
 // the same pipelined kernel with FP8 (E4M3) weight codes, n x k bytes (same conditions)
 hipError_t launch_gemm_w8_tiled(const GemmArgs& a, hipStream_t st);
 // the large-m W4A16 / W8A16 GEMM with 128 x 64 wave tiles (E4M3 / UE5M3 weight scales and FP8
-// weights; FP4 weights with E8M0 scales where its 256 x 256 tiles fill whole rounds of the GPU)
+// weights)
 bool a16w_uses(const GemmArgs& a, bool w8);
 hipError_t launch_gemm_a16w(const GemmArgs& a, bool w8, hipStream_t st);
+// the large-m W4A16 GEMM with two 4-wave workgroups per CU (FP4 codes, E8M0 scales, more
+// 128 x 256 tiles than CUs, and the pipelined kernel's other conditions)
+bool a16p_uses(const GemmArgs& a);
+hipError_t launch_gemm_a16p(const GemmArgs& a, hipStream_t st);
 // whether the m <= 2 sweeping GEMV takes FP8 codes of this shape, and its launcher
 bool w8_uses_sweep(const GemmArgs& a);
 hipError_t launch_gemv_sweep_w8(const GemmArgs& a, hipStream_t st);
