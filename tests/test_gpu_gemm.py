@@ -386,21 +386,21 @@ def test_c4_prefill(mode, layout, c4_full):
         del y
 
 
-# The wide-tile W4A16 kernel (256 x 256 tiles, 128 x 64 per wave), which takes E4M3 / UE5M3
-# scales with m > 128 (the pipelined tests above cover it at small shapes), at a shape the small
-# ones never reach: m 1000 (4 tiles, the last ragged), n 28600 (112 tiles, the last ragged); the
-# E8M0 case runs the two-workgroup kernel (896 tiles of 128 x 256).  Sampled rows and columns.
+# The one-workgroup-per-CU W4A16 kernels at a shape the small tests never reach: m 200, n 28600
+# (E8M0: 224 tiles of 128 x 256, too few for the two-workgroup kernel -> the 8-wave 128 x 256
+# kernel; E4M3 / UE5M3: the 8-wave 256 x 256 kernel, 112 tiles), the last n-tile ragged.
+# Sampled rows and columns.
 @pytest.mark.parametrize("fmt,g", [("e8m0", 1.0), ("ue5m3", 0.37), ("e4m3", 1.0)])
 def test_gemm_a16_wide_tiles_sampled(fmt, g):
     g = float(np.float32(g))
-    m, n, k = 1000, 28600, 1024
+    m, n, k = 200, 28600, 1024
     x = synth.normal((m, k), "bf16", "gw.x", 1.0)
     w = synth.normal((n, k), "bf16", "gw.w", 0.02, 0.01, 20.0)
     wd = bf16_dev(w)
     cd, sd = mx.mx_quantize(wd, 32, fmt, g)
     del wd
     cols = np.array([0, 1, 255, 256, 9999, 28415, 28416, 28599])
-    rows = np.array([0, 1, 127, 128, 255, 256, 767, 768, 999])
+    rows = np.array([0, 1, 31, 32, 127, 128, 199])
     rc, rs = oracle.quantize(w[cols], 32, fmt, g)
     np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
     np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
@@ -412,40 +412,45 @@ def test_gemm_a16_wide_tiles_sampled(fmt, g):
                           f"wide tiles {fmt} {dt}")
 
 
-# The two-workgroup W4A16 kernel (E8M0 scales, more 128 x 256 tiles than CUs), over its three
-# tile orders: m 1000 x n 16300 (8 m-tiles, 64 n-tiles: the XCD-grouped order), m 300 x n 28600
-# (3 m-tiles, 112 n-tiles: n-tiles by XCD), m 260 x n 33000 (129 n-tiles: plain order); m and n
-# ragged in each, k from two 256-k scale windows to eight, g = 1 and g != 1, both output types,
-# and output rows with a stride beyond n (16-byte aligned: chunk epilogue; odd: element
-# epilogue) whose columns past n must stay untouched.  Sampled rows and columns: both sides of
-# every 64-row wave block, 128-column wave block and tile edge that the sample reaches.
+# The two-workgroup W4A16 kernel (E8M0 scales, more 128 x 256 tiles than CUs; 4 waves of 64 x 128)
+# over its three tile orders: m 1000 x n 16300 (the XCD-grouped order), m 300 x n 28600 (n-tiles
+# by XCD), m 260 x n 33000 (plain order); m and n ragged in each, k from two 256-k scale windows
+# to eight, g = 1 and g != 1, both output types, and output rows with a stride beyond n
+# (16-byte aligned: chunk epilogue; odd: element epilogue) whose columns past n must stay
+# untouched.  The same cases with E4M3 / UE5M3 scales run the 8-wave 256 x 256 kernel (m > 128)
+# over its tile orders.  Sampled rows and columns: both sides of every wave block and tile edge
+# that the sample reaches.
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,n,k,g,ldy_extra", [(1000, 16300, 1024, 0.37, 0), (300, 28600, 512, 1.0, 8),
                                                (260, 33000, 2048, 1.0, 3)])
-def test_gemm_a16_paired_sampled(m, n, k, g, ldy_extra):
+def test_gemm_a16_paired_sampled(m, n, k, g, ldy_extra, fmt):
     g = float(np.float32(g))
     x = synth.normal((m, k), "bf16", f"gq.x.{m}", 1.0)
     w = synth.normal((n, k), "bf16", f"gq.w.{n}", 0.02, 0.01, 20.0)
     wd = bf16_dev(w)
-    cd, sd = mx.mx_quantize(wd, 32, "e8m0", g)
+    cd, sd = mx.mx_quantize(wd, 32, fmt, g)
     del wd
     last = (n - 1) // 256 * 256
-    cols = np.unique(np.array([0, 1, 127, 128, 255, 256, 383, 384, n // 2, last - 1, last, n - 1]))
-    rows = np.unique(np.array([0, 1, 63, 64, 127, 128, 191, m // 2, m - 1]))
-    rc, rs = oracle.quantize(w[cols], 32, "e8m0", g)
+    cols = np.unique(np.array([0, 1, 63, 64, 127, 128, 255, 256, 383, 384, n // 2, last - 1, last, last + 127,
+                               last + 128, n - 1]))
+    cols = cols[cols < n]
+    rows = np.unique(np.array([0, 1, 63, 64, 127, 128, 191, 255, 256, m // 2, m - 1]))
+    rows = rows[rows < m]
+    rc, rs = oracle.quantize(w[cols], 32, fmt, g)
     np.testing.assert_array_equal(to_host_bits(cd[cols]), rc)
     np.testing.assert_array_equal(to_host_bits(sd[cols]), rs)
-    yref, aref = oracle.gemm(x[rows], rc, rs, 32, "e8m0", g, "a16")
+    yref, aref = oracle.gemm(x[rows], rc, rs, 32, fmt, g, "a16")
     xd = bf16_dev(x)
     for dt in (torch.float32, torch.bfloat16):
         if ldy_extra:
             big = torch.full((m, n + ldy_extra), float("nan"), dtype=dt, device=DEV)
             y = big[:, :n]
-            mx.mx_gemm(xd, cd, sd, 32, "e8m0", g, "a16", y=y)
+            mx.mx_gemm(xd, cd, sd, 32, fmt, g, "a16", y=y)
         else:
-            y = mx.mx_gemm(xd, cd, sd, 32, "e8m0", g, "a16", out_dtype=dt)
+            y = mx.mx_gemm(xd, cd, sd, 32, fmt, g, "a16", out_dtype=dt)
         torch.cuda.synchronize()
         assert_gemm_close(to_host_bits(y[rows][:, cols].float()), yref, aref, dt == torch.bfloat16,
-                          f"paired {m}x{n}x{k} {dt}")
+                          f"paired {fmt} {m}x{n}x{k} {dt}")
         if ldy_extra:
             assert torch.isnan(big[:, n:].float()).all()
         del y
