@@ -417,12 +417,12 @@ def test_gemm_a16_wide_tiles_sampled(fmt, g):
 # by XCD), m 260 x n 33000 (plain order); m and n ragged in each, k from two 256-k scale windows
 # to eight, g = 1 and g != 1, both output types, and output rows with a stride beyond n
 # (16-byte aligned: chunk epilogue; odd: element epilogue) whose columns past n must stay
-# untouched.  The same cases with E4M3 / UE5M3 scales run the 8-wave 256 x 256 kernel (m > 128)
-# over its tile orders.  Sampled rows and columns: both sides of every wave block and tile edge
+# untouched; m 1000 x n 20400 (640 tiles) leaves its last round a quarter full.  The same cases
+# with E4M3 / UE5M3 scales run the 8-wave 256 x 256 kernel (m > 128) over its tile orders.  Sampled rows and columns: both sides of every wave block and tile edge
 # that the sample reaches.
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,n,k,g,ldy_extra", [(1000, 16300, 1024, 0.37, 0), (300, 28600, 512, 1.0, 8),
-                                               (260, 33000, 2048, 1.0, 3)])
+                                               (260, 33000, 2048, 1.0, 3), (1000, 20400, 1024, 1.0, 8)])
 def test_gemm_a16_paired_sampled(m, n, k, g, ldy_extra, fmt):
     g = float(np.float32(g))
     x = synth.normal((m, k), "bf16", f"gq.x.{m}", 1.0)
