@@ -405,6 +405,85 @@ __global__ __launch_bounds__(THREADS) void dequantize_fp8_kernel(const uint8_t* 
     }
 }
 
+// Blocks of 8 or more: each lane takes two units of 8 consecutive elements, 64 units apart
+// (a wave covers 128 consecutive units), so that every code load of a wave reads 512
+// contiguous bytes and every store writes 1 KB (bf16) or 2 KB (fp32) contiguous.  A unit is
+// decoded by the hardware converter with its scale's power of two, then multiplied by the
+// scale's mantissa (E4M3 / UE5M3) and by g: e * 2^p is exact in fp32, so is its product with
+// the mantissa (at most 8 significant bits), and the product with g is the one fp32 rounding
+// -- the same value as the per-element form above.  A unit with a NaN code (0x7F, 0xFF) or,
+// for g != 1, an E8M0 scale above 2^118 (where e * s may leave the fp32 range before g brings
+// it back) takes the per-element form.
+template <int BLOCK, int FMT>
+__device__ __forceinline__ void dq8_unit(const u32x2 cv, uint32_t sb, float gf, double g, float (&v)[8])
+{
+    // bit 7 of a byte of (b & 0x7F) + 1 is set exactly when b & 0x7F == 0x7F, with no carry
+    // into the next byte
+    const uint32_t nanb = (((cv.x & 0x7F7F7F7Fu) + 0x01010101u) | ((cv.y & 0x7F7F7F7Fu) + 0x01010101u)) & 0x80808080u;
+    if (nanb == 0 && !(FMT == FMT_E8M0 && sb > 245u && gf != 1.0f)) {
+        const WScale<FMT> ws = wscale<FMT>(sb);
+        const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cv.x, ws.pow2, false);
+        const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cv.x, ws.pow2, true);
+        const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cv.y, ws.pow2, false);
+        const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cv.y, ws.pow2, true);
+        v[0] = (a.x * ws.mant) * gf; v[1] = (a.y * ws.mant) * gf;
+        v[2] = (b.x * ws.mant) * gf; v[3] = (b.y * ws.mant) * gf;
+        v[4] = (c.x * ws.mant) * gf; v[5] = (c.y * ws.mant) * gf;
+        v[6] = (d.x * ws.mant) * gf; v[7] = (d.y * ws.mant) * gf;
+    } else {
+        const bool wide = FMT == FMT_E8M0 && sb > 245u;
+        const float sf = scale_value_f32<FMT>(sb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t cb = ((e < 4 ? cv.x : cv.y) >> (8 * (e & 3))) & 0xFFu;
+            v[e] = wide ? dq_value(cb, scale_value_f64<FMT>(sb) * g) : dq_value_f32(cb, sf, gf);
+        }
+    }
+}
+
+template <int BLOCK, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(THREADS) void dequantize_fp8_u2_kernel(const uint8_t* __restrict__ codes,
+                                                                    const uint8_t* __restrict__ scales,
+                                                                    FastDiv upr_div, uint32_t upr, uint32_t total,
+                                                                    int64_t k, double g, uint8_t* __restrict__ y,
+                                                                    int64_t ldy_bytes)
+{
+    static_assert(BLOCK >= 8, "one scale per unit");
+    const uint32_t t = blockIdx.x * THREADS + threadIdx.x;
+    const uint32_t u0 = (t >> 6) * 128 + (t & 63);           // units u0 and u0 + 64
+    const float gf = (float)g;
+    u32x2 cv[2];
+    uint32_t sb[2], row[2], c8[2];
+    bool ok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // all loads before any arithmetic
+        const uint32_t u = u0 + 64 * h;
+        ok[h] = u < total;
+        const uint32_t uu = ok[h] ? u : 0u;
+        row[h] = upr_div.div(uu);
+        c8[h] = uu - row[h] * upr;
+        cv[h] = *reinterpret_cast<const u32x2*>(codes + (int64_t)row[h] * k + (int64_t)c8[h] * 8);
+        sb[h] = scales[(int64_t)row[h] * (k / BLOCK) + (c8[h] * 8) / BLOCK];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (!ok[h]) continue;
+        float v[8];
+        dq8_unit<BLOCK, FMT>(cv[h], sb[h], gf, g, v);
+        if constexpr (OUT_BF16) {
+            uint32_t o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2 * j], (__bf16)v[2 * j + 1]});
+            *reinterpret_cast<u32x4*>(y + (int64_t)row[h] * ldy_bytes + (int64_t)c8[h] * 16) = u32x4{o[0], o[1], o[2], o[3]};
+        } else {
+            u32x4* p = reinterpret_cast<u32x4*>(y + (int64_t)row[h] * ldy_bytes + (int64_t)c8[h] * 32);
+            p[0] = u32x4{f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])};
+            p[1] = u32x4{f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])};
+        }
+    }
+}
+
 template <int FMT, bool OUT_BF16>
 __global__ __launch_bounds__(THREADS) void dequantize_fp8_generic_kernel(const uint8_t* __restrict__ codes,
                                                                          const uint8_t* __restrict__ scales,
@@ -612,10 +691,26 @@ static hipError_t launch_dq8(const DequantArgs& a, hipStream_t st)
                            static_cast<uint8_t*>(a.y), a.ldy);
         return hipGetLastError();
     }
+    const int64_t ldyb = a.ldy * (OUT_BF16 ? 2 : 4);
+    if (a.block >= 8) {
+        const uint32_t upr = (uint32_t)(a.k / 8), total = (uint32_t)(a.rows * upr);
+        const FastDiv fd = FastDiv::make(upr);
+        const dim3 grid((total + 2 * f8::THREADS - 1) / (2 * f8::THREADS));  // two units per lane
+#define MXDU(B)                                                                                              \
+    case B:                                                                                                  \
+        hipLaunchKernelGGL((f8::dequantize_fp8_u2_kernel<B, FMT, OUT_BF16>), grid, dim3(f8::THREADS), 0, st,  \
+                           a.codes, a.scales, fd, upr, total, a.k, a.g, static_cast<uint8_t*>(a.y), ldyb);  \
+        break;
+        switch (a.block) {
+            MXDU(8) MXDU(16) MXDU(32) MXDU(64) MXDU(128) MXDU(256)
+            default: return hipErrorInvalidValue;
+        }
+#undef MXDU
+        return hipGetLastError();
+    }
     const uint32_t upr = (uint32_t)(a.k / 8), total = (uint32_t)(a.rows * upr);
     const FastDiv fd = FastDiv::make(upr);
     const dim3 grid((total + f8::THREADS - 1) / f8::THREADS);
-    const int64_t ldyb = a.ldy * (OUT_BF16 ? 2 : 4);
 #define MXD8(B)                                                                                              \
     case B:                                                                                                  \
         hipLaunchKernelGGL((f8::dequantize_fp8_kernel<B, FMT, OUT_BF16>), grid, dim3(f8::THREADS), 0, st,   \
