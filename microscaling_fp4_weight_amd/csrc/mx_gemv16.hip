@@ -8,14 +8,15 @@
 //
 // Work is split in units of 16 weight rows (16 x 2 KB of codes, contiguous): workgroup b takes
 // units b, b + G, ..., so at any time the GPU streams one contiguous window of the weight.  Each
-// of the 8 waves of a workgroup owns one 512-k slice of every row and keeps the activations of
+// of the 16 waves of a workgroup owns one 256-k slice of every row and keeps the activations of
 // that slice in registers for the whole launch, as the B operand of bf16 MFMA 16x16x32 (X rows
 // are the 16 columns; rows past m are zero).  A unit's codes reach LDS by LDS-DMA in pieces of
-// 4 rows x 256 bytes (whole cache lines; the 16-byte chunks of each row permuted by XOR with
+// 8 rows x 128 bytes (whole cache lines; the 16-byte chunks of each row permuted by XOR with
 // the row's low bits), and each lane reads back the 16 bytes of its MFMA A-operand row (16
 // weight rows per MFMA) without bank conflicts; only the wave itself reads what it loaded, so
-// the loop has no barrier.  The next unit's codes and scales are in flight while a unit is
-// computed.  The waves' partial sums of each unit meet in LDS at the end, in a fixed order.
+// the loop has no barrier.  All of a workgroup's units are in flight from the start; each is
+// computed as soon as it has landed.  The waves' partial sums of each unit meet in LDS at the
+// end, in a fixed order.
 #include "mx_device.h"
 #include "mx_internal.h"
 #include "mx_wdeq.h"
@@ -155,7 +156,6 @@ __global__ __launch_bounds__(THREADS) void gemv16_kernel(const GemmArgs a)
         }
     };
 
-    issue(0, 0);
     // this wave's X slice as B operands: xb[jp][4 t + d] = dword d of X row r at
     // k = kw0 + 32 (4 jp + g) + 8 t.  Loaded as whole 64-byte pieces of a row (load t' of jp:
     // lane (g, r) takes bytes 16 g of the piece of 32-k chunk 4 jp + t'), which leaves piece t'
@@ -173,9 +173,11 @@ __global__ __launch_bounds__(THREADS) void gemv16_kernel(const GemmArgs a)
 #pragma unroll
             for (int d = 0; d < 4; ++d) xb[jp][4 * t + d] = v[t][d];
     }
-    // the other unit slots of the workgroup (all in flight from here on)
+    // then every unit slot of the workgroup, all in flight from here on (the X loads go first:
+    // they hit in L2 and are back before the first unit's codes; issued after the first unit,
+    // or later, they delayed the first MFMA)
 #pragma unroll
-    for (int i = 1; i < DEPTH; ++i) issue(i, i);
+    for (int i = 0; i < DEPTH; ++i) issue(i, i);
     // the scale loads were issued before everything else: wait for them alone, then share
     if (sc_wave) wait_vmcnt<DEPTH * NDMA + 4 * JP>();
     // a barrier without the memory fence of __syncthreads, which would also wait for the code
