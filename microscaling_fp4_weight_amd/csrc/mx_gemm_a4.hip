@@ -190,7 +190,7 @@ __device__ __forceinline__ void read_scales(const uint8_t* st, uint32_t offSA, u
     __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ - 1, ID)
 
 template <bool OUT_BF16, bool W_TILED, int NJ>
-__global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a, uint32_t tile_base)
+__device__ __forceinline__ void gemm_a4_tile(const GemmArgs& a, uint32_t tile_base, uint32_t bid)
 {
     using C = Cfg<NJ>;
     constexpr int BN = C::BN;
@@ -203,11 +203,12 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a, uint
     const uint32_t K = (uint32_t)a.k;
 
     // tile mapping over full 256 x 256 tiles: with the n-tile count a multiple of 8, XCD x
-    // (= tile % 8) takes n-tiles x, x+8, ... and, for each, every m-tile in turn.  A half-tile
-    // launch (NJ = 1) covers full tiles tile_base.. with two workgroups each.
+    // (= tile % 8) takes n-tiles x, x+8, ... and, for each, every m-tile in turn.  The half-tile
+    // part (NJ = 1) covers tiles tile_base.. with two workgroups each (bid: the workgroup's index
+    // within its part).
     const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + 255) / 256);
-    const uint32_t tile = tile_base + (NJ == 2 ? blockIdx.x : blockIdx.x >> 1);
-    const uint32_t whalf = NJ == 2 ? 0u : (blockIdx.x & 1u);
+    const uint32_t tile = tile_base + (NJ == 2 ? bid : bid >> 1);
+    const uint32_t whalf = NJ == 2 ? 0u : (bid & 1u);
     uint32_t mt, nt;
     if ((NT & 7) == 0) {
         const uint32_t x = tile & 7, local = tile >> 3;
@@ -381,24 +382,34 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_kernel(const GemmArgs a, uint
     }
 }
 
+// Full tiles 0 .. full - 1 (workgroups 0 .. full - 1), then the remaining tiles as half tiles,
+// two workgroups each, in one launch: half tiles start on CUs as the last full tiles finish.
+template <bool OUT_BF16, bool W_TILED>
+__global__ __launch_bounds__(THREADS) void gemm_a4_merged_kernel(const GemmArgs a, uint32_t full)
+{
+    if (blockIdx.x < full) gemm_a4_tile<OUT_BF16, W_TILED, 2>(a, 0u, blockIdx.x);
+    else gemm_a4_tile<OUT_BF16, W_TILED, 1>(a, full, blockIdx.x - full);
+}
+
 }  // namespace a4
 
-template <bool OUT_BF16, bool W_TILED, int NJ>
-static hipError_t launch_part(const GemmArgs& a, uint32_t tile_base, unsigned groups, hipStream_t st)
+template <bool OUT_BF16, bool W_TILED>
+static hipError_t launch_merged(const GemmArgs& a, uint32_t full, unsigned groups, hipStream_t st)
 {
     // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
     // (thread-safe function-local static initialisation)
-    static const hipError_t attr = hipFuncSetAttribute((const void*)a4::gemm_a4_kernel<OUT_BF16, W_TILED, NJ>,
+    static const hipError_t attr = hipFuncSetAttribute((const void*)a4::gemm_a4_merged_kernel<OUT_BF16, W_TILED>,
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       a4::Cfg<NJ>::LDS_BYTES);
+                                                       a4::Cfg<2>::LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((a4::gemm_a4_kernel<OUT_BF16, W_TILED, NJ>), dim3(groups), dim3(a4::THREADS),
-                       a4::Cfg<NJ>::LDS_BYTES, st, a, tile_base);
+    hipLaunchKernelGGL((a4::gemm_a4_merged_kernel<OUT_BF16, W_TILED>), dim3(groups), dim3(a4::THREADS),
+                       a4::Cfg<2>::LDS_BYTES, st, a, full);
     return hipGetLastError();
 }
 
 // Full 256 x 256 tiles run in whole rounds of kCUs workgroups; when the last round would be at
-// most half full, its tiles run instead as twice as many 256 x 128 half tiles, which fill it.
+// most half full, its tiles run instead as twice as many 256 x 128 half tiles, which fill it,
+// in the same launch (as two launches, the half tiles waited for the slowest full tile).
 constexpr unsigned kCUs = 256;
 
 template <bool OUT_BF16, bool W_TILED>
@@ -407,12 +418,7 @@ static hipError_t launch_tiled(const GemmArgs& a, hipStream_t st)
     const unsigned tiles = (unsigned)(((a.m + a4::BM - 1) / a4::BM) * ((a.n + 255) / 256));
     const unsigned rem = tiles % kCUs;
     const unsigned full = (rem != 0 && rem <= kCUs / 2) ? tiles - rem : tiles;
-    if (full) {
-        const hipError_t e = launch_part<OUT_BF16, W_TILED, 2>(a, 0u, full, st);
-        if (e != hipSuccess) return e;
-    }
-    if (full < tiles) return launch_part<OUT_BF16, W_TILED, 1>(a, full, 2 * (tiles - full), st);
-    return hipSuccess;
+    return launch_merged<OUT_BF16, W_TILED>(a, full, full + 2 * (tiles - full), st);
 }
 
 bool a4_uses_mfma(const GemmArgs& a)
