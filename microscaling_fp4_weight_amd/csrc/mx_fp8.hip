@@ -500,15 +500,15 @@ __global__ __launch_bounds__(THREADS) void dequantize_fp8_generic_kernel(const u
 }
 
 // ---------------------------------------------------------------------------------------
-// W8A16 GEMM / GEMV on bf16 16x16x32 matrix cores.  A workgroup (4 waves) owns 16 weight rows
-// (output columns) and 16 MT activation rows; its waves take every fourth 128-k window.  In a
-// window a lane holds weight row lane % 16 and the 32 consecutive k 32 (lane / 16) .. +31
-// (two 16-byte code loads: the four lanes of a row read its 128 bytes), dequantizes them to
-// bf16 in registers and feeds four MFMAs with the activations of the same k: MFMA i takes
-// k 32 (lane / 16) + 8 i .. +7 from every lane, the same permutation of k for both operands,
-// which leaves each dot product unchanged.  The next window's codes and scales are loaded
-// before the current window is computed.  The four waves' partial sums meet in LDS.
-// Requires k % 32 == 0.
+// W8A16 GEMM / GEMV on bf16 16x16x32 matrix cores.  A workgroup (NW waves) owns NG groups of 16
+// weight rows (output columns) and 16 MT activation rows; its waves take every NW-th 128-k
+// window.  In a window a lane holds, per row group, weight row lane % 16 and the 32 consecutive
+// k 32 (lane / 16) .. +31 (two 16-byte code loads: the four lanes of a row read its 128 bytes),
+// dequantizes them to bf16 in registers and feeds four MFMAs with the activations of the same
+// k: MFMA i takes k 32 (lane / 16) + 8 i .. +7 from every lane, the same permutation of k for
+// both operands, which leaves each dot product unchanged.  The activations of a window are
+// loaded once for all NG row groups.  The next window's codes and scales are loaded before the
+// current window is computed.  The waves' partial sums meet in LDS.  Requires k % 32 == 0.
 // ---------------------------------------------------------------------------------------
 template <int BLOCK>
 __device__ __forceinline__ uint64_t lane_scales(rsrc_t r, uint32_t off)
@@ -519,43 +519,53 @@ __device__ __forceinline__ uint64_t lane_scales(rsrc_t r, uint32_t off)
     else return bload64(r, off);
 }
 
-template <int BLOCK, int FMT, int MT, bool OUT_BF16>
-__global__ __launch_bounds__(THREADS) void gemm_w8_kernel(const W8Args a)
+template <int BLOCK, int FMT, int MT, bool OUT_BF16, int NG = 1, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_w8_kernel(const W8Args a)
 {
-    __shared__ f32x4 red[4][MT][64];
+    __shared__ f32x4 red[NW][NG][MT][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t r16 = lane & 15, q = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16, m0 = (int64_t)blockIdx.y * 16 * MT;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NG, m0 = (int64_t)blockIdx.y * 16 * MT;
     const uint32_t K = (uint32_t)a.k;
-    const uint32_t nrows = (uint32_t)(a.n - n0 < 16 ? a.n - n0 : 16);
+    const uint32_t nrows = (uint32_t)(a.n - n0 < 16 * NG ? a.n - n0 : 16 * NG);
     const uint32_t mrows = (uint32_t)(a.m - m0 < 16 * MT ? a.m - m0 : 16 * MT);
     const rsrc_t wc = make_rsrc(a.wc + n0 * a.k, nrows * K);
     const rsrc_t ws = make_rsrc(a.ws + n0 * (a.k / BLOCK), nrows * (K / BLOCK));
     const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, (uint32_t)(((int64_t)(mrows - 1) * a.ldx + a.k) * 2));
     const uint32_t nwin = (K + 127) / 128;
 
-    f32x4 acc[MT];
+    f32x4 acc[NG][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[gq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load_w = [&](uint32_t win, uint32_t (&cw)[8], uint64_t& sb) {
+    auto load_w = [&](uint32_t win, uint32_t (&cw)[NG][8], uint64_t (&sb)[NG]) {
         const uint32_t kc = win * 128 + 32 * q;
-        const bool ok = kc < K && r16 < nrows;
-        const uint32_t off = ok ? r16 * K + kc : kOOB;
-        const u32x4 c0 = bload128(wc, off), c1 = bload128(wc, ok ? off + 16 : kOOB);
-        cw[0] = c0.x; cw[1] = c0.y; cw[2] = c0.z; cw[3] = c0.w;
-        cw[4] = c1.x; cw[5] = c1.y; cw[6] = c1.z; cw[7] = c1.w;
-        sb = lane_scales<BLOCK>(ws, ok ? r16 * (K / BLOCK) + kc / BLOCK : kOOB);
+#pragma unroll
+        for (int gq = 0; gq < NG; ++gq) {
+            const uint32_t row = 16 * gq + r16;
+            const bool ok = kc < K && row < nrows;
+            const uint32_t off = ok ? row * K + kc : kOOB;
+            const u32x4 c0 = bload128(wc, off), c1 = bload128(wc, ok ? off + 16 : kOOB);
+            cw[gq][0] = c0.x; cw[gq][1] = c0.y; cw[gq][2] = c0.z; cw[gq][3] = c0.w;
+            cw[gq][4] = c1.x; cw[gq][5] = c1.y; cw[gq][6] = c1.z; cw[gq][7] = c1.w;
+            sb[gq] = lane_scales<BLOCK>(ws, ok ? row * (K / BLOCK) + kc / BLOCK : kOOB);
+        }
     };
 
-    uint32_t cw[8];
-    uint64_t sb = 0;
+    uint32_t cw[NG][8];
+    uint64_t sb[NG];
+#pragma unroll
+    for (int gq = 0; gq < NG; ++gq) sb[gq] = 0;
     uint32_t win = (uint32_t)wave;
     if (win < nwin) load_w(win, cw, sb);
-    for (; win < nwin; win += 4) {
-        uint32_t cn[8];
-        uint64_t sn = 0;
-        if (win + 4 < nwin) load_w(win + 4, cn, sn);
+    for (; win < nwin; win += NW) {
+        uint32_t cn[NG][8];
+        uint64_t sn[NG];
+#pragma unroll
+        for (int gq = 0; gq < NG; ++gq) sn[gq] = 0;
+        if (win + NW < nwin) load_w(win + NW, cn, sn);
         const uint32_t kc = win * 128 + 32 * q;
         u32x4 xa[MT][4];
 #pragma unroll
@@ -566,33 +576,45 @@ __global__ __launch_bounds__(THREADS) void gemm_w8_kernel(const W8Args a)
             for (int i = 0; i < 4; ++i)
                 xa[t][i] = bload128(xr, ok ? (xrow * (uint32_t)a.ldx + kc + 8 * i) * 2 : kOOB);
         }
-        uint32_t wb[16];
-        dequant_w8<BLOCK, FMT>(cw, sb, wb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 bv = {wb[4 * i], wb[4 * i + 1], wb[4 * i + 2], wb[4 * i + 3]};
+        for (int gq = 0; gq < NG; ++gq) {
+            uint32_t wb[16];
+            dequant_w8<BLOCK, FMT>(cw[gq], sb[gq], wb);
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[t][i]),
-                                                                 __builtin_bit_cast(bf16x8, bv), acc[t], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 bv = {wb[4 * i], wb[4 * i + 1], wb[4 * i + 2], wb[4 * i + 3]};
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+                    acc[gq][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[t][i]),
+                                                                         __builtin_bit_cast(bf16x8, bv), acc[gq][t], 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cw[j] = cn[j];
-        sb = sn;
+        for (int gq = 0; gq < NG; ++gq) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cw[gq][j] = cn[gq][j];
+            sb[gq] = sn[gq];
+        }
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+    for (int gq = 0; gq < NG; ++gq)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) red[wave][gq][t][lane] = acc[gq][t];
     __syncthreads();
-    // wave w adds the four partials of m-subtiles t = w, w + 4, ... and stores them:
-    // lane holds C[4 (lane / 16) + i][lane % 16], rows m, columns n
+    // wave w adds the four partials of (row group, m-subtile) pairs w, w + 4, ... and stores
+    // them: lane holds C[4 (lane / 16) + i][lane % 16], rows m, columns n
     constexpr uint32_t ESZ = OUT_BF16 ? 2 : 4;
     const rsrc_t yr = make_rsrc(static_cast<uint8_t*>(a.y) + (m0 * a.ldy + n0) * ESZ, 0x7FFFFFFFu);
-    for (int t = wave; t < MT; t += 4) {
-        const f32x4 s = red[0][t][lane] + red[1][t][lane] + red[2][t][lane] + red[3][t][lane];
+    for (int pr = wave; pr < NG * MT; pr += NW) {
+        const int gq = pr / MT, t = pr % MT;
+        f32x4 s = red[0][gq][t][lane];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) s += red[v][gq][t][lane];
+        const uint32_t nn = 16 * gq + r16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t mm = 16 * t + 4 * q + i;
-            const uint32_t off = (mm < mrows && r16 < nrows) ? (mm * (uint32_t)a.ldy + r16) * ESZ : kOOB;
+            const uint32_t off = (mm < mrows && nn < nrows) ? (mm * (uint32_t)a.ldy + nn) * ESZ : kOOB;
             const float v = s[i] * (float)a.g;
             if constexpr (OUT_BF16) bstore16(yr, off, __builtin_bit_cast(uint16_t, (__bf16)v));
             else bstore32(yr, off, f2u(v));
@@ -774,12 +796,19 @@ static hipError_t launch_w8(const W8Args& a, hipStream_t st)
     ga.ldy = a.ldy;
     if (w8_uses_sweep(ga)) return launch_gemv_sweep_w8(ga, st);
     if (a.m > 16 && w8_prefers_tiled(a) && a16_uses_tiled(ga)) return launch_gemm_w8_tiled(ga, st);
+    // m <= 16: 8 waves per workgroup and as many 16-row groups per workgroup (1, 2 or 4) as keep
+    // at least 224 workgroups, which share each activation load among more weight rows
+    // (n 14336, m 16: 4 groups, 19.5 against 30.8 us with one group of 4 waves; n 4096: one
+    // group, 9.5 against 10.0 us)
     const bool small = a.m <= 16;
-    const dim3 grid((unsigned)((a.n + 15) / 16), (unsigned)((a.m + (small ? 16 : 64) - 1) / (small ? 16 : 64)));
+    const int ng = !small ? 1 : (a.n + 63) / 64 >= 224 ? 4 : (a.n + 31) / 32 >= 224 ? 2 : 1;
+    const dim3 grid((unsigned)((a.n + 16 * ng - 1) / (16 * ng)), (unsigned)((a.m + (small ? 16 : 64) - 1) / (small ? 16 : 64)));
 #define MXW8(B)                                                                                                  \
     case B:                                                                                                      \
-        if (small) hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 1, OUT_BF16>), grid, dim3(f8::THREADS), 0, st, a); \
-        else hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 4, OUT_BF16>), grid, dim3(f8::THREADS), 0, st, a);       \
+        if (!small) hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 4, OUT_BF16, 1, 4>), grid, dim3(256), 0, st, a);   \
+        else if (ng == 4) hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 1, OUT_BF16, 4, 8>), grid, dim3(512), 0, st, a); \
+        else if (ng == 2) hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 1, OUT_BF16, 2, 8>), grid, dim3(512), 0, st, a); \
+        else hipLaunchKernelGGL((f8::gemm_w8_kernel<B, FMT, 1, OUT_BF16, 1, 8>), grid, dim3(512), 0, st, a);          \
         break;
     switch (a.block) {
         MXW8(4) MXW8(8) MXW8(16) MXW8(32) MXW8(64) MXW8(128) MXW8(256)

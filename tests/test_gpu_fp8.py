@@ -124,6 +124,25 @@ def test_gemm_fp8(m, fmt):
         assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 m={m} {fmt} {dt}")
 
 
+# The decode kernel with 2 or 4 groups of 16 weight rows per workgroup (taken for m <= 16 once n
+# keeps at least 224 workgroups): n 7200 (2 groups, 225 workgroups), n 14337 (4 groups, the last
+# workgroup holding a single row); a partial last 128-k window, m 3 and 16, g != 1.  Every output.
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k,g", [(3, 7200, 1280, 1.0), (16, 7200, 4096, 0.37), (16, 14337, 1280, 1.0),
+                                     (5, 14337, 1280, 0.37)])
+def test_gemm_fp8_row_groups(m, n, k, g, fmt):
+    g = float(np.float32(g))
+    x = synth.normal((m, k), "bf16", f"g8g.x.{m}", 1.0)
+    w = synth.normal((n, k), "bf16", f"g8g.w.{n}.{k}", 0.02 / g, 0.01, 20.0)
+    rc, rs = oracle.quantize_fp8(w, 32, fmt, g)
+    cd, sd = torch.from_numpy(rc).to(DEV), torch.from_numpy(rs).to(DEV)
+    yref, aref = oracle.gemm_fp8(x, rc, rs, 32, fmt, g)
+    for dt in (torch.float32, torch.bfloat16):
+        y = mx.mx_gemm_fp8(bf16_dev(x), cd, sd, 32, fmt, g, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16, f"w8 groups {m}x{n}x{k} {fmt} {dt}")
+
+
 @pytest.mark.parametrize("block", [4, 8, 16, 64, 128, 256])
 def test_gemm_fp8_blocks_tail_and_scale(block):
     # k = 1280 (a partial last 128-k window), ragged n, per-tensor g
