@@ -492,6 +492,39 @@ def test_gemm_a16_split_k(m, n, k, g, ldy_extra, fmt):
         np.testing.assert_array_equal(outs[0], outs[1])  # the same pieces, added in the same order
 
 
+def test_gemm_a16_split_k_graph_replay():
+    """The split schedule (a fill kernel zeroes the tile counters, then the split product)
+    captured in a HIP graph: every replay, with other work and new activations in between,
+    gives the eager call's bits."""
+    m, n, k, fmt = 200, 1000, 8192, "ue5m3"
+    need = mx.mx_gemm_workspace_size(m, n, k, 32, "a16")
+    assert need > 0
+    w = synth.normal((n, k), "bf16", "skg.w", 0.02, 0.01, 20.0)
+    wd = bf16_dev(w)
+    cd, sd = mx.mx_quantize(wd, 32, fmt)
+    xs = [bf16_dev(synth.normal((m, k), "bf16", f"skg.x.{i}", 1.0)) for i in range(3)]
+    x = xs[0].clone()
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mx.mx_gemm(x, cd, sd, 32, fmt, 1.0, "a16", y=y, workspace=ws)  # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mx.mx_gemm(x, cd, sd, 32, fmt, 1.0, "a16", y=y, workspace=ws)
+    for rep in range(6):
+        xi = xs[rep % 3]
+        ref = mx.mx_gemm(xi, cd, sd, 32, fmt, 1.0, "a16", workspace=torch.empty(need, dtype=torch.uint8, device=DEV))
+        x.copy_(xi)
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_host_bits(y), to_host_bits(ref), err_msg=f"replay {rep}")
+    del graph
+
+
 # activation rows of the 405B-FFN products: one in each 256-row m-tile for m = 4096
 C5_ROWS = {1: [0], 256: [0, 85, 170, 255], 4096: [256 * i + (97 * i) % 256 for i in range(15)] + [4095]}
 
