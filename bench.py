@@ -783,8 +783,7 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     M, N, K = 2048, 28672, 8192
     flops = 2 * M * N * K
     y = torch.empty((M, N), dtype=bf, device=dev)
-    ws = torch.empty(max(mx.mx_gemm_workspace_size(M, N, K, 32, md) for md in ("a4", "a16")), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(mx.mx_gemm_workspace_size(M, N, K, 32, "a4"), dtype=torch.uint8, device=dev)
     for mode, layout, peak in (("a16", "rowmajor", PEAK_BF16), ("a4", "rowmajor", PEAK_FP4),
                                ("a4", "tiled", PEAK_FP4)):
         sc = s4t if layout == "tiled" else s4
@@ -835,9 +834,7 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
     for m in (1, 256, 4096):
         x = dev_bf16(synth.c5_x(m))
         y = torch.empty((m, N), dtype=bf, device=dev)
-        # the optional W4A16 workspace (the k-split schedule at m = 256), allocated once
-        ws = torch.empty(mx.mx_gemm_workspace_size(m, N, K, 32, "a16"), dtype=torch.uint8, device=dev)
-        fn = lambda: mx.mx_gemm(x, c5, s5, 32, "ue5m3", g, "a16", y=y, workspace=ws)
+        fn = lambda: mx.mx_gemm(x, c5, s5, 32, "ue5m3", g, "a16", y=y)
         time_launches(torch, stream, [fn])
         ts = time_launches(torch, stream, [fn], reps=3)
         t = sorted(ts)[1]
@@ -850,7 +847,7 @@ def measure_rows(mx, L, torch, np, synth, dev, stream):
             ent.update({"frac_peak_bf16": round(tf * 1e12 / PEAK_BF16, 4)})
         rows[f"gemm_a16.ue5m3.g.m{m}.n{N}.k{K}"] = ent
         log(f"C5 m={m}: {t:.3f} ms")
-        del x, y, ws
+        del x, y
     del c5, s5
     torch.cuda.empty_cache()
     return rows

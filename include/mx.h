@@ -238,15 +238,10 @@ typedef enum { MX_LAYER_QKV = 0, MX_LAYER_FFN_GATE_UP = 1, MX_LAYER_OUTPUT = 2 }
 int mx_layer_block_size(mx_layer_kind kind);
 
 /*
- * mx_gemm_workspace_size -- bytes of device workspace mx_gemm uses for this shape and mode
+ * mx_gemm_workspace_size -- bytes of device workspace mx_gemm needs for this shape and mode
  * (0 when none).  MX_A4 needs room for the quantized activations: m*k/2 code bytes and
  * mx_scale_bytes(m, k, 32, MX_LAYOUT_TILED) scale bytes, each rounded up to 256 bytes.
- * MX_A16 takes an optional workspace (block 32, m > 128, k % 512 == 0, fewer 256 x 256
- * output tiles than the GPU has CUs and k long enough): the product is then split along k
- * over all CUs, each output tile's pieces added in a fixed order (results reproducible bit
- * for bit; they differ from the unsplit order within the accuracy bound below).  Its size is
- * 4 bytes per output tile rounded up to 256, plus 512 KB per workgroup of the split (at most
- * 256 workgroups, 128 MB).  Returns 0 for arguments mx_gemm would reject.
+ * Returns 0 for arguments mx_gemm would reject.
  */
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode);
 
@@ -266,16 +261,13 @@ size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act
  *               and the product runs on the block-scaled FP4 matrix cores.  Requires
  *               fmt == MX_SCALE_E8M0 and block == 32 (MX_ERR_UNSUPPORTED otherwise).
  *  y          : output, m x n, element type y_type, row stride ld_y >= n.
- *  workspace  : device buffer of at least mx_gemm_workspace_size(...) bytes, 16-byte aligned
- *               (may be NULL when that is 0; in MX_A16 mode it is optional: NULL or smaller
- *               runs the product unsplit); owned by the caller, contents on return unspecified.
- *               Calls that share a workspace must not overlap.
+ *  workspace  : device buffer of at least mx_gemm_workspace_size(...) bytes (may be NULL
+ *               when that is 0); owned by the caller, contents on return unspecified.
  * The weight's per-tensor scale is applied to the fp32 accumulator.  Accuracy: for each
  * output, |Y - Y_exact| <= 2e-5 * sum_k |Xhat_k * What_k| before the output rounding
  * (bf16 output adds at most half a bf16 ulp).
- * Errors: as for mx_quantize, plus MX_ERR_INVALID_ARG when ld_y < n or the MX_A4 workspace is
- * smaller than required, MX_ERR_ALIGNMENT for a workspace in use that is not 16-byte aligned,
- * and MX_ERR_UNSUPPORTED as above.
+ * Errors: as for mx_quantize, plus MX_ERR_INVALID_ARG when ld_y < n or the workspace is
+ * smaller than required, and MX_ERR_UNSUPPORTED as above.
  */
 mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
                   const uint8_t* w_codes, const uint8_t* w_scales, int block, mx_scale_fmt fmt,
@@ -293,7 +285,7 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
  *  Arguments, results and errors as mx_gemm (the same kernels run), plus MX_ERR_TOO_LARGE when
  *  mx_gemm_workspace_size(m, n, k, block, mode) exceeds MX_GEMM_STATIC_SCRATCH_BYTES (W4A4 with
  *  m * k above about 6.3e7), checked on the host before anything is launched.  W4A16 calls use
- *  no scratch (and so run unsplit along k).
+ *  no scratch.
  *  All calls on one GPU share that GPU's buffer: two W4A4 calls that may run at the same time
  *  on one GPU (different streams without ordering between them) race on it and give wrong
  *  results.  Calls ordered on one stream are safe; each call writes all the scratch it reads.

@@ -356,10 +356,7 @@ def mx_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, bloc
             tensor_scale: float = 1.0, mode: str = "a16", out_dtype: torch.dtype = torch.bfloat16,
             layout: str = "rowmajor", y: torch.Tensor | None = None,
             workspace: torch.Tensor | None = None, stream=None):
-    """Y = X . dequant(Wq)^T.  x: m x k bf16; w_codes: n x k/2; w_scales: n x k/block.
-    workspace: mode "a4" needs mx_gemm_workspace_size bytes; for "a16" it is optional (a k-split
-    schedule for products with few output tiles uses it when it is large enough; an empty
-    tensor runs without).  Allocated here when not given."""
+    """Y = X . dequant(Wq)^T.  x: m x k bf16; w_codes: n x k/2; w_scales: n x k/block."""
     m, k, ldx = _rows_ld(x, "x")
     _need_dtype(x, "x", (torch.bfloat16,))
     if w_codes.dim() != 2 or w_codes.size(1) != k // 2:
@@ -375,7 +372,7 @@ def mx_gemm(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, bloc
     need = mx_gemm_workspace_size(m, n, k, block, mode)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    if workspace is not None and mode != "a16":
+    if workspace is not None:
         _need_bytes(workspace, "workspace", need)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _need_gpu(x=x, w_codes=w_codes, w_scales=w_scales, y=y, workspace=workspace)

@@ -372,10 +372,8 @@ int mx_use_fp8(double sigma)
 size_t mx_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int block, mx_act_mode mode)
 {
     if (m < 0 || n < 0 || k < 0 || (k & 1) || !valid_block(block) || k % block != 0) return 0;
-    if (block != 32) return 0;
-    // W4A16: optional, for the k-split schedule of products with few output tiles
-    if (mode == MX_A16) return mxk::a16w_split_workspace(m, n, k);
     if (mode != MX_A4) return 0;
+    if (block != 32) return 0;
     // activation scales in the tiled layout (never smaller than row-major ones)
     return round256((size_t)m * (size_t)(k / 2)) + round256((size_t)mxk::tiled_scale_bytes(m, k));
 }
@@ -402,10 +400,8 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y))
         return MX_ERR_ALIGNMENT;
     const size_t need = mx_gemm_workspace_size(m, n, k, block, mode);
-    // W4A4 requires its workspace; W4A16 uses one when it is given and large enough
-    const bool use_ws = need && workspace && workspace_bytes >= need;
-    if (mode == MX_A4 && need && !use_ws) return MX_ERR_INVALID_ARG;
-    if (use_ws && !aligned16(workspace)) return MX_ERR_ALIGNMENT;
+    if (workspace_bytes < need || (need && !workspace)) return MX_ERR_INVALID_ARG;
+    if (need && !aligned16(workspace)) return MX_ERR_ALIGNMENT;
     if (k > kMaxGemmK) return MX_ERR_UNSUPPORTED;
 
     mxk::GemmArgs a{};
@@ -426,7 +422,6 @@ mx_status mx_gemm(const void* x, int64_t m, int64_t n, int64_t k, int64_t ld_x,
     a.ws_pre = layout == MX_LAYOUT_PRESHUFFLED;
     a.xq_codes = nullptr;
     a.xq_scales = nullptr;
-    a.a16_ws = mode == MX_A16 && use_ws ? static_cast<uint8_t*>(workspace) : nullptr;
     // weight scales in the tiled layout are read by the W4A4 matrix-core kernel only
     const bool mfma_a4 = mode == MX_A4 && mxk::a4_uses_mfma(a);
     if (a.ws_tiled && !mfma_a4) return MX_ERR_UNSUPPORTED;

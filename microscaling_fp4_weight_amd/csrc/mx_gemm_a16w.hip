@@ -186,23 +186,44 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[MI][NJ], const u32x4 (&x
         }
 }
 
-// The k loop over stages [sb, se) (sb and se multiples of SPW) of one output tile, whose
-// activation rows, weight codes and weight scales the descriptors cover; acc is zeroed first.
-//
-// Pipeline, one stage per iteration: dequantize the stage's weights, then MFMA steps 0-2
-// with each step's activations read one step ahead; once this stage's reads have completed
-// and the next stage has landed, one barrier publishes it and frees this stage's buffer,
-// which receives the stage three ahead; the next stage's weights and step-0 activations
-// are read while step 3's MFMAs run.  Scale window j + 1 is requested at stage 8j.  Stages
-// past the end of k load as zeros (out-of-range offsets), so every iteration has the same
-// shape; those past se (when a tile's k is split) are loaded and not used.
-template <int FMT, bool W8>
-__device__ __forceinline__ void run_k(uint8_t* lds, int wave, int lane, rsrc_t xr, rsrc_t wr, rsrc_t sr, uint32_t ldx,
-                                      uint32_t K, int sb, int se, f32x16 (&acc)[MI][NJ])
+template <int FMT, bool OUT_BF16, bool W8>
+__global__ __launch_bounds__(THREADS) void gemm_a16w_kernel(const GemmArgs a)
 {
     using G = Geo<W8>;
     constexpr int STAGE_BYTES = G::STAGE_BYTES, SWIN_OFF = G::SWIN_OFF, LPS = G::LOADS_PER_STAGE;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
+    const uint32_t K = (uint32_t)a.k, ldx = (uint32_t)a.ldx;
+
+    // tile mapping: with the n-tile count a multiple of 8, XCD x (= block % 8) takes n-tiles
+    // x, x+8, ...; with the m-tile count a multiple of 4 it runs them for 4 m-tiles at a time,
+    // so that the workgroups resident on an XCD share a few activation and weight tiles
+    // through its L2; else, for each n-tile, every m-tile in turn
+    const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + BN - 1) / BN);
+    uint32_t mt, nt;
+    if ((NT & 7) == 0 && (MT & 3) == 0) {
+        const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3, NT8 = NT >> 3;
+        const uint32_t grp = local / (4 * NT8), r = local - grp * (4 * NT8);
+        mt = grp * 4 + (r & 3);
+        nt = (r >> 2) * 8 + x;
+    } else if ((NT & 7) == 0) {
+        const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3;
+        mt = local % MT;
+        nt = (local / MT) * 8 + x;
+    } else {
+        mt = blockIdx.x % MT;
+        nt = blockIdx.x / MT;
+    }
+    const int64_t m0 = (int64_t)mt * BM, n0 = (int64_t)nt * BN;
+    const uint32_t mrows = (uint32_t)(a.m - m0 < BM ? a.m - m0 : BM);
+    const uint32_t nrows = (uint32_t)(a.n - n0 < BN ? a.n - n0 : BN);
+    const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, ((mrows - 1) * ldx + K) * 2);
+    const uint32_t wrowb = W8 ? K : K / 2;                   // code bytes per weight row
+    const rsrc_t wr = make_rsrc(a.wc + n0 * (int64_t)wrowb, nrows * wrowb);
+    const rsrc_t sr = make_rsrc(a.ws + n0 * (a.k / 32), nrows * (K / 32));
+
+    f32x16 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -210,11 +231,17 @@ __device__ __forceinline__ void run_k(uint8_t* lds, int wave, int lane, rsrc_t x
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    const int w0 = sb / SPW;
-    issue_window(lds + SWIN_OFF + (w0 & 1) * SWIN_BYTES, wave, lane, (uint32_t)w0, sr, K);
+    // Pipeline, one stage per iteration: dequantize the stage's weights, then MFMA steps 0-2
+    // with each step's activations read one step ahead; once this stage's reads have completed
+    // and the next stage has landed, one barrier publishes it and frees this stage's buffer,
+    // which receives the stage three ahead; the next stage's weights and step-0 activations
+    // are read while step 3's MFMAs run.  Scale window j + 1 is requested at stage 8j.  Stages
+    // past the end of k load as zeros (out-of-range offsets), so every iteration has the same
+    // shape.
+    const int S = (int)((K + BK - 1) / BK);
+    issue_window(lds + SWIN_OFF, wave, lane, 0, sr, K);
 #pragma unroll
-    for (int p = 0; p < STAGES; ++p)
-        issue_stage<W8>(lds + p * STAGE_BYTES, wave, lane, (uint32_t)(sb + p), xr, wr, ldx, K);
+    for (int p = 0; p < STAGES; ++p) issue_stage<W8>(lds + p * STAGE_BYTES, wave, lane, (uint32_t)p, xr, wr, ldx, K);
 
     const uint32_t r32 = lane & 31, h = lane >> 5;
     const uint32_t xrow0 = wm * 128 + r32, wrow0 = wn * 64 + r32;
@@ -224,11 +251,11 @@ __device__ __forceinline__ void run_k(uint8_t* lds, int wave, int lane, rsrc_t x
     uint32_t bw[NJ][16];
     wait_vmcnt<(STAGES - 1) * LPS>();
     barrier_only();
-    read_w(lds, lds + SWIN_OFF + (w0 & 1) * SWIN_BYTES, h, wrow0, h, wf);
+    read_w(lds, lds + SWIN_OFF, h, wrow0, h, wf);
     read_x<0>(lds, xrow0, h, xa);
 
     uint32_t cur = 0;  // byte offset of stage s's buffer
-    for (int s = sb; s < se; ++s) {
+    for (int s = 0; s < S; ++s) {
         const uint32_t nxt = cur + STAGE_BYTES == (uint32_t)(STAGES * STAGE_BYTES) ? 0u : cur + STAGE_BYTES;
         dequant_w<FMT, W8>(wf, bw);
         read_x<1>(lds + cur, xrow0, h, xb);
@@ -256,21 +283,13 @@ __device__ __forceinline__ void run_k(uint8_t* lds, int wave, int lane, rsrc_t x
         cur = nxt;
     }
     wait_vmcnt<0>();
-}
 
-// Epilogue: Y tile = g * acc.  Transposed 32x32 result layout: for tile (i, jn) a lane holds
-// output row m = i*32 + lane%32 and, for group q = e/4, columns n = jn*32 + 8q + 4*(lane/32)
-// + e%4.  A wave's 128 x 64 block is staged through LDS in passes of 64 (bf16) or 32 (fp32)
-// rows (a region per wave, rows padded against bank conflicts; the LDS accesses of one wave
-// complete in order, so a pass's writes follow the previous pass's reads) and written back as
-// whole 16-byte chunks.  Out-of-range chunks get an out-of-range offset and are dropped.
-template <bool OUT_BF16, bool W8>
-__device__ __forceinline__ void store_tile(const GemmArgs& a, uint8_t* lds, int wave, int lane, int64_t m0, int64_t n0,
-                                           uint32_t mrows, uint32_t nrows, const f32x16 (&acc)[MI][NJ])
-{
-    using G = Geo<W8>;
-    const int wm = wave >> 2, wn = wave & 3;
-    const uint32_t r32 = lane & 31, h = lane >> 5;
+    // Epilogue.  Transposed 32x32 result layout: for tile (i, jn) a lane holds output row
+    // m = i*32 + lane%32 and, for group q = e/4, columns n = jn*32 + 8q + 4*(lane/32) + e%4.
+    // A wave's 128 x 64 block is staged through LDS in passes of 64 (bf16) or 32 (fp32) rows
+    // (a region per wave, rows padded against bank conflicts; the LDS accesses of one wave
+    // complete in order, so a pass's writes follow the previous pass's reads) and written back
+    // as whole 16-byte chunks.  Out-of-range chunks get an out-of-range offset and are dropped.
     constexpr uint32_t ESZ = OUT_BF16 ? 2 : 4;
     const rsrc_t yr = make_rsrc(static_cast<uint8_t*>(a.y) + (m0 * a.ldy + n0) * ESZ, 0x7FFFFFFFu);
     const uint32_t ldy = (uint32_t)a.ldy;
@@ -333,237 +352,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, uint8_t* lds, int 
     }
 }
 
-// Descriptors of output tile (mt, nt): activation rows, weight codes, weight scales.
-template <bool W8>
-struct TileRes {
-    int64_t m0, n0;
-    uint32_t mrows, nrows;
-    rsrc_t xr, wr, sr;
-};
-template <bool W8>
-__device__ __forceinline__ TileRes<W8> tile_res(const GemmArgs& a, uint32_t mt, uint32_t nt)
-{
-    TileRes<W8> t;
-    const uint32_t K = (uint32_t)a.k, ldx = (uint32_t)a.ldx;
-    t.m0 = (int64_t)mt * BM;
-    t.n0 = (int64_t)nt * BN;
-    t.mrows = (uint32_t)(a.m - t.m0 < BM ? a.m - t.m0 : BM);
-    t.nrows = (uint32_t)(a.n - t.n0 < BN ? a.n - t.n0 : BN);
-    t.xr = make_rsrc(a.x + t.m0 * a.ldx, ((t.mrows - 1) * ldx + K) * 2);
-    const uint32_t wrowb = W8 ? K : K / 2;                   // code bytes per weight row
-    t.wr = make_rsrc(a.wc + t.n0 * (int64_t)wrowb, t.nrows * wrowb);
-    t.sr = make_rsrc(a.ws + t.n0 * (a.k / 32), t.nrows * (K / 32));
-    return t;
-}
-
-template <int FMT, bool OUT_BF16, bool W8>
-__global__ __launch_bounds__(THREADS) void gemm_a16w_kernel(const GemmArgs a)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // tile mapping: with the n-tile count a multiple of 8, XCD x (= block % 8) takes n-tiles
-    // x, x+8, ...; with the m-tile count a multiple of 4 it runs them for 4 m-tiles at a time,
-    // so that the workgroups resident on an XCD share a few activation and weight tiles
-    // through its L2; else, for each n-tile, every m-tile in turn
-    const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + BN - 1) / BN);
-    uint32_t mt, nt;
-    if ((NT & 7) == 0 && (MT & 3) == 0) {
-        const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3, NT8 = NT >> 3;
-        const uint32_t grp = local / (4 * NT8), r = local - grp * (4 * NT8);
-        mt = grp * 4 + (r & 3);
-        nt = (r >> 2) * 8 + x;
-    } else if ((NT & 7) == 0) {
-        const uint32_t x = blockIdx.x & 7, local = blockIdx.x >> 3;
-        mt = local % MT;
-        nt = (local / MT) * 8 + x;
-    } else {
-        mt = blockIdx.x % MT;
-        nt = blockIdx.x / MT;
-    }
-    const TileRes<W8> t = tile_res<W8>(a, mt, nt);
-    f32x16 acc[MI][NJ];
-    run_k<FMT, W8>(lds, wave, lane, t.xr, t.wr, t.sr, (uint32_t)a.ldx, (uint32_t)a.k, 0, (int)((a.k + BK - 1) / BK), acc);
-    store_tile<OUT_BF16, W8>(a, lds, wave, lane, t.m0, t.n0, t.mrows, t.nrows, acc);
-}
-
-// ---------------------------------------------------------------------------------------
-// Split along k, for fewer output tiles than CUs (a single, partly empty round): the work is
-// the T = tiles x W scale windows of 512 k (W per tile, tiles in order t = nt * MT + mt), and
-// workgroup w of G takes windows [floor(w T / G), floor((w + 1) T / G)) -- the same amount of
-// work for every CU.  Its range cuts at most its first and its last tile: a tile whose windows
-// all fall in one workgroup is stored as usual; the pieces of a cut tile (p = 0, 1, ... in k
-// order, from consecutive workgroups) meet through the workspace.  Every piece but the one
-// that finishes the tile writes its fp32 partial tile and counts itself on the tile's counter
-// (zeroed before the launch); the finishing piece, the one that finds all the others counted,
-// adds the partials in piece order (fixed: the result does not depend on timing) and stores
-// the tile.  A piece first reads the counter: when the others are all in, it finishes without
-// writing its own partial (the last piece of a tile usually does).  No workgroup ever waits
-// for another.  At most one piece finishes: one that finds the others in has not counted
-// itself, so no other can see a full count, and otherwise the last to count finishes.
-// ---------------------------------------------------------------------------------------
-constexpr int PART_FLOATS = MI * NJ * 16 * THREADS;  // one partial tile (256 x 256 fp32)
-// workspace: the tile counters (rounded up to 256 bytes), then two partial slots per workgroup
-__host__ __device__ constexpr uint64_t counts_bytes(uint64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
-
-// workgroup that holds window u: the largest w with floor(w T / G) <= u
-__device__ __forceinline__ uint32_t owner(uint64_t u, uint64_t T, uint64_t G)
-{
-    return (uint32_t)(((u + 1) * G - 1) / T);
-}
-
-// partial slot of piece p of a tile whose piece 0 belongs to workgroup w0: a piece p > 0
-// starts its workgroup's range (slot 2 (w0 + p)), piece 0 ends it (slot 2 w0 + 1)
-__device__ __forceinline__ float* part_slot(float* base, uint32_t w0, uint32_t p)
-{
-    const uint64_t slot = p > 0 ? 2ull * (w0 + p) : 2ull * w0 + 1;
-    return base + slot * PART_FLOATS;
-}
-
-template <int FMT, bool OUT_BF16, bool W8>
-__global__ __launch_bounds__(THREADS) void gemm_a16w_split_kernel(const GemmArgs a, uint32_t wpt)
-{
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ uint32_t fin_s;
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t MT = (uint32_t)((a.m + BM - 1) / BM), NT = (uint32_t)((a.n + BN - 1) / BN);
-    const uint64_t T = (uint64_t)MT * NT * wpt, G = gridDim.x, w = blockIdx.x;
-    const uint64_t u0 = w * T / G, u1 = (w + 1) * T / G;
-    float* parts = reinterpret_cast<float*>(a.a16_ws + counts_bytes(MT * NT));
-    f32x16 acc[MI][NJ];
-    // The range is at most one tile long (the plan guarantees it), so it is one piece, or the end
-    // of tile t1 and the start of tile t1 + 1.  The piece that starts a tile runs first: then
-    // every workgroup sweeps k upwards from about the same window at about the same time, and
-    // the activation windows they read at once stay few enough for the L2 to share.
-    const uint32_t t1 = (uint32_t)(u0 / wpt), a0 = (uint32_t)(u0 - (uint64_t)t1 * wpt), len = (uint32_t)(u1 - u0);
-    const bool wraps = a0 + len > wpt;
-    for (int piece = 0; piece < (wraps ? 2 : 1); ++piece) {
-        // lane-dependent addresses are recomputed for each piece: kept from the previous piece
-        // they would stay live through the epilogue and fix-up and spill
-        int lane_i = lane, tid_i = tid;
-        asm volatile("" : "+v"(lane_i), "+v"(tid_i));
-        const bool head = wraps && piece == 0;  // the start of tile t1 + 1
-        const uint32_t tile = head ? t1 + 1 : t1, wb = head ? 0u : a0;
-        const uint32_t we = head ? a0 + len - wpt : (wraps ? wpt : a0 + len);
-        const TileRes<W8> t = tile_res<W8>(a, tile % MT, tile / MT);
-        if (piece) barrier_only();  // the previous piece's epilogue is done with the LDS
-        run_k<FMT, W8>(lds, wave, lane_i, t.xr, t.wr, t.sr, (uint32_t)a.ldx, (uint32_t)a.k, (int)(wb * SPW),
-                       (int)(we * SPW), acc);
-        bool store = wb == 0 && we == wpt;  // the whole tile in this workgroup
-        if (!store) {
-            const uint64_t tw = (uint64_t)tile * wpt;
-            const uint32_t w0 = owner(tw, T, G), np = owner(tw + wpt - 1, T, G) - w0 + 1, p = (uint32_t)w - w0;
-            uint32_t* cnt = reinterpret_cast<uint32_t*>(a.a16_ws) + tile;
-            // Visibility across workgroups (and XCDs) with one write-back of the L2 per partial
-            // (a release fence before the count) and one invalidation per finished tile (an
-            // acquire fence after reading the full count): the other workgroups of the XCD keep
-            // their activation and weight lines in the L2 meanwhile.
-            if (tid_i == 0) {
-                const bool all_in = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-                if (all_in) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                fin_s = all_in;
-            }
-            __syncthreads();
-            store = fin_s != 0;
-            if (!store) {
-                // partial: the 16 floats of thread tid's 32 x 32 tile (i, jn) at
-                // ((i NJ + jn) THREADS + tid) 16, as four 16-byte stores
-                f32x4* dst = reinterpret_cast<f32x4*>(part_slot(parts, w0, p)) + 4 * tid_i;
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int jn = 0; jn < NJ; ++jn)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            dst[(i * NJ + jn) * 4 * THREADS + c] =
-                                f32x4{acc[i][jn][4 * c], acc[i][jn][4 * c + 1], acc[i][jn][4 * c + 2], acc[i][jn][4 * c + 3]};
-                wait_vmcnt<0>();  // this wave's partial has reached its L2
-                __syncthreads();
-                if (tid_i == 0) {
-                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                    const bool last = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == np - 1;
-                    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                    fin_s = last;
-                }
-                __syncthreads();
-                store = fin_s != 0;
-            }
-            if (store) {
-                // the tile = the pieces' partials added in piece order, this piece's from
-                // registers: ((P0 + P1) + P2) ...
-#pragma unroll
-                for (int i = 0; i < MI; ++i)
-#pragma unroll
-                    for (int jn = 0; jn < NJ; ++jn) {
-                        const uint32_t off = (uint32_t)(((i * NJ + jn) * THREADS + tid_i) * 4);  // in f32x4
-                        f32x16 sum = acc[i][jn];
-                        if (p != 0) {
-                            const f32x4* src = reinterpret_cast<const f32x4*>(part_slot(parts, w0, 0)) + off;
-#pragma unroll
-                            for (int c = 0; c < 4; ++c) {
-                                const f32x4 v = src[c];
-                                sum[4 * c] = v.x; sum[4 * c + 1] = v.y; sum[4 * c + 2] = v.z; sum[4 * c + 3] = v.w;
-                            }
-                        }
-                        for (uint32_t q = 1; q < np; ++q) {
-                            if (q == p) {
-                                sum += acc[i][jn];
-                            } else {
-                                const f32x4* src = reinterpret_cast<const f32x4*>(part_slot(parts, w0, q)) + off;
-#pragma unroll
-                                for (int c = 0; c < 4; ++c) {
-                                    const f32x4 v = src[c];
-                                    sum[4 * c] += v.x; sum[4 * c + 1] += v.y; sum[4 * c + 2] += v.z; sum[4 * c + 3] += v.w;
-                                }
-                            }
-                        }
-                        acc[i][jn] = sum;
-                    }
-            }
-        }
-        if (store) store_tile<OUT_BF16, W8>(a, lds, wave, lane_i, t.m0, t.n0, t.mrows, t.nrows, acc);
-    }
-}
-
-// The split schedule: G workgroups over the windows of fewer tiles than CUs, at least
-// MIN_WINDOWS windows (3072 k) per workgroup; used when it adds workgroups.
-constexpr uint32_t SPLIT_CUS = 256, MIN_WINDOWS = 6;
-struct SplitPlan {
-    uint32_t tiles, wpt, groups;
-};
-inline SplitPlan split_plan(int64_t m, int64_t n, int64_t k)
-{
-    SplitPlan s{0, 0, 0};
-    if (m <= 128 || n <= 0 || k <= 0 || k % SWIN_K != 0) return s;  // m as for the unsplit kernel
-    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-    if (tiles >= SPLIT_CUS) return s;
-    const int64_t wpt = k / SWIN_K, T = tiles * wpt;
-    int64_t g = T / MIN_WINDOWS;
-    if (g > SPLIT_CUS) g = SPLIT_CUS;
-    if (g <= tiles) return s;
-    if ((T + g - 1) / g > wpt) return s;  // every range at most one tile long
-    s.tiles = (uint32_t)tiles;
-    s.wpt = (uint32_t)wpt;
-    s.groups = (uint32_t)g;
-    return s;
-}
-
 template <int FMT, bool OUT_BF16, bool W8>
 static hipError_t launch(const GemmArgs& a, hipStream_t st)
 {
     constexpr int LDS = Geo<W8>::LDS_BYTES;
-    const SplitPlan sp = split_plan(a.m, a.n, a.k);
-    if (sp.groups && a.a16_ws) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void*)gemm_a16w_split_kernel<FMT, OUT_BF16, W8>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (attr != hipSuccess) return attr;
-        // the tile counters start at zero (a fill kernel: no memset node if the call is captured)
-        const hipError_t e = launch_fill_zero(a.a16_ws, 1, sp.tiles, sp.tiles, false, st);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((gemm_a16w_split_kernel<FMT, OUT_BF16, W8>), dim3(sp.groups), dim3(THREADS), LDS, st, a,
-                           sp.wpt);
-        return hipGetLastError();
-    }
     // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
     static const hipError_t attr = hipFuncSetAttribute(
         (const void*)gemm_a16w_kernel<FMT, OUT_BF16, W8>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
@@ -592,13 +384,6 @@ bool a16w_uses(const GemmArgs& a, bool w8)
     // 8-wave one: in cycles both beat this one (2048 x 16384 x 8192: 692 k / 780 k cycles per
     // XCD, modelled from the measured rounds, against 814 k measured)
     return w8;
-}
-
-size_t a16w_split_workspace(int64_t m, int64_t n, int64_t k)
-{
-    const a16w::SplitPlan sp = a16w::split_plan(m, n, k);
-    if (!sp.groups) return 0;
-    return a16w::counts_bytes(sp.tiles) + (size_t)sp.groups * 2 * a16w::PART_FLOATS * sizeof(float);
 }
 
 hipError_t launch_gemm_a16w(const GemmArgs& a, bool w8, hipStream_t st)

@@ -76,9 +76,6 @@ struct GemmArgs {
     // matrix-core kernel, row-major for the direct one)
     uint8_t* xq_codes;
     uint8_t* xq_scales;
-    // W4A16 / W8A16 split along k: workspace of a16w_split_workspace(m, n, k) bytes for the
-    // wide-tile kernel (a counter per output tile, then fp32 partial tiles), or null
-    uint8_t* a16_ws;
 };
 
 // Tiled scale layout (block 32): rows in tiles of 256, k in stages of 256 (8 blocks); the
@@ -113,9 +110,6 @@ hipError_t launch_gemm_w8_tiled(const GemmArgs& a, hipStream_t st);
 // weights)
 bool a16w_uses(const GemmArgs& a, bool w8);
 hipError_t launch_gemm_a16w(const GemmArgs& a, bool w8, hipStream_t st);
-// Workspace bytes for the split-k schedule of the wide-tile kernel at this shape (0 when the
-// shape does not take it): fewer 256 x 256 output tiles than CUs and long enough k.
-size_t a16w_split_workspace(int64_t m, int64_t n, int64_t k);
 // the large-m W4A16 GEMM with two 4-wave workgroups per CU (FP4 codes, E8M0 scales, more
 // 128 x 256 tiles than CUs, and the pipelined kernel's other conditions)
 bool a16p_uses(const GemmArgs& a);

@@ -52,8 +52,8 @@ extern "C" mx_status mx_gemm_static(const void* x, int64_t m, int64_t n, int64_t
                                     mx_act_mode mode, void* y, mx_dtype y_type, int64_t ld_y,
                                     void* stream)
 {
-    const size_t need = mode == MX_A16 ? 0 : mx_gemm_workspace_size(m, n, k, block, mode);
-    if (need == 0)  // W4A16 (its workspace is optional), invalid arguments or an empty shape
+    const size_t need = mx_gemm_workspace_size(m, n, k, block, mode);
+    if (need == 0)  // W4A16, invalid arguments or an empty shape: mx_gemm decides
         return mx_gemm(x, m, n, k, ld_x, w_codes, w_scales, block, fmt, tensor_scale, layout, mode, y,
                        y_type, ld_y, nullptr, 0, stream);
     if (need > kScratchBytes) return MX_ERR_TOO_LARGE;

@@ -168,21 +168,6 @@ static void gemm_rules()
         CHECK(ptr(g_launches[2].aux) == wc && ptr(g_launches[2].aux2) == ws);
     }
 
-    // W4A16: the workspace is optional (the k-split schedule of products with few output
-    // tiles); passed on only when given, large enough and aligned
-    {
-        const int64_t M16 = 300, N16 = 1024, K16 = 8192;
-        const size_t n16 = mx_gemm_workspace_size(M16, N16, K16, 32, MX_A16);
-        CHECK(n16 > 0 && mx_gemm_workspace_size(M16, N16, K16, 16, MX_A16) == 0);
-        const struct { uint8_t* w; size_t bytes; const uint8_t* want; } cases[] = {
-            {nullptr, 0, ws}, {work, n16 - 1, ws}, {nullptr, n16, ws}, {work, n16, work}};
-        for (const auto& c : cases) {
-            EXPECT(mx_gemm(x, M16, N16, K16, K16, wc, ws, 32, MX_SCALE_E8M0, 1.0f, MX_LAYOUT_ROWMAJOR, MX_A16, y, MX_BF16, N16, c.w, c.bytes, nullptr), MX_OK);
-            CHECK(g_launches.size() == 1 && ptr(g_launches[0].aux2) == c.want);
-        }
-        EXPECT_NO_LAUNCH(mx_gemm(x, M16, N16, K16, K16, wc, ws, 32, MX_SCALE_E8M0, 1.0f, MX_LAYOUT_ROWMAJOR, MX_A16, y, MX_BF16, N16, work + 8, n16, nullptr), MX_ERR_ALIGNMENT);
-    }
-
     // W4A4: activation pre-pass into the workspace (codes, then tiled scales at a 256-byte
     // boundary), then the product reading them
     const int64_t M4 = 300, N4 = 512, K4 = 256;

@@ -4,8 +4,7 @@
 // launcher, the row or m count it was handed, and its principal pointers) and returns
 // hipSuccess, or hipErrorInvalidValue when the driver asks the next launch to fail.  The three
 // helper functions return values of the right kind: a4_uses_mfma the k condition of the
-// matrix-core W4A4 kernel, the group counts a positive number within their caps, the k-split
-// workspace a positive size for the shapes that take it.
+// matrix-core W4A4 kernel, the group counts a positive number within their caps.
 #include <vector>
 
 #include "mx_internal.h"
@@ -38,16 +37,7 @@ hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t) { return record(
 hipError_t launch_dequantize_fp8(const DequantArgs& a, hipStream_t) { return record("dequantize_fp8", a.rows, a.codes, a.y, a.scales); }
 hipError_t launch_quant_error(const ErrArgs& a, hipStream_t) { return record("quant_error", a.rows, a.x, a.out, a.partials); }
 hipError_t launch_tensor_stats(const StatsArgs& a, hipStream_t) { return record("tensor_stats", a.rows, a.x, a.out, a.partials); }
-hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t)
-{
-    // aux2: the weight scales, or the k-split workspace when the call passes one on
-    return record("gemm_a16", a.m, a.x, a.y, a.wc, a.a16_ws ? static_cast<const void*>(a.a16_ws) : a.ws);
-}
-// any positive size for the shapes the k-split schedule takes exercises the C-ABI layer
-size_t a16w_split_workspace(int64_t m, int64_t n, int64_t k)
-{
-    return m > 128 && k % 512 == 0 && ((m + 255) / 256) * ((n + 255) / 256) < 256 ? size_t(1) << 20 : 0;
-}
+hipError_t launch_gemm_a16(const GemmArgs& a, hipStream_t) { return record("gemm_a16", a.m, a.x, a.y, a.wc, a.ws); }
 hipError_t launch_gemm_a4(const GemmArgs& a, hipStream_t) { return record("gemm_a4", a.m, a.xq_codes, a.y, a.xq_scales, a.x); }
 hipError_t launch_gemm_w8(const W8Args& a, hipStream_t) { return record("gemm_w8", a.m, a.x, a.y, a.wc, a.ws); }
 hipError_t launch_fill_zero(void* y, int64_t m, int64_t, int64_t, bool, hipStream_t) { return record("fill_zero", m, nullptr, y); }

@@ -456,75 +456,6 @@ def test_gemm_a16_paired_sampled(m, n, k, g, ldy_extra, fmt):
         del y
 
 
-# W4A16 split along k (the wide-tile kernel's schedule for fewer 256 x 256 output tiles than CUs,
-# taken when the call has a workspace): G workgroups each take an equal run of 512-k windows of
-# the tiles in order, so that a tile is cut among up to six workgroups and one workgroup can end
-# one tile and start the next; the pieces meet through the workspace in piece order.
-# m 200 x n 1000 x k 8192: 4 tiles of 16 windows, 10 workgroups (6-7 windows each); m 300 x
-# n 700 x k 16384: 6 tiles (ragged in m and n) of 32 windows, 32 workgroups; g != 1, strided
-# output rows whose columns past n stay untouched.  Every output against the oracle, for both
-# output types; with a workspace the result repeats bit for bit and agrees with the unsplit
-# kernel (no workspace) to the same tolerance.
-@pytest.mark.parametrize("fmt", ["e4m3", "ue5m3"])
-@pytest.mark.parametrize("m,n,k,g,ldy_extra", [(200, 1000, 8192, 1.0, 0), (300, 700, 16384, 0.37, 8)])
-def test_gemm_a16_split_k(m, n, k, g, ldy_extra, fmt):
-    g = float(np.float32(g))
-    need = mx.mx_gemm_workspace_size(m, n, k, 32, "a16")
-    assert need > 0, "the shape takes the k-split schedule"
-    x = synth.normal((m, k), "bf16", f"sk.x.{m}", 1.0)
-    w = synth.normal((n, k), "bf16", f"sk.w.{n}", 0.02, 0.01, 20.0)
-    c, s, cd, sd = quantize_ref(w, 32, fmt, g)
-    yref, aref = oracle.gemm(x, c, s, 32, fmt, g, "a16")
-    xd = bf16_dev(x)
-    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
-    for dt in (torch.float32, torch.bfloat16):
-        outs = []
-        for workspace in (ws, ws, torch.empty(0, dtype=torch.uint8, device=DEV)):
-            big = torch.full((m, n + ldy_extra), float("nan"), dtype=dt, device=DEV)
-            y = big[:, :n]
-            mx.mx_gemm(xd, cd, sd, 32, fmt, g, "a16", y=y, workspace=workspace)
-            torch.cuda.synchronize()
-            assert_gemm_close(to_host_bits(y.float()), yref, aref, dt == torch.bfloat16,
-                              f"split-k {fmt} {m}x{n}x{k} {dt} workspace {workspace.numel()}")
-            if ldy_extra:
-                assert torch.isnan(big[:, n:].float()).all()
-            outs.append(to_host_bits(y.contiguous()))
-        np.testing.assert_array_equal(outs[0], outs[1])  # the same pieces, added in the same order
-
-
-def test_gemm_a16_split_k_graph_replay():
-    """The split schedule (a fill kernel zeroes the tile counters, then the split product)
-    captured in a HIP graph: every replay, with other work and new activations in between,
-    gives the eager call's bits."""
-    m, n, k, fmt = 200, 1000, 8192, "ue5m3"
-    need = mx.mx_gemm_workspace_size(m, n, k, 32, "a16")
-    assert need > 0
-    w = synth.normal((n, k), "bf16", "skg.w", 0.02, 0.01, 20.0)
-    wd = bf16_dev(w)
-    cd, sd = mx.mx_quantize(wd, 32, fmt)
-    xs = [bf16_dev(synth.normal((m, k), "bf16", f"skg.x.{i}", 1.0)) for i in range(3)]
-    x = xs[0].clone()
-    y = torch.empty((m, n), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        mx.mx_gemm(x, cd, sd, 32, fmt, 1.0, "a16", y=y, workspace=ws)  # warm-up outside capture
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        mx.mx_gemm(x, cd, sd, 32, fmt, 1.0, "a16", y=y, workspace=ws)
-    for rep in range(6):
-        xi = xs[rep % 3]
-        ref = mx.mx_gemm(xi, cd, sd, 32, fmt, 1.0, "a16", workspace=torch.empty(need, dtype=torch.uint8, device=DEV))
-        x.copy_(xi)
-        graph.replay()
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(to_host_bits(y), to_host_bits(ref), err_msg=f"replay {rep}")
-    del graph
-
-
 # activation rows of the 405B-FFN products: one in each 256-row m-tile for m = 4096
 C5_ROWS = {1: [0], 256: [0, 85, 170, 255], 4096: [256 * i + (97 * i) % 256 for i in range(15)] + [4095]}
 
