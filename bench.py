@@ -888,7 +888,10 @@ def cpu_baseline(np, synth, gpu_value, rows):
        slice of weight rows for the 70B-FFN prefill (W4A16 and W4A4) and the 405B-FFN m = 4096
        product; their full-size times are estimated from a 16-row and a 1-row run of the same
        weight slice (per weight row: one dequantization plus one dot product per activation
-       row), scaled to all n rows.
+       row), scaled to all n rows;
+     * the tiny round trip in full (256 x 256 fp32 weight, block 32 E4M3: quantize, dequantize,
+       GEMV) and the 405B-FFN weight's offline quantize (UE5M3 with its tensor scale) on its
+       first 512 of 53248 rows, scaled to all rows.
     Inputs are generated and the sampled weights quantized before the clock starts; only the
     oracle calls are timed."""
     import oracle
@@ -909,6 +912,12 @@ def cpu_baseline(np, synth, gpu_value, rows):
         wc, wsc = oracle.quantize(w, 32, fmt, g)
         gemm_inputs.append((x[:ms], wc, wsc, fmt, g))
         del w
+    c1w, c1x = synth.c1_weight(), synth.c1_x()
+    c5_rows = 512
+    c5g = (rows or {}).get("c5_tensor_scale")
+    if c5g is None:
+        c5g = synth.c5_tensor_scale(synth.c5_weight())
+    c5w = synth.c5_weight(row0=0, nrows=c5_rows)
     cpu = sorted(os.sched_getaffinity(0))[0]
     saved = os.sched_getaffinity(0)
     os.sched_setaffinity(0, {cpu})
@@ -945,6 +954,19 @@ def cpu_baseline(np, synth, gpu_value, rows):
                 gpu_s = g_row["us_per_launch"] * 1e-6 if "us_per_launch" in g_row else g_row["ms"] * 1e-3
                 ent["gpu_speedup"] = round(est / gpu_s, 1)
             gemm[name] = ent
+        t1 = time.perf_counter()
+        c, sc = oracle.quantize(c1w, 32, "e4m3")
+        oracle.dequantize(c, sc, 256, 32, "e4m3")
+        oracle.gemm(c1x, c, sc, 32, "e4m3", 1.0, "a16")
+        gemm["c1_round_trip_and_gemv"] = {"s": round(time.perf_counter() - t1, 4), "sample": "in full"}
+        t1 = time.perf_counter()
+        oracle.quantize(c5w, 32, "ue5m3", c5g)
+        qt = time.perf_counter() - t1
+        ent = {"s": round(qt, 3), "full_s": round(qt * 53248 / c5_rows, 1), "sample": f"{c5_rows} of 53248 rows"}
+        g_row = (rows or {}).get("quantize.ue5m3.g.n53248.k16384")
+        if g_row is not None:
+            ent["gpu_speedup"] = round(qt * 53248 / c5_rows / (g_row["ms"] * 1e-3), 1)
+        gemm["quantize.ue5m3.g.n53248.k16384"] = ent
     finally:
         os.sched_setaffinity(0, saved)
     value = byt / dt / 1e9
