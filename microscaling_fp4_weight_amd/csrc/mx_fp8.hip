@@ -279,10 +279,11 @@ __global__ __launch_bounds__(THREADS) void quantize_fp8_hw32_kernel(const uint8_
     }
     if (!act) return;
     u32x4* cp = reinterpret_cast<u32x4*>(codes + (int64_t)row * k + (int64_t)gc * 32);
-    cp[0] = u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                  __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])};
-    cp[1] = u32x4{__builtin_bit_cast(uint32_t, h[4]), __builtin_bit_cast(uint32_t, h[5]),
-                  __builtin_bit_cast(uint32_t, h[6]), __builtin_bit_cast(uint32_t, h[7])};
+    // non-temporal: the codes are not read again by this launch
+    __builtin_nontemporal_store(u32x4{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                      __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])}, cp);
+    __builtin_nontemporal_store(u32x4{__builtin_bit_cast(uint32_t, h[4]), __builtin_bit_cast(uint32_t, h[5]),
+                                      __builtin_bit_cast(uint32_t, h[6]), __builtin_bit_cast(uint32_t, h[7])}, cp + 1);
     uint8_t* sp = scales + (int64_t)row * (k / BLOCK);
     if constexpr (NB == 1) {
         if (LANES == 1 || (gc % LANES) == 0) sp[gc / LANES] = (uint8_t)sb[0];
@@ -475,11 +476,13 @@ __global__ __launch_bounds__(THREADS) void dequantize_fp8_u2_kernel(const uint8_
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 o[j] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2 * j], (__bf16)v[2 * j + 1]});
-            *reinterpret_cast<u32x4*>(y + (int64_t)row[h] * ldy_bytes + (int64_t)c8[h] * 16) = u32x4{o[0], o[1], o[2], o[3]};
+            // non-temporal stores: 8% faster than plain ones here (bf16 out, 27.3-28.4 -> 25.3-25.8 us)
+            __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]},
+                                        reinterpret_cast<u32x4*>(y + (int64_t)row[h] * ldy_bytes + (int64_t)c8[h] * 16));
         } else {
             u32x4* p = reinterpret_cast<u32x4*>(y + (int64_t)row[h] * ldy_bytes + (int64_t)c8[h] * 32);
-            p[0] = u32x4{f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])};
-            p[1] = u32x4{f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])};
+            __builtin_nontemporal_store(u32x4{f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])}, p);
+            __builtin_nontemporal_store(u32x4{f2u(v[4]), f2u(v[5]), f2u(v[6]), f2u(v[7])}, p + 1);
         }
     }
 }
