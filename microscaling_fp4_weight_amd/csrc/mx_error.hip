@@ -179,8 +179,10 @@ __global__ __launch_bounds__(ERR_THREADS) void quant_error_fast_kernel(
             const double s64 = scale_value_f64<FMT>(sbyte);
             const bool flushed = s64 == 0.0;
             const float amf = u2f(amax[b]);
-            double acc = 0.0;  // squared errors of the elements below the maximum
-            uint32_t ties = 0;
+            // squared errors of all the lane's elements of the block; an element tied with the
+            // maximum (|x| = max) has exactly the maximum's squared error, so the block's
+            // maximum term is taken off the total once, below, instead of testing every element
+            double acc = 0.0;
             uint32_t cmax;     // code magnitude of the maximum
             double sqm;        // its squared error
 
@@ -209,16 +211,13 @@ __global__ __launch_bounds__(ERR_THREADS) void quant_error_fast_kernel(
                     }
                     const float q0 = FMT == FMT_E8M0 ? d.x : d.x * dp.mant;  // e * s, exact
                     const float q1 = FMT == FMT_E8M0 ? d.y : d.y * dp.mant;
-                    const bool t0 = __builtin_fabsf(lo) == amf, t1 = __builtin_fabsf(hi) == amf;
-                    ties += (uint32_t)t0 + (uint32_t)t1;
                     double e0, e1;
                     if constexpr (BF16) {
-                        const float f0 = t0 ? 0.0f : q0 - lo, f1 = t1 ? 0.0f : q1 - hi;  // exact
-                        e0 = (double)f0;
-                        e1 = (double)f1;
+                        e0 = (double)(q0 - lo);  // exact in fp32
+                        e1 = (double)(q1 - hi);
                     } else {
-                        e0 = (double)q0 - (double)(t0 ? q0 : lo);
-                        e1 = (double)q1 - (double)(t1 ? q1 : hi);
+                        e0 = (double)q0 - (double)lo;
+                        e1 = (double)q1 - (double)hi;
                     }
                     acc = __builtin_fma(e0, e0, acc);
                     acc = __builtin_fma(e1, e1, acc);
@@ -247,9 +246,7 @@ __global__ __launch_bounds__(ERR_THREADS) void quant_error_fast_kernel(
                     const f32x2 d = dec_pair_sel<0>(cb, 1.0f);  // e
                     const double q0 = (double)d.x * sg, q1 = (double)d.y * sg;  // exact
                     const float lo = u2f(b0), hi = u2f(b1);
-                    const bool t0 = __builtin_fabsf(lo) == amf, t1 = __builtin_fabsf(hi) == amf;
-                    ties += (uint32_t)t0 + (uint32_t)t1;
-                    const double e0 = t0 ? 0.0 : q0 - (double)lo, e1 = t1 ? 0.0 : q1 - (double)hi;
+                    const double e0 = q0 - (double)lo, e1 = q1 - (double)hi;
                     acc = __builtin_fma(e0, e0, acc);
                     acc = __builtin_fma(e1, e1, acc);
                     if constexpr (XHAT) {
@@ -263,20 +260,16 @@ __global__ __launch_bounds__(ERR_THREADS) void quant_error_fast_kernel(
                 }
             }
 
-            // block-level terms: once per block (by the block's first lane when it spans lanes)
+            // block-level terms: once per block (by the block's first lane when it spans lanes);
+            // the block's elements other than one maximum are its ordinary-element term
             bool lead = true;
-            if constexpr (LANES > 1) {
-#pragma unroll
-                for (int off = 1; off < LANES; off <<= 1) ties += (uint32_t)__shfl_xor((int)ties, off);
-                lead = (cgc & (LANES - 1)) == 0;
-            }
-            const double tsq = lead ? (double)ties * sqm : 0.0;  // all tied elements
-            st += acc + tsq;
+            if constexpr (LANES > 1) lead = (cgc & (LANES - 1)) == 0;
+            st += acc;
             if (flushed) {
-                sz += acc + tsq;
+                sz += acc;
                 nzero += lead ? 1.0 : 0.0;
             } else {
-                se += acc + ((lead && ties) ? (double)(ties - 1u) * sqm : 0.0);
+                se += lead ? acc - sqm : acc;
                 sm += lead ? sqm : 0.0;
                 nnot6 += (lead && cmax != 7u) ? 1.0 : 0.0;
             }
