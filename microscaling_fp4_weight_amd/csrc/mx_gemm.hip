@@ -632,12 +632,13 @@ static hipError_t launch_sweep(const GemmArgs& a, uint32_t units, hipStream_t st
     const dim3 grid(units < SW_GRID ? units : SW_GRID);
     const size_t lds = (size_t)MM * a.k * 2;  // X; at most 64 KB (m <= 2, k <= 16384)
     // allow the full 64 KB of dynamic LDS next to the static partial sums
-    static const hipError_t attr_pre = hipFuncSetAttribute(
-        (const void*)gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>, hipFuncAttributeMaxDynamicSharedMemorySize, 65536);
-    if (attr_pre != hipSuccess) return attr_pre;
-    if (attr != hipSuccess) return attr;
+    static LdsLimit lim_pre, lim;
+    if (const hipError_t e = lim_pre.ensure((const void*)gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>, 65536, st);
+        e != hipSuccess)
+        return e;
+    if (const hipError_t e = lim.ensure((const void*)gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>, 65536, st);
+        e != hipSuccess)
+        return e;
     if (!W8 && a.ws_pre) hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, true, MM, false>), grid, dim3(256), lds, st, a, units);
     else hipLaunchKernelGGL((gemv_sweep_kernel<FMT, OUT_BF16, false, MM, W8>), grid, dim3(256), lds, st, a, units);
     return hipGetLastError();
@@ -813,9 +814,10 @@ static hipError_t launch_a16_fmt(const GemmArgs& a, hipStream_t st)
         const int lds_bytes = need > GL_RED ? need : GL_RED;
         switch (a.block) {
 #define MXL(B) case B: { \
-    static const hipError_t attr = hipFuncSetAttribute((const void*)gemv_lds_kernel<B, FMT, OUT_BF16>, \
-        hipFuncAttributeMaxDynamicSharedMemorySize, 16 * GL_PITCH > GL_RED ? 16 * GL_PITCH : GL_RED); \
-    if (attr != hipSuccess) return attr; \
+    static LdsLimit lim; \
+    if (const hipError_t e = lim.ensure((const void*)gemv_lds_kernel<B, FMT, OUT_BF16>, \
+                                        16 * GL_PITCH > GL_RED ? 16 * GL_PITCH : GL_RED, st); e != hipSuccess) \
+        return e; \
     hipLaunchKernelGGL((gemv_lds_kernel<B, FMT, OUT_BF16>), dim3(g), dim3(64 * GL_WAVES), lds_bytes, st, a); \
     break; }
             MXL(4) MXL(8) MXL(16) MXL(32) MXL(64) MXL(128) MXL(256)

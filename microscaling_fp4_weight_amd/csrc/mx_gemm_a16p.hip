@@ -331,10 +331,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_a16p_kernel(const GemmArgs a)
 template <int FMT, bool OUT_BF16>
 static hipError_t launch(const GemmArgs& a, hipStream_t st)
 {
-    // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)gemm_a16p_kernel<FMT, OUT_BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-    if (attr != hipSuccess) return attr;
+    // the LDS ring exceeds the default 64 KB dynamic limit
+    static LdsLimit lim;
+    if (const hipError_t e = lim.ensure((const void*)gemm_a16p_kernel<FMT, OUT_BF16>, LDS_BYTES, st); e != hipSuccess)
+        return e;
     const unsigned tiles = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + BN - 1) / BN));
     hipLaunchKernelGGL((gemm_a16p_kernel<FMT, OUT_BF16>), dim3(tiles), dim3(THREADS), LDS_BYTES, st, a);
     return hipGetLastError();

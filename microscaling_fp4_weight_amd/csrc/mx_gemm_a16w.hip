@@ -356,10 +356,10 @@ template <int FMT, bool OUT_BF16, bool W8>
 static hipError_t launch(const GemmArgs& a, hipStream_t st)
 {
     constexpr int LDS = Geo<W8>::LDS_BYTES;
-    // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)gemm_a16w_kernel<FMT, OUT_BF16, W8>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-    if (attr != hipSuccess) return attr;
+    // the LDS ring exceeds the default 64 KB dynamic limit
+    static LdsLimit lim;
+    if (const hipError_t e = lim.ensure((const void*)gemm_a16w_kernel<FMT, OUT_BF16, W8>, LDS, st); e != hipSuccess)
+        return e;
     const unsigned tiles = (unsigned)(((a.m + BM - 1) / BM) * ((a.n + BN - 1) / BN));
     hipLaunchKernelGGL((gemm_a16w_kernel<FMT, OUT_BF16, W8>), dim3(tiles), dim3(THREADS), LDS, st, a);
     return hipGetLastError();

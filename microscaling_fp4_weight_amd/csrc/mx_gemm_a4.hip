@@ -396,12 +396,11 @@ __global__ __launch_bounds__(THREADS) void gemm_a4_merged_kernel(const GemmArgs 
 template <bool OUT_BF16, bool W_TILED>
 static hipError_t launch_merged(const GemmArgs& a, uint32_t full, unsigned groups, hipStream_t st)
 {
-    // the LDS ring exceeds the default 64 KB dynamic limit; raise it once per instance
-    // (thread-safe function-local static initialisation)
-    static const hipError_t attr = hipFuncSetAttribute((const void*)a4::gemm_a4_merged_kernel<OUT_BF16, W_TILED>,
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       a4::Cfg<2>::LDS_BYTES);
-    if (attr != hipSuccess) return attr;
+    // the LDS ring exceeds the default 64 KB dynamic limit
+    static LdsLimit lim;
+    if (const hipError_t e = lim.ensure((const void*)a4::gemm_a4_merged_kernel<OUT_BF16, W_TILED>,
+                                        a4::Cfg<2>::LDS_BYTES, st); e != hipSuccess)
+        return e;
     hipLaunchKernelGGL((a4::gemm_a4_merged_kernel<OUT_BF16, W_TILED>), dim3(groups), dim3(a4::THREADS),
                        a4::Cfg<2>::LDS_BYTES, st, a, full);
     return hipGetLastError();

@@ -274,8 +274,8 @@ template <int BLOCK, int FMT, bool OUT_BF16, int MAXU>
 static hipError_t launch_one(const GemmArgs& a, uint32_t grid, hipStream_t st)
 {
     const void* k = (const void*)g16::gemv16_kernel<BLOCK, FMT, OUT_BF16, MAXU>;
-    static const hipError_t attr = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, g16::Lay<MAXU>::BYTES);
-    if (attr != hipSuccess) return attr;
+    static LdsLimit lim;
+    if (const hipError_t e = lim.ensure(k, g16::Lay<MAXU>::BYTES, st); e != hipSuccess) return e;
     hipLaunchKernelGGL((g16::gemv16_kernel<BLOCK, FMT, OUT_BF16, MAXU>), dim3(grid), dim3(g16::THREADS),
                        g16::Lay<MAXU>::BYTES, st, a);
     return hipGetLastError();

@@ -7,7 +7,38 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mxk {
+
+// The dynamic-LDS limit of one kernel, raised above the 64 KB default.  The limit is an
+// attribute the runtime keeps per device, so it is set once on each device that launches the
+// kernel (the device of the launch stream; the calling thread's current device for the null
+// stream) and remembered in a bit per device; devices 32 and up set it on every launch.
+class LdsLimit {
+public:
+    hipError_t ensure(const void* kernel, int bytes, hipStream_t st)
+    {
+        int dev = 0;
+        hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint32_t bit = dev >= 0 && dev < 32 ? 1u << dev : 0u;
+        if (bit && (done_.load(std::memory_order_acquire) & bit)) return hipSuccess;
+        int cur = dev;
+        if (st && (e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (cur != dev) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess) e = r;
+        }
+        if (e == hipSuccess && bit) done_.fetch_or(bit, std::memory_order_release);
+        return e;
+    }
+
+private:
+    std::atomic<uint32_t> done_{0};
+};
 
 enum { FMT_E4M3 = 0, FMT_UE5M3 = 1, FMT_E8M0 = 2 };  // same values as mx_scale_fmt
 
