@@ -72,8 +72,10 @@ def gemv_bytes(m: int, n: int, k: int, block: int) -> int:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 2000 steps of 2.65 ms: about 5 s of timed GPU work, long enough for an outside
+    # utilisation sampler to see it
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-rows", action="store_true", help="skip the GEMV/GEMM rows")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--detail", default=None,
