@@ -235,7 +235,10 @@ __global__ __launch_bounds__(THREADS) void gemv16_kernel(const GemmArgs a)
 
     // partial sums of every unit: [unit][wave][lane]; then every thread sums one output over
     // the waves in wave order (fixed, so the result does not depend on timing); the columns
-    // of X rows past m are zero padding and are skipped
+    // of X rows past m are zero padding and are skipped.  The partials overwrite the code
+    // buffers, into which a workgroup with fewer units than slots may still have LDS-DMA
+    // loads of its unused slots in flight (out of range: they write zeros): wait for them.
+    wait_vmcnt<0>();
     __syncthreads();
     f32x4* red = reinterpret_cast<f32x4*>(lds);
 #pragma unroll
