@@ -423,6 +423,12 @@ __device__ __forceinline__ void bstore128(rsrc_t r, uint32_t off, u32x4 v)
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
+// The same store marked non-temporal (cache-policy bit 1, "nt"): output that no later work
+// in the launch reads, kept from displacing the operand tiles in the L2.
+__device__ __forceinline__ void bstore128_nt(rsrc_t r, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+}
 
 // ---------------------------------------------------------------------------------------
 // Dequantization helpers.

@@ -307,7 +307,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_a16p_kernel(const GemmArgs a)
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * PITCH + chunk * 16);
                 const uint32_t mm = wm * 64 + pass * PASS_ROWS + row, nn = wn * 128 + chunk * CE;
                 const uint32_t off = (mm < mrows && nn < nrows) ? (mm * ldy + nn) * ESZ : kOOB;
-                bstore128(yr, off, v);
+                bstore128_nt(yr, off, v);
             }
         }
     } else {

@@ -360,7 +360,7 @@ __device__ __forceinline__ void gemm_a4_tile(const GemmArgs& a, uint32_t tile_ba
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * PITCH + chunk * 16);
                 const uint32_t mm = wm * 128 + pass * PASS_ROWS + row, nn = wn * 32 * NJ + chunk * CE;
                 const uint32_t off = (mm < mlim && nn < nlim) ? (mm * ldy + nn) * ESZ : kOOB;
-                bstore128(yr, off, v);
+                bstore128_nt(yr, off, v);
             }
         }
     } else {
