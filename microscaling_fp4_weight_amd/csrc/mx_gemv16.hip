@@ -28,13 +28,10 @@ namespace g16 {
 
 constexpr uint32_t KTOT = 4096;  // k handled by this kernel
 
-#ifndef MX_G16_WAVES
-#define MX_G16_WAVES 16
-#endif
-constexpr int WAVES = MX_G16_WAVES;               // waves per workgroup; wave w owns k slice w
+constexpr int WAVES = 16;                         // waves per workgroup; wave w owns k slice w
 constexpr uint32_t GRID_CAP = 256;                // workgroups (one per CU)
 constexpr int THREADS = 64 * WAVES;
-constexpr uint32_t KCHUNK = KTOT / WAVES;         // k per wave slice (512 or 256)
+constexpr uint32_t KCHUNK = KTOT / WAVES;         // k per wave slice (256)
 constexpr uint32_t CPR = KCHUNK / 32;             // 16-byte code chunks per row of a slice
 constexpr uint32_t RPI = 64 / CPR;                // rows per LDS-DMA instruction
 constexpr int NDMA = 16 / RPI;                    // LDS-DMA instructions per unit
