@@ -4,6 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
     python bench.py --pmc-run      # launches for rocprofv3 --pmc traffic counters (see below)
     python bench.py --pmc-run rows # launches of the GEMV / GEMM rows for rocprofv3 --pmc
+    python bench.py --pmc-run c5   # launches of the 405B-FFN W4A16 products for rocprofv3 --pmc
 
 One step = the whole block-size/scale sweep on the Llama-7B FFN-shaped weight
 (4096 x 11008 bf16 ~ N(0, sigma^2), 0.1% entries x20): for every sigma in {0.005, 0.02, 0.1},
@@ -31,7 +32,8 @@ size (five times, the calibration for the HBM byte counters), for
 profiles/traffic.json and reported as `roofline.traffic` while the kernel source is unchanged.
 `--pmc-run rows` launches the decode GEMV (m 1, 4, 16; n 14336), the 405B-FFN GEMV (m 1), the 70B-FFN
 prefill GEMM in W4A16 and W4A4 (tiled weight scales) three times each, and the same copy, for
-the HBM byte and matrix-core counters of those kernels.
+the HBM byte and matrix-core counters of those kernels; `--pmc-run c5` launches the 405B-FFN
+W4A16 products (m 256 and 4096) three times each.
 """
 from __future__ import annotations
 
@@ -83,9 +85,9 @@ def main():
     ap.add_argument("--library-ref", action="store_true",
                     help="only time the vendor library's bf16 and MXFP4 GEMMs at the 70B-FFN "
                          "shape beside this library's W4A16 and W4A4 modes (one JSON line)")
-    ap.add_argument("--pmc-run", nargs="?", const="quantize", choices=("quantize", "rows"),
+    ap.add_argument("--pmc-run", nargs="?", const="quantize", choices=("quantize", "rows", "c5"),
                     help="only the launches that the counters are read on: the dominant kernel "
-                         "(default) or the GEMV / GEMM rows")
+                         "(default), the GEMV / GEMM rows, or the 405B-FFN W4A16 products")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path runs on a single MI355X and this "
@@ -109,6 +111,9 @@ def main():
         return
     if args.pmc_run == "rows":
         pmc_rows(mx, torch, np, synth, dev)
+        return
+    if args.pmc_run == "c5":
+        pmc_c5(mx, torch, np, synth, dev)
         return
     if args.library_ref:
         library_ref(mx, torch, np, synth, dev, stream)
@@ -601,6 +606,29 @@ def pmc_rows(mx, torch, np, synth, dev):
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"pmc rows: 5 x copy ({COPY_BYTES} bytes read, {COPY_BYTES} written)")
+
+
+def pmc_c5(mx, torch, np, synth, dev):
+    """Three launches each of the 405B-FFN W4A16 product (53248 x 16384 UE5M3 weight with its
+    per-tensor scale) at m 256 and m 4096, each after a 512 MB fill that evicts the Infinity
+    Cache, for the L2 / matrix-core / vector counters of the wide-tile kernel."""
+    wh = synth.c5_weight()
+    g = synth.c5_tensor_scale(wh)
+    w = torch.from_numpy(wh.view(np.int16)).view(torch.bfloat16).to(dev)
+    del wh
+    N, K = 53248, 16384
+    c5, s5 = mx.mx_quantize(w, 32, "ue5m3", g)
+    del w
+    torch.cuda.empty_cache()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for m in (256, 4096):
+        x = torch.from_numpy(synth.c5_x(m).view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            flush.fill_(1)
+            mx.mx_gemm(x, c5, s5, 32, "ue5m3", g, "a16", y=y)
+        torch.cuda.synchronize()
+        log(f"pmc c5: 3 x W4A16 {m} x {N} x {K} ({2 * m * N * K} flops)")
 
 
 def library_ref(mx, torch, np, synth, dev, stream):
