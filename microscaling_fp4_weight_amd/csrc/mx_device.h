@@ -270,6 +270,19 @@ __device__ __forceinline__ uint32_t rd32_bits(double t)  // t > 0
     return b;
 }
 
+// The seven thresholds for a block whose s * g is sg (exact in fp64, > 0).
+__device__ __forceinline__ void enc_thresholds(double sg, uint32_t (&u)[7])
+{
+    const double t[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+        const double tt = t[i] * sg;
+        uint32_t b = rd32_bits(tt);
+        if ((i & 1) && (double)u2f(b) == tt) b -= 1u;  // ">=" points: 0.75, 1.75, 3.5
+        u[i] = b;
+    }
+}
+
 template <int FMT>
 __device__ __forceinline__ EncG enc_params_g(uint32_t byte, double g)
 {
@@ -280,15 +293,36 @@ __device__ __forceinline__ EncG enc_params_g(uint32_t byte, double g)
         for (int i = 0; i < 7; ++i) p.u[i] = 0x7F800000u;  // nothing exceeds +Inf
         return p;
     }
-    const double sg = s * g;
-    const double t[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-#pragma unroll
-    for (int i = 0; i < 7; ++i) {
-        const double tt = t[i] * sg;
-        uint32_t b = rd32_bits(tt);
-        if ((i & 1) && (double)u2f(b) == tt) b -= 1u;  // ">=" points: 0.75, 1.75, 3.5
-        p.u[i] = b;
-    }
+    enc_thresholds(s * g, p.u);
+    return p;
+}
+
+// The same thresholds from a per-workgroup table.  Every scale value s of the three formats
+// is (1 + j/8) 2^e with j its three mantissa bits as an fp32 number, and while the thresholds
+// for s = 1 + j/8 and their 2^e multiples are all normal fp32 numbers, rounding down and the
+// one-ulp step of the ">=" points commute with the factor 2^e: the thresholds for s are the
+// table's row j with e added to each exponent field.  tab[8 j + i] holds threshold i for
+// s = 1 + j/8 (enc_thresholds((1 + j/8) g)); a block outside that range (s = 0, an fp32-subnormal
+// s, a table row or a result beyond the normal range) takes enc_params_g.
+template <int FMT>
+__device__ __forceinline__ EncG enc_params_g_tab(uint32_t byte, double g, const uint32_t* tab)
+{
+    const uint32_t sb = f2u(scale_value_f32<FMT>(byte));
+    const int es = (int)(sb >> 23);
+    const uint32_t* row = tab + 8 * ((sb >> 20) & 7u);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(row);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 4);
+    const int e = es - 127, e0 = (int)(lo.x >> 23), e6 = (int)(hi.z >> 23);
+    if (es == 0 || es >= 255 || e0 < 1 || e0 + e < 1 || e6 > 253 || e6 + e > 254) return enc_params_g<FMT>(byte, g);
+    const uint32_t d = (uint32_t)e << 23;
+    EncG p;
+    p.u[0] = lo.x + d;
+    p.u[1] = lo.y + d;
+    p.u[2] = lo.z + d;
+    p.u[3] = lo.w + d;
+    p.u[4] = hi.x + d;
+    p.u[5] = hi.y + d;
+    p.u[6] = hi.z + d;
     return p;
 }
 

@@ -58,6 +58,22 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
         for (int j = 0; j < NW; ++j) w[j] = 0u;
     }
 
+    // with a per-tensor scale: the element thresholds of the eight scale mantissas, once per
+    // workgroup (threads 0-7, one mantissa each), while the loads above are in flight; the
+    // barrier leaves the global loads alone (only the table's LDS writes are waited for)
+    __shared__ __attribute__((aligned(16))) uint32_t gtab[64];
+    if constexpr (!G1) {
+        if (threadIdx.x < 8) {
+            uint32_t u[7];
+            enc_thresholds((1.0 + 0.125 * (double)threadIdx.x) * g, u);
+#pragma unroll
+            for (int i = 0; i < 7; ++i) gtab[8 * threadIdx.x + i] = u[i];
+            gtab[8 * threadIdx.x + 7] = 0u;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's table writes are done
+        asm volatile("s_barrier" ::: "memory");
+    }
+
     // absmax bits (fp32 pattern of |x|) per lane-local block part
     uint32_t amax[NB];
 #pragma unroll
@@ -187,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
         uint32_t z[16];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const EncG16 q = enc_params_g16(enc_params_g<FMT>(sbyte[b], g));
+            const EncG16 q = enc_params_g16(enc_params_g_tab<FMT>(sbyte[b], g, gtab));
 #pragma unroll
             for (int jj = 0; jj < WPB; ++jj) z[b * WPB + jj] = enc_pair_g16(w[b * WPB + jj], q);
         }
@@ -196,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void quantize_fast_kernel(
     } else {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const EncG p = enc_params_g<FMT>(sbyte[b], g);
+            const EncG p = enc_params_g_tab<FMT>(sbyte[b], g, gtab);
             constexpr int EPB = 32 / NB;  // elements per lane-local block part
 #pragma unroll
             for (int ee = 0; ee < EPB; ++ee) {
