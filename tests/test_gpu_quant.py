@@ -134,11 +134,14 @@ def _tensor_scale_decision_blocks(fmt: str, g: float, dtype: str) -> np.ndarray:
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("g", [0.37, 1.0 / 3.0, 0.70710677, 3.3e-3, 1234.5, 2.0 ** -7, 4.0])
+@pytest.mark.parametrize("g", [0.37, 1.0 / 3.0, 0.70710677, 3.3e-3, 1234.5, 2.0 ** -7, 4.0, 2e-38, 1e37])
 def test_quantize_tensor_scale_decision_points(dtype, fmt, g):
-    # with g != 1 the kernel decides elements from x * fl32(1/M) (s g = M 2^F) and redoes, with
-    # the exact comparison, lanes whose quotient comes near a decision point; these blocks put
-    # elements at and around every decision point of every scale, so both ways are exercised
+    # with g != 1 the kernel compares each |x| with the block's seven decision thresholds t s g,
+    # rounded to fp32 bit patterns; they come from a per-workgroup table of the eight scale
+    # mantissas scaled by the block's power of two, or, where that would leave the normal fp32
+    # range (the smallest and largest scales, and every block at g = 2e-38 or 1e37), from fp64
+    # products.  These blocks put elements at and around every decision point of every scale,
+    # so both ways are exercised against the exact oracle
     g = float(np.float32(g))
     x = _tensor_scale_decision_blocks(fmt, g, dtype)
     c, s = run_quant(x, 32, fmt, g)
