@@ -112,6 +112,31 @@ def test_gemv16(fmt, block, m, n):
         assert_gemm_close(got, yref, aref, out == "bf16", f"gemv16 m={m} n={n} {fmt} B={block} {out}")
 
 
+# Row strides through the small-m kernels: activation rows longer than k (16-byte aligned, which
+# the 2 <= m <= 16 kernel takes, and unaligned, which goes to the generic GEMV) and output rows
+# longer than n, whose extra columns must stay untouched; m = 1 takes the sweeping kernel
+# (n 1000) and the row-group kernel (n 33609).
+@pytest.mark.parametrize("ldx", [4096 + 64, 4096 + 3])
+@pytest.mark.parametrize("m,n", [(1, 1000), (1, 33609), (2, 1000), (7, 1000), (16, 33609)])
+def test_gemv_small_m_strides(ldx, m, n):
+    k, fmt = 4096, "ue5m3"
+    g = float(np.float32(0.37))
+    x = synth.normal((m, ldx), "bf16", f"gvs.x.{m}.{ldx}", 1.0)
+    w = synth.normal((n, k), "bf16", f"gvs.w.{n}", 0.02, 0.01, 20.0)
+    c, s, cd, sd = quantize_ref(w, 32, fmt, g)
+    cols = np.unique(np.concatenate([np.arange(0, n, 97), np.arange(n - 20, n)]))
+    yref, aref = oracle.gemm(np.ascontiguousarray(x[:, :k]), c[cols], s[cols], 32, fmt, g, "a16")
+    xd = bf16_dev(x)[:, :k]
+    for dt in (torch.float32, torch.bfloat16):
+        big = torch.full((m, n + 24), float("nan"), dtype=dt, device=DEV)
+        y = big[:, :n]
+        mx.mx_gemm(xd, cd, sd, 32, fmt, g, "a16", y=y)
+        torch.cuda.synchronize()
+        got = to_host_bits(y.float())[:, cols]
+        assert_gemm_close(got, yref, aref, dt == torch.bfloat16, f"strided GEMV m={m} n={n} ldx={ldx} {dt}")
+        assert torch.isnan(big[:, n:].float()).all()
+
+
 # Zero-scale blocks through the GEMVs (an E4M3 / UE5M3 scale's mantissa multiplies each block's
 # sum there, so a zero scale must give a zero block): all-zero blocks and blocks small enough
 # to flush (a <= 3 s_min: 1e-4 under E4M3, 1e-6 under UE5M3), on the sweeping kernel (k 4096)
