@@ -71,11 +71,13 @@ def test_quantize_tensor_scale(fmt, g):
     g = float(np.float32(g))
     x = synth.normal((19, 1024), "bf16", "gq.g", 0.3, 0.01, 20.0)
     x = np.concatenate([x, edge_tensor(1024)[:40]])
-    for block in (4, 32, 256):
-        c, s = run_quant(x, block, fmt, g)
+    xf = synth.bf16_to_f32(x)
+    for block in (4, 8, 16, 32, 64, 128, 256):
         rc, rs = oracle.quantize(x, block, fmt, g)
-        np.testing.assert_array_equal(s, rs)
-        np.testing.assert_array_equal(c, rc)
+        for inp in (x, xf):  # bf16 input, and the same values as fp32
+            c, s = run_quant(inp, block, fmt, g)
+            np.testing.assert_array_equal(s, rs)
+            np.testing.assert_array_equal(c, rc)
 
 
 def _tensor_scale_decision_blocks(fmt: str, g: float, dtype: str) -> np.ndarray:
