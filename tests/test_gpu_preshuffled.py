@@ -27,22 +27,24 @@ def _gpu():
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rows,k", [(8, 2048), (13, 4224), (300, 8192), (5, 64), (17, 2112)])
-def test_quantize_dequantize_preshuffled(dtype, fmt, rows, k):
+@pytest.mark.parametrize("g", [1.0, 0.37])
+def test_quantize_dequantize_preshuffled(dtype, fmt, rows, k, g):
+    g = float(np.float32(g))
     x = synth.normal((rows, k), dtype, f"ps.{dtype}.{rows}.{k}", 0.02, 0.01, 20.0)
     xd = bf16_dev(x) if dtype == "bf16" else f32_dev(x)
-    codes, scales = mx.mx_quantize(xd, 32, fmt, layout="preshuffled")
+    codes, scales = mx.mx_quantize(xd, 32, fmt, g, layout="preshuffled")
     assert scales.numel() == mx.mx_scale_bytes(rows, k, 32, "preshuffled")
-    rc, rs = oracle.quantize(x, 32, fmt)
+    rc, rs = oracle.quantize(x, 32, fmt, g)
     got = to_host_bits(scales)
     np.testing.assert_array_equal(to_host_bits(codes), rc)
     np.testing.assert_array_equal(got[preshuffled_positions(rows, k)], rs)
     assert np.all(got[preshuffled_padding_positions(rows, k)] == 0)
     for out in ("f32", "bf16"):
         dt = torch.float32 if out == "f32" else torch.bfloat16
-        y = mx.mx_dequantize(codes, scales, k, 32, fmt, out_dtype=dt, layout="preshuffled")
-        ref = oracle.dequantize(rc, rs, k, 32, fmt, 1.0, out)
-        g = to_host_bits(y)
-        np.testing.assert_array_equal(g.view(np.uint32) if out == "f32" else g,
+        y = mx.mx_dequantize(codes, scales, k, 32, fmt, g, out_dtype=dt, layout="preshuffled")
+        ref = oracle.dequantize(rc, rs, k, 32, fmt, g, out)
+        yb = to_host_bits(y)
+        np.testing.assert_array_equal(yb.view(np.uint32) if out == "f32" else yb,
                                       ref.view(np.uint32) if out == "f32" else ref)
 
 

@@ -25,14 +25,16 @@ def _gpu():
 
 @pytest.mark.parametrize("rows,k", [(300, 8192), (256, 4224), (7, 96), (513, 1024)])
 @pytest.mark.parametrize("fmt", ["e8m0", "e4m3"])
-def test_quantize_tiled(rows, k, fmt):
+@pytest.mark.parametrize("g", [1.0, 0.37])
+def test_quantize_tiled(rows, k, fmt, g):
+    g = float(np.float32(g))
     x = synth.normal((rows, k), "bf16", f"tl.{rows}.{k}", 0.5, 0.01, 30.0)
-    c_ref, s_ref = oracle.quantize(x, 32, fmt, 1.0)
+    c_ref, s_ref = oracle.quantize(x, 32, fmt, g)
     xd = bf16_dev(x)
     nbytes = mx.mx_scale_bytes(rows, k, 32, "tiled")
     assert nbytes == -(-rows // 256) * -(-k // 256) * 2048
     scales = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)  # poison the padding
-    codes, scales = mx.mx_quantize(xd, 32, fmt, layout="tiled", scales=scales)
+    codes, scales = mx.mx_quantize(xd, 32, fmt, g, layout="tiled", scales=scales)
     torch.cuda.synchronize()
     got = to_host_bits(scales)
     np.testing.assert_array_equal(to_host_bits(codes), c_ref)
@@ -41,8 +43,8 @@ def test_quantize_tiled(rows, k, fmt):
     assert np.all(got[pad] == 0), "padding blocks of the last stage must read 0"
     # dequantization from tiled scales is the row-major result bit for bit
     for dt in (torch.float32, torch.bfloat16):
-        y_t = mx.mx_dequantize(codes, scales, k, 32, fmt, out_dtype=dt, layout="tiled")
-        y_r = mx.mx_dequantize(codes, torch.from_numpy(s_ref).to(DEV), k, 32, fmt, out_dtype=dt)
+        y_t = mx.mx_dequantize(codes, scales, k, 32, fmt, g, out_dtype=dt, layout="tiled")
+        y_r = mx.mx_dequantize(codes, torch.from_numpy(s_ref).to(DEV), k, 32, fmt, g, out_dtype=dt)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_host_bits(y_t), to_host_bits(y_r))
 
