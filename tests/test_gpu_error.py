@@ -49,9 +49,13 @@ def test_error_split_tiny_round_trip_config():
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "ue5m3", "e8m0"])
-def test_error_split_tensor_scale(fmt):
+@pytest.mark.parametrize("block", [4, 32, 256])
+def test_error_split_tensor_scale(fmt, block):
     x = synth.normal((64, 1024), "bf16", "er.g", 0.01, 0.01, 20.0)
-    check(x, bf16_dev(x), 32, fmt, float(np.float32(0.0137)))
+    g = float(np.float32(0.0137))
+    check(x, bf16_dev(x), block, fmt, g)
+    xf = synth.bf16_to_f32(x)  # the same values as fp32 input
+    check(xf, torch.from_numpy(xf).to(DEV), block, fmt, g)
 
 
 def test_error_split_flushed_tensor():
